@@ -1,0 +1,370 @@
+"""Pins of the fp64 CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against something other than itself: hand-derived
+worked examples (tests/golden/worked_example.json), closed forms, a special
+case that reduces to a library routine (torch CPU scaled-dot-product
+attention), an independent dense brute force (tests/bruteforce.py), finite
+differences and fp64 autograd of the dense formulation, and invariants.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import bruteforce as bf
+from oracle import oracle as ora
+from lsh_sparse_attention_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rand_problem(seed, L, d, nh, nb, scale_q=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((L, d)) * scale_q
+    v = rng.standard_normal((L, d))
+    rot = rng.standard_normal((nh, d, nb // 2))
+    do = rng.standard_normal((L, d))
+    return q, v, rot, do
+
+
+def _weights_to_rows(rows, L):
+    out = np.zeros((len(rows), L))
+    for i, row in enumerate(rows):
+        for k, w in row.items():
+            out[i, int(k)] = float(Fraction(w)) if isinstance(w, str) else w
+    return out
+
+
+# ----------------------------------------------------------------------------- hash
+
+def test_hash_golden_identity_rotation():
+    g = _golden()["hash"]
+    q = np.array(g["q"], float)
+    rot = np.array(g["rot"], float)
+    assert ora.hash_(q, rot, g["n_buckets"]).tolist() == g["buckets"]
+
+
+def test_hash_identity_rotation_closed_form():
+    # R = first nb/2 columns of I_d: bucket = index of max |q_j| over j < nb/2,
+    # offset by nb/2 when that entry is negative.
+    rng = np.random.default_rng(3)
+    d, nb = 16, 12
+    q = rng.standard_normal((300, d))
+    rot = np.eye(d)[:, : nb // 2][None]
+    j = np.argmax(np.abs(q[:, : nb // 2]), axis=1)
+    want = j + (nb // 2) * (q[np.arange(300), j] < 0)
+    assert np.array_equal(ora.hash_(q, rot, nb)[0], want)
+
+
+def test_hash_two_buckets_is_sign():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((500, 8))
+    rot = rng.standard_normal((3, 8, 1))
+    got = ora.hash_(q, rot, 2)
+    for r in range(3):
+        assert np.array_equal(got[r], np.where(q @ rot[r, :, 0] > 0, 0, 1))
+
+
+@pytest.mark.parametrize("nb", [2, 8, 64, 1024])
+def test_hash_matches_bruteforce(nb):
+    q, _, rot, _ = _rand_problem(5 + nb, 200, 32, 3, nb)
+    assert np.array_equal(ora.hash_(q, rot, nb), bf.buckets(q, rot))
+
+
+def test_hash_sign_order_matters():
+    # [xR; -xR] puts the negated half second: -y_j wins at index nb/2 + j.
+    q = np.array([[-3.0, 1.0]])
+    rot = np.eye(2)[None]
+    assert ora.hash_(q, rot, 4)[0, 0] == 2
+
+
+# ----------------------------------------------------------------------------- sort
+
+def test_sort_golden():
+    g = _golden()["attention"]
+    bk = np.array(g["buckets"], np.int32)
+    perm, inv, win_lo = ora.sort(bk, g["chunk_len"])
+    assert perm.tolist() == g["perm"]
+    assert inv.tolist() == g["inv"]
+    assert win_lo.tolist() == g["win_lo"]
+
+
+@pytest.mark.parametrize("seed,L,nb,m", [(1, 64, 4, 8), (2, 256, 16, 32), (3, 512, 2, 512),
+                                         (4, 384, 64, 16), (5, 128, 1000, 16)])
+def test_sort_is_stable_permutation(seed, L, nb, m):
+    rng = np.random.default_rng(seed)
+    nh = 3
+    bk = rng.integers(0, nb, size=(nh, L)).astype(np.int32)
+    perm, inv, win_lo = ora.sort(bk, m)
+    p2, i2 = bf.sort(bk)
+    assert np.array_equal(perm, p2) and np.array_equal(inv, i2)
+    for r in range(nh):
+        assert np.array_equal(np.sort(perm[r]), np.arange(L))
+        assert np.array_equal(inv[r][perm[r]], np.arange(L))
+        sb = bk[r][perm[r]]
+        assert np.all(np.diff(sb) >= 0)
+        same = np.diff(sb) == 0
+        assert np.all(np.diff(perm[r])[same] > 0)
+        # win_lo closed form: max(first sorted index of the bucket, (chunk-1)*m)
+        start = {}
+        for s in range(L):
+            start.setdefault(int(sb[s]), s)
+        c = inv[r] // m
+        want = np.maximum([start[int(b)] for b in bk[r]], (c - 1) * m)
+        assert np.array_equal(win_lo[r], want)
+
+
+def test_win_lo_is_min_of_round_set():
+    rng = np.random.default_rng(9)
+    L, nb, m, nh = 96, 6, 8, 2
+    bk = rng.integers(0, nb, size=(nh, L)).astype(np.int32)
+    _, inv, win_lo = ora.sort(bk, m)
+    masks = bf.round_masks(bk, m)
+    for r in range(nh):
+        for i in range(L):
+            assert win_lo[r, i] == inv[r][masks[r, i]].min()
+
+
+# ----------------------------------------------------------------------------- attended sets
+
+def test_union_golden():
+    g = _golden()["attention"]
+    bk = np.array(g["buckets"], np.int32)
+    L, m = g["L"], g["chunk_len"]
+    for key, nh in (("round0_only", 1), ("both_rounds", 2)):
+        perm, inv, _ = ora.sort(bk[:nh], m)
+        mask = ora.union_mask(bk[:nh], perm, inv, m)
+        for i, members in enumerate(g[key]["sets"]):
+            got = sorted(set(np.nonzero(mask[i])[0].tolist()) - {i})
+            assert got == members, (key, i)
+
+
+@pytest.mark.parametrize("seed,L,nb,nh,m", [(1, 64, 4, 1, 8), (2, 128, 8, 3, 16), (3, 96, 2, 2, 32),
+                                            (4, 256, 32, 4, 16), (5, 64, 16, 2, 64), (6, 200, 4, 2, 8)])
+def test_union_matches_bruteforce(seed, L, nb, nh, m):
+    rng = np.random.default_rng(seed)
+    bk = rng.integers(0, nb, size=(nh, L)).astype(np.int32)
+    perm, inv, _ = ora.sort(bk, m)
+    assert np.array_equal(ora.union_mask(bk, perm, inv, m), bf.union_mask(bk, m))
+
+
+# ----------------------------------------------------------------------------- forward
+
+def test_forward_golden_one_hot():
+    g = _golden()["attention"]
+    bk = np.array(g["buckets"], np.int32)
+    L, m = g["L"], g["chunk_len"]
+    q = np.random.default_rng(0).standard_normal((L, L))
+    v = np.eye(L)
+    for key, nh in (("round0_only", 1), ("both_rounds", 2)):
+        perm, inv, _ = ora.sort(bk[:nh], m)
+        out, lse = ora.forward(q, v, bk[:nh], perm, inv, m, g["scale"])
+        want = _weights_to_rows(g[key]["out_rows_as_weights"], L)
+        np.testing.assert_allclose(out, want, atol=1e-15)
+        sizes = np.array([len(s) for s in g[key]["sets"]])
+        np.testing.assert_allclose(lse, np.where(sizes > 0, np.log(np.maximum(sizes, 1)), 0.0), atol=1e-15)
+
+
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(1, 64, 8, 4, 1, 8), (2, 128, 16, 8, 3, 16),
+                                              (3, 256, 32, 16, 2, 32), (4, 96, 4, 2, 4, 96),
+                                              (5, 160, 8, 64, 2, 16)])
+def test_forward_matches_dense_bruteforce(seed, L, d, nb, nh, m):
+    q, v, rot, _ = _rand_problem(seed, L, d, nh, nb, scale_q=1.5)
+    scale = 1 / np.sqrt(d)
+    res = ora.head(q, v, rot, nb, m, scale)
+    bk = bf.buckets(q, rot)
+    assert np.array_equal(res["buckets"], bk)
+    out, lse = bf.attention(q, v, bf.union_mask(bk, m), scale)
+    np.testing.assert_allclose(res["out"], out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse, rtol=1e-12, atol=1e-12)
+
+
+def _one_side(q, r):
+    s = np.sign(q @ r)
+    s[s == 0] = 1
+    return q * s[:, None]
+
+
+def test_one_bucket_is_full_causal_shared_qk_attention():
+    # nb = 2 with every query on the positive side of r gives one bucket; with
+    # m = L the union is {j <= i}: full causal shared-QK attention where self is
+    # masked except for the first token.  Reference: torch CPU fp64 SDPA.
+    rng = np.random.default_rng(7)
+    L, d = 128, 16
+    rot = rng.standard_normal((1, d, 1))
+    q = _one_side(rng.standard_normal((L, d)), rot[0, :, 0])
+    v = rng.standard_normal((L, d))
+    scale = 0.37
+    res = ora.head(q, v, rot, 2, L, scale)
+    assert np.all(res["buckets"] == 0)
+    assert np.array_equal(res["perm"][0], np.arange(L))
+    qt = torch.from_numpy(q)[None, None]
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    mask = torch.tril(torch.ones(L, L, dtype=torch.bool), diagonal=-1)
+    mask[0, 0] = True
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, torch.from_numpy(v)[None, None], attn_mask=mask, scale=scale)[0, 0].numpy()
+    np.testing.assert_allclose(res["out"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_one_bucket_chunked_is_banded_causal_attention():
+    # One bucket and m < L: query i sees j <= i in its own chunk and the one before.
+    rng = np.random.default_rng(8)
+    L, d, m = 96, 8, 16
+    rot = rng.standard_normal((1, d, 1))
+    q = _one_side(rng.standard_normal((L, d)), rot[0, :, 0])
+    v = rng.standard_normal((L, d))
+    res = ora.head(q, v, rot, 2, m, 0.5)
+    c = np.arange(L) // m
+    i, j = np.arange(L)[:, None], np.arange(L)[None, :]
+    mask = (j < i) & (c[i] - c[j] <= 1)
+    mask[0, 0] = True
+    qt = torch.from_numpy(q)[None, None]
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, torch.from_numpy(v)[None, None], attn_mask=torch.from_numpy(mask), scale=0.5)[0, 0].numpy()
+    np.testing.assert_allclose(res["out"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_first_token_attends_to_itself():
+    q, v, rot, _ = _rand_problem(11, 256, 16, 4, 16)
+    res = ora.head(q, v, rot, 16, 32, 0.25)
+    assert np.array_equal(res["out"][0], v[0])
+    assert res["lse"][0] == pytest.approx(0.25 * np.linalg.norm(q[0]), rel=1e-14)
+
+
+def test_repeated_rotation_equals_one_round():
+    # Identical rounds give identical sets; duplicates must count once.
+    q, v, rot, _ = _rand_problem(12, 256, 16, 1, 16)
+    one = ora.head(q, v, rot, 16, 32, 0.3)
+    four = ora.head(q, v, np.repeat(rot, 4, axis=0), 16, 32, 0.3)
+    np.testing.assert_allclose(four["out"], one["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(four["lse"], one["lse"], rtol=1e-13, atol=1e-13)
+
+
+def test_m_equals_L_is_exact_per_bucket_causal_attention():
+    q, v, rot, _ = _rand_problem(13, 128, 8, 1, 8)
+    res = ora.head(q, v, rot, 8, 128, 0.7)
+    bk = res["buckets"][0]
+    i, j = np.arange(128)[:, None], np.arange(128)[None, :]
+    mask = (bk[:, None] == bk[None, :]) & (j <= i)
+    out, _ = bf.attention(q, v, mask, 0.7)
+    np.testing.assert_allclose(res["out"], out, rtol=1e-12, atol=1e-12)
+
+
+def test_convex_hull_and_constant_values():
+    q, v, rot, _ = _rand_problem(14, 192, 8, 3, 8)
+    res = ora.head(q, v, rot, 8, 16, 0.35)
+    mask = ora.union_mask(res["buckets"], res["perm"], res["inv"], 16)
+    for i in range(192):
+        members = v[mask[i]]
+        assert np.all(res["out"][i] <= members.max(axis=0) + 1e-12)
+        assert np.all(res["out"][i] >= members.min(axis=0) - 1e-12)
+    const = np.tile(np.arange(8.0), (192, 1))
+    res2 = ora.head(q, const, rot, 8, 16, 0.35)
+    np.testing.assert_allclose(res2["out"], const, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _loss_grad(q, v, do, bk, perm, inv, m, scale):
+    out, lse = ora.forward(q, v, bk, perm, inv, m, scale)
+    dq, dv = ora.backward(q, v, do, bk, perm, inv, out, lse, m, scale)
+    return float((out * do).sum()), dq, dv
+
+
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(21, 48, 6, 4, 2, 8), (22, 64, 4, 2, 3, 16)])
+def test_backward_finite_differences(seed, L, d, nb, nh, m):
+    q, v, rot, do = _rand_problem(seed, L, d, nh, nb)
+    scale = 0.8
+    bk = ora.hash_(q, rot, nb)
+    perm, inv, _ = ora.sort(bk, m)
+    _, dq, dv = _loss_grad(q, v, do, bk, perm, inv, m, scale)
+    h = 1e-6
+    rng = np.random.default_rng(seed)
+    for (t, c) in zip(rng.integers(0, L, 40), rng.integers(0, d, 40)):
+        for x, g in ((q, dq), (v, dv)):
+            xp, xm = x.copy(), x.copy()
+            xp[t, c] += h
+            xm[t, c] -= h
+            args_p = (xp, v) if x is q else (q, xp)
+            args_m = (xm, v) if x is q else (q, xm)
+            lp = float((ora.forward(*args_p, bk, perm, inv, m, scale)[0] * do).sum())
+            lm = float((ora.forward(*args_m, bk, perm, inv, m, scale)[0] * do).sum())
+            assert (lp - lm) / (2 * h) == pytest.approx(g[t, c], rel=1e-6, abs=1e-7)
+
+
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(31, 128, 16, 8, 3, 16), (32, 96, 8, 4, 2, 96),
+                                              (33, 160, 32, 32, 4, 8)])
+def test_backward_matches_dense_autograd(seed, L, d, nb, nh, m):
+    q, v, rot, do = _rand_problem(seed, L, d, nh, nb, scale_q=1.3)
+    scale = 1 / np.sqrt(d)
+    res = ora.head(q, v, rot, nb, m, scale, dout=do)
+    mask = bf.union_mask(res["buckets"], m)
+    allowed = mask & ~np.eye(L, dtype=bool)
+    empty = ~allowed.any(axis=1)
+    allowed[empty, np.nonzero(empty)[0]] = True
+    qt = torch.tensor(q, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    logits = (scale * qt @ kt.T).masked_fill(~torch.from_numpy(allowed), float("-inf"))
+    out = torch.softmax(logits, dim=-1) @ vt
+    (out * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(res["out"], out.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["dq"], qt.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(res["dv"], vt.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_backward_value_gradient_conserves_mass():
+    # Rows of the attention matrix sum to one, so sum_j dv_j = sum_i dO_i.
+    q, v, rot, do = _rand_problem(41, 256, 16, 4, 32)
+    res = ora.head(q, v, rot, 32, 32, 0.25, dout=do)
+    np.testing.assert_allclose(res["dv"].sum(axis=0), do.sum(axis=0), rtol=1e-11, atol=1e-11)
+
+
+def test_backward_constant_values_give_no_query_gradient():
+    # With constant V the output does not depend on q.
+    q, _, rot, do = _rand_problem(42, 128, 8, 3, 8)
+    v = np.ones((128, 8)) * 2.5
+    res = ora.head(q, v, rot, 8, 16, 0.5, dout=do)
+    np.testing.assert_allclose(res["dq"], 0.0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def test_generator_reproducible_and_margin():
+    cfg = gen.small_config(seq_len=256, head_dim=32, n_buckets=64, n_hashes=3, dtype="bf16", seed=5)
+    a = gen.generate(cfg)
+    b = gen.generate(cfg)
+    for k in ("q", "v", "rot", "dout"):
+        assert a[k].dtype == np.uint16 and np.array_equal(a[k], b[k])
+    q64 = gen.to_f64(a["q"], "bf16").reshape(-1, 32)
+    assert gen.margin_ok(q64, gen.to_f64(a["rot"], "bf16")).all()
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
+    got = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(x))
+    # bf16 spacing near 1 is 2^-7: 1+2^-8 ties to even (1.0), 1+3*2^-8 ties to even (1+2^-6),
+    # 1+2^-8+2^-20 is above the midpoint (1+2^-7)
+    np.testing.assert_array_equal(got, np.array([1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0 + 2 ** -7], np.float32))
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(got, t)
+
+
+def test_clustered_generator_skews_buckets():
+    cfg = gen.small_config(seq_len=2048, head_dim=64, n_buckets=256, n_hashes=2, dtype="bf16",
+                           clustered=True, n_clusters=16, seed=6)
+    a = gen.generate(cfg, with_grad=False)
+    q = gen.to_f64(a["q"][0, 0], "bf16")
+    bk = ora.hash_(q, gen.to_f64(a["rot"], "bf16"), 256)
+    assert len(np.unique(bk[0])) <= 64          # far fewer buckets than 256 occupied
+    assert np.bincount(bk[0]).max() >= 64       # and some of them big
