@@ -1,0 +1,174 @@
+/*
+ * lsh.h -- C ABI of the MI355X (gfx950) shared-QK LSH attention library.
+ *
+ * The library computes the hot path of LSH attention as described in
+ * "Reformer: The Efficient Transformer" (Kitaev, Kaiser, Levskaya): angular
+ * LSH by random rotation, a stable sort by (bucket, position), attention over
+ * chunks of the sorted order (each chunk sees itself and one chunk back, with
+ * causal, self and duplicate masking), a logsumexp-weighted combine over the
+ * hash rounds with the unsort, and the backward pass through the fixed
+ * permutation.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to contiguous row-major arrays,
+ *     owned by the caller, at least 16-byte aligned.  The library allocates
+ *     nothing, frees nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and nothing synchronises with the host.  Outputs are valid once the
+ *     stream reaches that point.
+ *   - The return value is an lsh_status_t.  Arguments are validated before
+ *     anything is launched: LSH_ERR_INVALID for malformed arguments (null
+ *     pointer, bad size, too small a workspace), LSH_ERR_UNSUPPORTED for a
+ *     well-formed problem outside what the kernels implement.  A failed
+ *     launch returns LSH_ERR_HIP.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.
+ *   - Results are deterministic: the same inputs give the same bits.
+ *
+ * Shapes: B batch, H heads, L sequence length, d head dim, nh hash rounds,
+ * nb buckets, m chunk length.  "dtype" below is problem.dtype (fp32 or bf16).
+ */
+#ifndef LSH_H
+#define LSH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LSH_OK = 0,
+    LSH_ERR_INVALID = 1,
+    LSH_ERR_UNSUPPORTED = 2,
+    LSH_ERR_HIP = 3
+} lsh_status_t;
+
+typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype_t;
+
+/* Which call a workspace is for (lsh_workspace_bytes). */
+typedef enum { LSH_WS_SORT = 0, LSH_WS_FWD = 1, LSH_WS_BWD = 2 } lsh_ws_kind_t;
+
+/*
+ * Problem description, passed by pointer to every call.
+ *   batch, heads, seq_len, head_dim: B, H, L, d.  Supported: d in {32, 64, 128};
+ *       1 <= L <= 65536.
+ *   n_hashes: nh >= 1 hash rounds (<= 16).
+ *   n_buckets: nb, even, 2 <= nb <= 4096; nb = 2 * columns of the rotation.
+ *   chunk_len: m, 1 <= m, L % m == 0 (m == L gives one chunk).
+ *   causal: must be 1 (the pages spell out causal masking only); 0 returns
+ *       LSH_ERR_UNSUPPORTED.
+ *   scale: the softmax scale applied to q_i . k_j (1/sqrt(d) for standard
+ *       scaled dot-product attention).
+ *   dtype: element type of q, v, rot, out, dout, dq, dv and o_rounds.
+ */
+typedef struct {
+    int32_t batch, heads, seq_len, head_dim;
+    int32_t n_hashes, n_buckets, chunk_len;
+    int32_t causal;
+    float scale;
+    int32_t dtype; /* lsh_dtype_t */
+} lsh_problem_t;
+
+/* Human-readable text of a status code (static storage). */
+const char *lsh_status_string(int status);
+
+/* Version of this ABI: major * 10000 + minor * 100 + patch. */
+int lsh_version(void);
+
+/* Bytes of device workspace that lsh_sort (LSH_WS_SORT), lsh_attn_fwd
+ * (LSH_WS_FWD) or lsh_attn_bwd (LSH_WS_BWD) needs for `prob`; 0 if the
+ * problem is invalid.  Alignment of the workspace pointer: 256 bytes. */
+size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind);
+
+/*
+ * lsh_hash -- angular LSH by random rotation ("Reformer" §2, random
+ * projections h(x) = argmax([xR; -xR])).
+ *   q       [B][H][L][d] dtype: queries (keys are q/|q|; hashing q or q/|q|
+ *           gives the same bucket).
+ *   rot     [nh][d][nb/2] dtype: one rotation per round, shared by all (b, h).
+ *   buckets [B][H][nh][L] int32 out: index in [0, nb) of the largest entry of
+ *           [qR_r ; -qR_r]; entry j < nb/2 is +y_j, entry nb/2 + j is -y_j;
+ *           ties go to the smaller index.
+ * Products are formed exactly and summed in fp32.
+ */
+int lsh_hash(const lsh_problem_t *prob, const void *q, const void *rot, int32_t *buckets,
+             void *stream);
+
+/*
+ * lsh_sort -- per (b, h, round), the stable sort of positions by bucket
+ * ("Reformer" §2: sorting by bucket clusters same-bucket pairs; ties by
+ * position), i.e. ascending order of the unique keys bucket * L + position.
+ *   buckets [B][H][nh][L] int32 in, values in [0, nb).
+ *   perm    [B][H][nh][L] int32 out: sorted index -> position.
+ *   inv     [B][H][nh][L] int32 out: position -> sorted index.
+ *   win_lo  [B][H][nh][L] int32 out, indexed by position t: the smallest
+ *           sorted index of the round's attended set of t (same bucket, not
+ *           after t, own chunk or the one before):
+ *           max(first sorted index of t's bucket, (inv[t]/m - 1) * m).
+ *           The set is exactly the sorted range [win_lo[t], inv[t]].
+ *   ws      workspace of lsh_workspace_bytes(prob, LSH_WS_SORT) bytes.
+ * Bucket values outside [0, nb) are undefined behaviour (not checked on the
+ * device).
+ */
+int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, int32_t *inv,
+             int32_t *win_lo, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lsh_attn_fwd -- per-round chunked attention ("Reformer" §2 and App. A):
+ * in round r, query t attends to the members of its attended set other than
+ * itself, with logits scale * q_t . k_j, k_j = q_j / |q_j|.  A member j that
+ * already belongs to the attended set of t in an earlier round is masked
+ * (the duplicate correction of App. A, folded into the mask), so that the
+ * rounds together count every member of the union once.  Outputs are
+ * written at the original positions (the unsort).
+ *   q, v       [B][H][L][d] dtype.
+ *   perm, inv, win_lo  as produced by lsh_sort.
+ *   o_rounds   [B][H][nh][L][d] dtype out: softmax-weighted average of v over
+ *              the round's unmasked members (0 if there are none).
+ *   lse_rounds [B][H][nh][L] fp32 out: log of the round's softmax
+ *              denominator (-inf if there are no unmasked members).
+ *   ws         workspace of lsh_workspace_bytes(prob, LSH_WS_FWD) bytes.
+ */
+int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const int32_t *perm,
+                 const int32_t *inv, const int32_t *win_lo, void *o_rounds, float *lse_rounds,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lsh_combine -- logsumexp-weighted combine over the rounds ("Reformer"
+ * App. A: each round's output is independently computable and the outputs
+ * are combined):  lse_t = log sum_r exp(lse_rounds[r][t]),
+ * out_t = sum_r exp(lse_rounds[r][t] - lse_t) o_rounds[r][t].
+ * A token with no member in any round (e.g. the first token) attends only to
+ * itself: out_t = v_t and lse_t = scale * |q_t| ("Reformer" §2 and App. A
+ * masking rule).
+ *   q, v       [B][H][L][d] dtype (read only for such tokens).
+ *   o_rounds, lse_rounds  as produced by lsh_attn_fwd.
+ *   out        [B][H][L][d] dtype out.   lse  [B][H][L] fp32 out.
+ */
+int lsh_combine(const lsh_problem_t *prob, const void *q, const void *v, const void *o_rounds,
+                const float *lse_rounds, void *out, float *lse, void *stream);
+
+/*
+ * lsh_attn_bwd -- gradient of the combined output with respect to q and v,
+ * with the bucket assignment and sort order held fixed (no differentiation
+ * through hashing or sorting, as the Reformer authors state in Hacker News
+ * thread 22095523).  Gradient flows through both the query and the
+ * normalised key k = q / |q|.
+ *   q, v, out, dout  [B][H][L][d] dtype; out and lse as produced by
+ *                    lsh_combine for the same q, v, perm, inv, win_lo.
+ *   lse        [B][H][L] fp32.
+ *   perm, inv, win_lo  as produced by lsh_sort.
+ *   dq, dv     [B][H][L][d] dtype out.
+ *   ws         workspace of lsh_workspace_bytes(prob, LSH_WS_BWD) bytes.
+ */
+int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void *out,
+                 const void *dout, const float *lse, const int32_t *perm, const int32_t *inv,
+                 const int32_t *win_lo, void *dq, void *dv, void *ws, size_t ws_bytes,
+                 void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_H */

@@ -1,0 +1,568 @@
+// attn_generic.hip -- per-query (wave per sorted row) kernels of the chunked
+// LSH attention, forward and backward, with fp32 arithmetic for both fp32 and
+// bf16 storage.  These are the fp32 path, and the bf16 path for shapes the
+// MFMA kernels do not take.
+//
+// Method: "Reformer: The Efficient Transformer" §2 (shared-QK attention over
+// sorted chunks, causal mask through the permutation, self only as a
+// fallback) and App. A (each query attends to the union of its round sets;
+// duplicates are masked; per-round outputs combined by logsumexp weights).
+//
+// Round r of query i (sorted index s) attends to the sorted range
+// [s - w, s - 1], w = s - win_lo.  A member j is skipped in round r when it
+// is also in the attended set of i in an earlier round r' < r, so that every
+// member of the union is counted in exactly one round (the first that holds
+// it).  Lanes of a wave take keys for the scores and head-dim components for
+// the weighted sums.
+#include "common.hpp"
+
+namespace lsh {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kRowsPerWave = 4;
+
+// ---------------------------------------------------------------------------
+// prep: packed records, inverse norms, and (backward) D = dO . O
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *__restrict__ q,
+                                                        const int32_t *__restrict__ inv,
+                                                        const int32_t *__restrict__ win_lo,
+                                                        uint32_t *__restrict__ meta, uint32_t *__restrict__ srec,
+                                                        float *__restrict__ rnorm, const T *__restrict__ out,
+                                                        const T *__restrict__ dout, float *__restrict__ Dvec)
+{
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (t >= L)
+        return;
+    const size_t tok = (size_t)bh * L + t;
+    float ss = 0.f;
+    const T *row = q + tok * D;
+    for (int c = 0; c < D; c += 8) {
+        float x[8];
+        load8(row + c, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            ss = fmaf(x[k], x[k], ss);
+    }
+    rnorm[tok] = 1.0f / sqrtf(ss);
+    for (int r = 0; r < nh; ++r) {
+        const size_t idx = ((size_t)bh * nh + r) * L + t;
+        const uint32_t s = (uint32_t)inv[idx];
+        const uint32_t w = s - (uint32_t)win_lo[idx];
+        meta[tok * nh + r] = s | (w << 16);
+        srec[((size_t)bh * nh + r) * L + s] = (uint32_t)t | (w << 16);
+    }
+    if (Dvec) {
+        const T *o = out + tok * D, *g = dout + tok * D;
+        float acc = 0.f;
+        for (int c = 0; c < D; c += 8) {
+            float x[8], y[8];
+            load8(o + c, x);
+            load8(g + c, y);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                acc = fmaf(x[k], y[k], acc);
+        }
+        Dvec[tok] = acc;
+    }
+}
+
+// Dot of a per-lane row (global) with a wave-distributed vector whose
+// component c sits in lane c % 64 of reg[c / 64].
+template <typename T, int D>
+__device__ __forceinline__ float dot_row_bcast(const T *row, const float (&reg)[(D + 63) / 64])
+{
+    float acc = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < D; c0 += 8) {
+        float x[8];
+        load8(row + c0, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            acc = fmaf(x[k], readlane(reg[(c0 + k) / 64], (c0 + k) % 64), acc);
+    }
+    return acc;
+}
+
+// Is key j masked in round r for query i because it belongs to i's
+// attended set in an earlier round?
+__device__ __forceinline__ bool owned_earlier(const uint32_t *__restrict__ meta_i,
+                                              const uint32_t *__restrict__ meta_j, int r)
+{
+    bool hit = false;
+    for (int rr = 0; rr < r; ++rr)
+        hit |= in_window(meta_i[rr], rec_lo(meta_j[rr]));
+    return hit;
+}
+
+// ---------------------------------------------------------------------------
+// forward: one wave per (round, sorted query row)
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scale, const T *__restrict__ q,
+                                                       const T *__restrict__ v, const uint32_t *__restrict__ meta,
+                                                       const uint32_t *__restrict__ srec,
+                                                       const float *__restrict__ rnorm, T *__restrict__ o_rounds,
+                                                       float *__restrict__ lse_rounds)
+{
+    constexpr int NC = (D + 63) / 64;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = blockIdx.y, bh = blockIdx.z;
+    const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
+    const size_t tok0 = (size_t)bh * L;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int s = (blockIdx.x * kWaves + wave) * kRowsPerWave + k;
+        if (s >= L)
+            break;
+        const uint32_t rec = sr[s];
+        const int i = (int)rec_lo(rec), w = (int)rec_hi(rec);
+        const uint32_t *mi = meta + (tok0 + i) * nh;
+        float qreg[NC], acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            qreg[c] = e < D ? ld(q, (tok0 + i) * D + e) : 0.f;
+            acc[c] = 0.f;
+        }
+        float M = -INFINITY, l = 0.f;
+        for (int kb = 0; kb < w; kb += kWave) {
+            const int idx = kb + lane;
+            bool valid = idx < w;
+            const uint32_t kr = valid ? sr[s - w + idx] : rec;
+            const int j = (int)rec_lo(kr);
+            if (valid)
+                valid = !owned_earlier(mi, meta + (tok0 + j) * nh, r);
+            const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
+            const float logit = valid ? dp * scale * rnorm[tok0 + j] : -INFINITY;
+            const float bm = wave_max(logit);
+            if (bm == -INFINITY)
+                continue;
+            const float Mn = fmaxf(M, bm);
+            const float corr = expf(M - Mn);
+            const float p = valid ? expf(logit - Mn) : 0.f;
+            l = l * corr + wave_sum(p);
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                acc[c] *= corr;
+            M = Mn;
+            const int nk = min(kWave, w - kb);
+            for (int kk = 0; kk < nk; ++kk) {
+                const float pk = readlane(p, kk);
+                if (pk == 0.f)
+                    continue;
+                const int jk = readlane(j, kk);
+                const T *vj = v + (tok0 + jk) * D;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int e = c * 64 + lane;
+                    if (e < D)
+                        acc[c] = fmaf(pk, ld(vj, e), acc[c]);
+                }
+            }
+        }
+        const size_t orow = ((size_t)bh * nh + r) * L + i;
+        const float inv_l = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            if (e < D)
+                o_rounds[orow * D + e] = from_f<T>(acc[c] * inv_l);
+        }
+        if (lane == 0)
+            lse_rounds[orow] = l > 0.f ? M + logf(l) : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// combine: one wave per token
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void combine_kernel(int L, int nh, int ntok, float scale,
+                                                           const T *__restrict__ q, const T *__restrict__ v,
+                                                           const T *__restrict__ o_rounds,
+                                                           const float *__restrict__ lse_rounds,
+                                                           T *__restrict__ out, float *__restrict__ lse)
+{
+    constexpr int NC = (D + 63) / 64;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int tok = blockIdx.x * kWaves + wave;
+    if (tok >= ntok)
+        return;
+    const int bh = tok / L, t = tok % L;
+    float M = -INFINITY;
+    for (int r = 0; r < nh; ++r)
+        M = fmaxf(M, lse_rounds[((size_t)bh * nh + r) * L + t]);
+    if (M == -INFINITY) {
+        // no member in any round: the token attends only to itself
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            if (e < D) {
+                const float x = ld(q, (size_t)tok * D + e);
+                ss = fmaf(x, x, ss);
+                out[(size_t)tok * D + e] = v[(size_t)tok * D + e];
+            }
+        }
+        ss = wave_sum(ss);
+        if (lane == 0)
+            lse[tok] = scale * sqrtf(ss);
+        return;
+    }
+    float den = 0.f;
+    for (int r = 0; r < nh; ++r)
+        den += expf(lse_rounds[((size_t)bh * nh + r) * L + t] - M);
+    const float total = M + logf(den);
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        acc[c] = 0.f;
+    for (int r = 0; r < nh; ++r) {
+        const size_t orow = ((size_t)bh * nh + r) * L + t;
+        const float wgt = expf(lse_rounds[orow] - total);
+        if (wgt == 0.f)
+            continue;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            if (e < D)
+                acc[c] = fmaf(wgt, ld(o_rounds, orow * D + e), acc[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int e = c * 64 + lane;
+        if (e < D)
+            out[(size_t)tok * D + e] = from_f<T>(acc[c]);
+    }
+    if (lane == 0)
+        lse[tok] = total;
+}
+
+// ---------------------------------------------------------------------------
+// backward, query side: dq_i of round r (wave per sorted query row)
+//   p = exp(scale q_i.k_j - lse_i)  (global lse, so the rounds add up to the
+//   union softmax),  g = p (dO_i.v_j - D_i),  dq_i += scale g k_j.
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float scale, const T *__restrict__ q,
+                                                          const T *__restrict__ v, const T *__restrict__ dout,
+                                                          const float *__restrict__ lse,
+                                                          const float *__restrict__ Dvec,
+                                                          const uint32_t *__restrict__ meta,
+                                                          const uint32_t *__restrict__ srec,
+                                                          const float *__restrict__ rnorm,
+                                                          float *__restrict__ dq_part)
+{
+    constexpr int NC = (D + 63) / 64;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = blockIdx.y, bh = blockIdx.z;
+    const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
+    const size_t tok0 = (size_t)bh * L;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int s = (blockIdx.x * kWaves + wave) * kRowsPerWave + k;
+        if (s >= L)
+            break;
+        const uint32_t rec = sr[s];
+        const int i = (int)rec_lo(rec), w = (int)rec_hi(rec);
+        const uint32_t *mi = meta + (tok0 + i) * nh;
+        const float lse_i = lse[tok0 + i], D_i = Dvec[tok0 + i];
+        float qreg[NC], goreg[NC], acc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            qreg[c] = e < D ? ld(q, (tok0 + i) * D + e) : 0.f;
+            goreg[c] = e < D ? ld(dout, (tok0 + i) * D + e) : 0.f;
+            acc[c] = 0.f;
+        }
+        for (int kb = 0; kb < w; kb += kWave) {
+            const int idx = kb + lane;
+            bool valid = idx < w;
+            const uint32_t kr = valid ? sr[s - w + idx] : rec;
+            const int j = (int)rec_lo(kr);
+            if (valid)
+                valid = !owned_earlier(mi, meta + (tok0 + j) * nh, r);
+            const float rn = rnorm[tok0 + j];
+            const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
+            const float dv = dot_row_bcast<T, D>(v + (tok0 + j) * D, goreg);
+            const float p = valid ? expf(dp * scale * rn - lse_i) : 0.f;
+            const float coef = scale * p * (dv - D_i) * rn;
+            const int nk = min(kWave, w - kb);
+            for (int kk = 0; kk < nk; ++kk) {
+                const float ck = readlane(coef, kk);
+                if (ck == 0.f)
+                    continue;
+                const int jk = readlane(j, kk);
+                const T *qj = q + (tok0 + jk) * D;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int e = c * 64 + lane;
+                    if (e < D)
+                        acc[c] = fmaf(ck, ld(qj, e), acc[c]);
+                }
+            }
+        }
+        const size_t orow = ((size_t)bh * nh + r) * L + i;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            if (e < D)
+                dq_part[orow * D + e] = acc[c];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward, key side: dk_j and dv_j of round r (wave per sorted key row).
+// The queries whose round-r set holds key j (sorted index s) are the sorted
+// rows s' > s with s' - w(s') <= s; win_lo is non-decreasing along the sorted
+// order, so they form a prefix of s+1, s+2, ...
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float scale, const T *__restrict__ q,
+                                                           const T *__restrict__ v, const T *__restrict__ dout,
+                                                           const float *__restrict__ lse,
+                                                           const float *__restrict__ Dvec,
+                                                           const uint32_t *__restrict__ meta,
+                                                           const uint32_t *__restrict__ srec,
+                                                           const float *__restrict__ rnorm,
+                                                           float *__restrict__ dk_part, float *__restrict__ dv_part)
+{
+    constexpr int NC = (D + 63) / 64;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int r = blockIdx.y, bh = blockIdx.z;
+    const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
+    const size_t tok0 = (size_t)bh * L;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int s = (blockIdx.x * kWaves + wave) * kRowsPerWave + k;
+        if (s >= L)
+            break;
+        const int j = (int)rec_lo(sr[s]);
+        const uint32_t *mj = meta + (tok0 + j) * nh;
+        const float rn = rnorm[tok0 + j];
+        float kreg[NC], vreg[NC], dk[NC], dv[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            kreg[c] = e < D ? ld(q, (tok0 + j) * D + e) * rn : 0.f;
+            vreg[c] = e < D ? ld(v, (tok0 + j) * D + e) : 0.f;
+            dk[c] = dv[c] = 0.f;
+        }
+        for (int qb = s + 1; qb < L; qb += kWave) {
+            const int si = qb + lane;
+            bool inwin = false;
+            int i = j;
+            if (si < L) {
+                const uint32_t qrec = sr[si];
+                i = (int)rec_lo(qrec);
+                inwin = (si - (int)rec_hi(qrec)) <= s;
+            }
+            const bool more = __ballot(!inwin) == 0ull;  // whole batch in window: look further
+            bool valid = inwin;
+            if (valid)
+                valid = !owned_earlier(meta + (tok0 + i) * nh, mj, r);
+            const float dp = dot_row_bcast<T, D>(q + (tok0 + i) * D, kreg);
+            const float dg = dot_row_bcast<T, D>(dout + (tok0 + i) * D, vreg);
+            const float p = valid ? expf(dp * scale - lse[tok0 + i]) : 0.f;
+            const float g = valid ? scale * p * (dg - Dvec[tok0 + i]) : 0.f;
+            const int nk = min(kWave, L - qb);
+            for (int kk = 0; kk < nk; ++kk) {
+                const float pk = readlane(p, kk);
+                if (pk == 0.f)
+                    continue;
+                const float gk = readlane(g, kk);
+                const int ik = readlane(i, kk);
+                const T *qi = q + (tok0 + ik) * D, *gi = dout + (tok0 + ik) * D;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int e = c * 64 + lane;
+                    if (e < D) {
+                        dv[c] = fmaf(pk, ld(gi, e), dv[c]);
+                        dk[c] = fmaf(gk, ld(qi, e), dk[c]);
+                    }
+                }
+            }
+            if (!more)
+                break;
+        }
+        const size_t orow = ((size_t)bh * nh + r) * L + j;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            if (e < D) {
+                dk_part[orow * D + e] = dk[c];
+                dv_part[orow * D + e] = dv[c];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward reduce: sum the rounds, pass dk through k = q/|q|, add the
+// self-only rows' dO to dv.  One wave per token.
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int ntok, const T *__restrict__ q,
+                                                              const T *__restrict__ dout,
+                                                              const uint32_t *__restrict__ meta,
+                                                              const float *__restrict__ rnorm,
+                                                              const float *__restrict__ dq_part,
+                                                              const float *__restrict__ dk_part,
+                                                              const float *__restrict__ dv_part,
+                                                              T *__restrict__ dq, T *__restrict__ dv)
+{
+    constexpr int NC = (D + 63) / 64;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int tok = blockIdx.x * kWaves + wave;
+    if (tok >= ntok)
+        return;
+    const int bh = tok / L, t = tok % L;
+    float aq[NC], ak[NC], av[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        aq[c] = ak[c] = av[c] = 0.f;
+    bool alone = true;
+    for (int r = 0; r < nh; ++r) {
+        alone &= rec_hi(meta[(size_t)tok * nh + r]) == 0u;
+        const size_t row = (((size_t)bh * nh + r) * L + t) * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int e = c * 64 + lane;
+            if (e < D) {
+                aq[c] += dq_part[row + e];
+                ak[c] += dk_part[row + e];
+                av[c] += dv_part[row + e];
+            }
+        }
+    }
+    const float rn = rnorm[tok];
+    float kreg[NC], kd = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int e = c * 64 + lane;
+        kreg[c] = e < D ? ld(q, (size_t)tok * D + e) * rn : 0.f;
+        kd = fmaf(kreg[c], ak[c], kd);
+    }
+    kd = wave_sum(kd);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int e = c * 64 + lane;
+        if (e < D) {
+            float gv = av[c];
+            if (alone)
+                gv += ld(dout, (size_t)tok * D + e);
+            dq[(size_t)tok * D + e] = from_f<T>(aq[c] + (ak[c] - kreg[c] * kd) * rn);
+            dv[(size_t)tok * D + e] = from_f<T>(gv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+template <typename T, int D>
+hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32_t *win_lo, uint32_t *meta,
+                   uint32_t *srec, float *rnorm, const void *out, const void *dout, float *Dv, hipStream_t st)
+{
+    dim3 grid((P.L + kThreads - 1) / kThreads, P.BH());
+    hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, (const T *)q, inv, win_lo,
+                       meta, srec, rnorm, (const T *)out, (const T *)dout, Dv);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
+                  const float *rnorm, void *o_rounds, float *lse_rounds, hipStream_t st)
+{
+    const int rows = kWaves * kRowsPerWave;
+    dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
+    hipLaunchKernelGGL((fwd_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
+                       (const T *)v, meta, srec, rnorm, (T *)o_rounds, lse_rounds);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o_rounds, const float *lse_rounds,
+                      void *out, float *lse, hipStream_t st)
+{
+    const int ntok = P.BH() * P.L;
+    dim3 grid((ntok + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((combine_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, ntok, P.scale,
+                       (const T *)q, (const T *)v, (const T *)o_rounds, lse_rounds, (T *)out, lse);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
+                  const float *Dv, const uint32_t *meta, const uint32_t *srec, const float *rnorm, float *dq_part,
+                  float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t st)
+{
+    const int rows = kWaves * kRowsPerWave;
+    dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
+                       (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dq_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
+                       (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dk_part, dv_part);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    const int ntok = P.BH() * P.L;
+    hipLaunchKernelGGL((bwd_reduce_kernel<T, D>), dim3((ntok + kWaves - 1) / kWaves), dim3(kThreads), 0, st,
+                       P.L, P.nh, ntok, (const T *)q, (const T *)dout, meta, rnorm, dq_part, dk_part, dv_part,
+                       (T *)dq, (T *)dv);
+    return hipGetLastError();
+}
+
+#define LSH_DISPATCH(dtype, d, CALL)                                                                          \
+    do {                                                                                                      \
+        if ((dtype) == LSH_BF16) {                                                                            \
+            if ((d) == 32) { using T = bf16; constexpr int D = 32; return CALL; }                             \
+            if ((d) == 64) { using T = bf16; constexpr int D = 64; return CALL; }                             \
+            if ((d) == 128) { using T = bf16; constexpr int D = 128; return CALL; }                           \
+        } else {                                                                                              \
+            if ((d) == 32) { using T = float; constexpr int D = 32; return CALL; }                            \
+            if ((d) == 64) { using T = float; constexpr int D = 64; return CALL; }                            \
+            if ((d) == 128) { using T = float; constexpr int D = 128; return CALL; }                          \
+        }                                                                                                     \
+        return hipErrorInvalidValue;                                                                          \
+    } while (0)
+
+}  // namespace
+
+hipError_t launch_prep(const Dims &P, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, float *rnorm, const void *out,
+                       const void *dout, float *Dv, hipStream_t st)
+{
+    (void)perm;
+    LSH_DISPATCH(dtype, P.d, (prep_go<T, D>(P, q, inv, win_lo, meta, srec, rnorm, out, dout, Dv, st)));
+}
+
+hipError_t launch_attn_fwd(const Dims &P, int dtype, const void *q, const void *v, const uint32_t *meta,
+                           const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
+                           hipStream_t st)
+{
+    LSH_DISPATCH(dtype, P.d, (fwd_go<T, D>(P, q, v, meta, srec, rnorm, o_rounds, lse_rounds, st)));
+}
+
+hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v, const void *o_rounds,
+                          const float *lse_rounds, void *out, float *lse, hipStream_t st)
+{
+    LSH_DISPATCH(dtype, P.d, (combine_go<T, D>(P, q, v, o_rounds, lse_rounds, out, lse, st)));
+}
+
+hipError_t launch_attn_bwd(const Dims &P, int dtype, const void *q, const void *v, const void *dout,
+                           const float *lse, const float *Dv, const uint32_t *meta, const uint32_t *srec,
+                           const float *rnorm, float *dq_part, float *dk_part, float *dv_part, void *dq, void *dv,
+                           hipStream_t st)
+{
+    LSH_DISPATCH(dtype, P.d,
+                 (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, rnorm, dq_part, dk_part, dv_part, dq, dv, st)));
+}
+
+}  // namespace lsh

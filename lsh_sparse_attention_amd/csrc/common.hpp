@@ -1,0 +1,138 @@
+// common.hpp -- internal helpers shared by the gfx950 kernels of liblsh.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsh.h"
+
+namespace lsh {
+
+constexpr int kWave = 64;
+
+// bf16 stored as raw bits.
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x)
+{
+    // round to nearest even; NaN stays NaN
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return bf16{uint16_t((u >> 16) | 0x40u)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16{uint16_t(u >> 16)};
+}
+
+template <typename T> __device__ __forceinline__ float ld(const T *p, size_t i) { return to_f(p[i]); }
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x = fmaxf(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+
+// Packed per-(position, round) record: low 16 bits = sorted index of the
+// position in that round, high 16 bits = w = sorted index - win_lo, the number
+// of members of the round's attended set other than the position itself.
+// Sorted-order record: low 16 bits = position, high 16 bits = w.
+__device__ __forceinline__ uint32_t rec_lo(uint32_t r) { return r & 0xffffu; }
+__device__ __forceinline__ uint32_t rec_hi(uint32_t r) { return r >> 16; }
+
+// Is key j (sorted index sj in round r') a member other than i of the
+// round-r' attended set of query i, given i's record (si, wi) for r'?
+// The set without i is the sorted range [si - wi, si - 1].
+__device__ __forceinline__ bool in_window(uint32_t qrec, uint32_t sj)
+{
+    uint32_t si = rec_lo(qrec), wi = rec_hi(qrec);
+    return (si - 1u - sj) < wi;   // unsigned: 0 <= si-1-sj < wi
+}
+
+struct Dims {
+    int B, H, L, d, nh, nb, m;
+    float scale;
+    int BH() const { return B * H; }
+};
+
+inline Dims dims_of(const lsh_problem_t *p)
+{
+    return Dims{p->batch, p->heads, p->seq_len, p->head_dim, p->n_hashes, p->n_buckets, p->chunk_len,
+                p->scale};
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Launch helpers implemented per kernel file; all return hipError_t.
+hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, int32_t *buckets,
+                       hipStream_t);
+hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv,
+                       int32_t *win_lo, void *ws, hipStream_t);
+size_t sort_ws_bytes(const Dims &);
+hipError_t launch_prep(const Dims &, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, float *rnorm,
+                       const void *out, const void *dout, float *D, hipStream_t);
+hipError_t launch_attn_fwd(const Dims &, int dtype, const void *q, const void *v, const uint32_t *meta,
+                           const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
+                           hipStream_t);
+hipError_t launch_combine(const Dims &, int dtype, const void *q, const void *v, const void *o_rounds,
+                          const float *lse_rounds, void *out, float *lse, hipStream_t);
+hipError_t launch_attn_bwd(const Dims &, int dtype, const void *q, const void *v, const void *dout,
+                           const float *lse, const float *D, const uint32_t *meta, const uint32_t *srec,
+                           const float *rnorm, float *dq_part, float *dk_part, float *dv_part,
+                           void *dq, void *dv, hipStream_t);
+
+}  // namespace lsh
+
+namespace lsh {
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ void load8(const bf16 *p, float out[8])
+{
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[2 * k] = __uint_as_float(w[k] << 16);
+        out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ void load8(const float *p, float out[8])
+{
+    float4 a = *reinterpret_cast<const float4 *>(p);
+    float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+__device__ __forceinline__ float readlane(float x, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+__device__ __forceinline__ int readlane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
+
+// Order LDS traffic of the lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace lsh

@@ -1,0 +1,191 @@
+// lsh_api.cpp -- the C ABI of liblsh: argument validation, workspace layout
+// and launches.  Declarations and contracts are in include/lsh.h.
+#include <math.h>
+
+#include "common.hpp"
+
+using namespace lsh;
+
+namespace {
+
+constexpr int kMaxHashes = 16;
+constexpr int kMaxLen = 65536;   // sorted indices and positions are packed in 16 bits
+constexpr int kMaxBucketsAbi = 4096;
+
+int validate(const lsh_problem_t *p)
+{
+    if (!p)
+        return LSH_ERR_INVALID;
+    if (p->batch < 1 || p->heads < 1 || p->seq_len < 1 || p->head_dim < 1 || p->n_hashes < 1 ||
+        p->n_buckets < 2 || (p->n_buckets & 1) || p->chunk_len < 1 || p->seq_len % p->chunk_len ||
+        !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16))
+        return LSH_ERR_INVALID;
+    if (p->causal != 1)
+        return LSH_ERR_UNSUPPORTED;
+    if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128)
+        return LSH_ERR_UNSUPPORTED;
+    if (p->seq_len > kMaxLen || p->n_hashes > kMaxHashes || p->n_buckets > kMaxBucketsAbi)
+        return LSH_ERR_UNSUPPORTED;
+    // every element index must fit in size_t arithmetic and every segment count in int
+    const double tok_rounds = (double)p->batch * p->heads * p->n_hashes * p->seq_len;
+    if (tok_rounds > 2147483647.0)
+        return LSH_ERR_UNSUPPORTED;
+    return LSH_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
+
+struct FwdWs {
+    uint32_t *meta, *srec;
+    float *rnorm;
+    size_t bytes;
+};
+
+struct BwdWs {
+    uint32_t *meta, *srec;
+    float *rnorm, *D, *dq_part, *dk_part, *dv_part;
+    size_t bytes;
+};
+
+FwdWs fwd_layout(const Dims &P, void *base)
+{
+    const size_t tok = (size_t)P.BH() * P.L, rnd = tok * P.nh;
+    const uintptr_t b = (uintptr_t)base;
+    FwdWs w{};
+    size_t o = 0;
+    w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
+    w.bytes = o;
+    return w;
+}
+
+BwdWs bwd_layout(const Dims &P, void *base)
+{
+    const size_t tok = (size_t)P.BH() * P.L, rnd = tok * P.nh, part = rnd * P.d * sizeof(float);
+    const uintptr_t b = (uintptr_t)base;
+    BwdWs w{};
+    size_t o = 0;
+    w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
+    w.D = (float *)(b + o); o += align_up(tok * 4, 256);
+    w.dq_part = (float *)(b + o); o += align_up(part, 256);
+    w.dk_part = (float *)(b + o); o += align_up(part, 256);
+    w.dv_part = (float *)(b + o); o += align_up(part, 256);
+    w.bytes = o;
+    return w;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *lsh_status_string(int status)
+{
+    switch (status) {
+    case LSH_OK: return "ok";
+    case LSH_ERR_INVALID: return "invalid argument";
+    case LSH_ERR_UNSUPPORTED: return "unsupported problem";
+    case LSH_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int lsh_version(void) { return 100; }
+
+size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
+{
+    if (validate(prob) != LSH_OK)
+        return 0;
+    const Dims P = dims_of(prob);
+    switch (kind) {
+    case LSH_WS_SORT: return sort_ws_bytes(P);
+    case LSH_WS_FWD: return fwd_layout(P, nullptr).bytes;
+    case LSH_WS_BWD: return bwd_layout(P, nullptr).bytes;
+    default: return 0;
+    }
+}
+
+int lsh_hash(const lsh_problem_t *prob, const void *q, const void *rot, int32_t *buckets, void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK)
+        return st;
+    if (!q || !rot || !buckets || !aligned16(q) || !aligned16(rot) || !aligned16(buckets))
+        return LSH_ERR_INVALID;
+    return hip_status(launch_hash(dims_of(prob), prob->dtype, q, rot, buckets, (hipStream_t)stream));
+}
+
+int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, int32_t *inv, int32_t *win_lo,
+             void *ws, size_t ws_bytes, void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK)
+        return st;
+    const Dims P = dims_of(prob);
+    if (!buckets || !perm || !inv || !win_lo || !ws || ws_bytes < sort_ws_bytes(P) || ((uintptr_t)ws & 255u))
+        return LSH_ERR_INVALID;
+    return hip_status(launch_sort(P, buckets, perm, inv, win_lo, ws, (hipStream_t)stream));
+}
+
+int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const int32_t *perm, const int32_t *inv,
+                 const int32_t *win_lo, void *o_rounds, float *lse_rounds, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK)
+        return st;
+    const Dims P = dims_of(prob);
+    if (!q || !v || !perm || !inv || !win_lo || !o_rounds || !lse_rounds || !ws || ((uintptr_t)ws & 255u) ||
+        !aligned16(q) || !aligned16(v) || !aligned16(o_rounds))
+        return LSH_ERR_INVALID;
+    const FwdWs w = fwd_layout(P, ws);
+    if (ws_bytes < w.bytes)
+        return LSH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, nullptr, nullptr,
+                               nullptr, s);
+    if (e == hipSuccess)
+        e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
+    return hip_status(e);
+}
+
+int lsh_combine(const lsh_problem_t *prob, const void *q, const void *v, const void *o_rounds,
+                const float *lse_rounds, void *out, float *lse, void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK)
+        return st;
+    if (!q || !v || !o_rounds || !lse_rounds || !out || !lse || !aligned16(q) || !aligned16(v) ||
+        !aligned16(o_rounds) || !aligned16(out))
+        return LSH_ERR_INVALID;
+    return hip_status(
+        launch_combine(dims_of(prob), prob->dtype, q, v, o_rounds, lse_rounds, out, lse, (hipStream_t)stream));
+}
+
+int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void *out, const void *dout,
+                 const float *lse, const int32_t *perm, const int32_t *inv, const int32_t *win_lo, void *dq, void *dv,
+                 void *ws, size_t ws_bytes, void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK)
+        return st;
+    const Dims P = dims_of(prob);
+    if (!q || !v || !out || !dout || !lse || !perm || !inv || !win_lo || !dq || !dv || !ws ||
+        ((uintptr_t)ws & 255u) || !aligned16(q) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dv))
+        return LSH_ERR_INVALID;
+    const BwdWs w = bwd_layout(P, ws);
+    if (ws_bytes < w.bytes)
+        return LSH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, out, dout, w.D, s);
+    if (e == hipSuccess)
+        e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part, w.dk_part,
+                            w.dv_part, dq, dv, s);
+    return hip_status(e);
+}
+
+}  // extern "C"

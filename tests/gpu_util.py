@@ -1,0 +1,112 @@
+"""Helpers of the GPU parity tests: run the library through its C ABI on
+seeded inputs, run the oracle on the same inputs, compare."""
+import os
+import sys
+
+import numpy as np
+import torch
+
+import lsh_sparse_attention_amd as lsh
+from lsh_sparse_attention_amd import inputs as gen
+from oracle import oracle as ora
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def to_f64(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def run_gpu(x, backward=True, rounds=False):
+    cfg = x["cfg"]
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype)
+    q = to_device(x["q"], cfg.dtype)
+    v = to_device(x["v"], cfg.dtype)
+    rot = to_device(x["rot"], cfg.dtype)
+    mod = lsh.LshAttention(prob, backward=backward)
+    mod.forward(q, v, rot)
+    res = {}
+    if backward:
+        do = to_device(x["dout"], cfg.dtype)
+        mod.backward(q, v, do)
+    torch.cuda.synchronize()
+    for k in ("buckets", "perm", "inv", "win_lo"):
+        res[k] = getattr(mod, k).cpu().numpy()
+    res["out"] = to_f64(mod.out)
+    res["lse"] = mod.lse.cpu().numpy().astype(np.float64)
+    if rounds:
+        res["o_rounds"] = to_f64(mod.o_rounds)
+        res["lse_rounds"] = mod.lse_rounds.cpu().numpy().astype(np.float64)
+    if backward:
+        res["dq"] = to_f64(mod.dq)
+        res["dv"] = to_f64(mod.dv)
+    del mod
+    return res
+
+
+def assert_close(name, got, want, tol):
+    err = np.abs(got - want)
+    bad = err > tol + tol * np.abs(want)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{name}: {bad.sum()} of {bad.size} outside atol=rtol={tol}; max abs err "
+                             f"{err.max():.3e}; first at {idx.tolist()}: got {got[tuple(idx[0])]} "
+                             f"want {want[tuple(idx[0])]}")
+
+
+def check_sort_properties(res, cfg):
+    """Any-size properties of lsh_sort's output, for every (b, h, round)."""
+    B, H, nh, L = res["buckets"].shape
+    m = cfg.chunk_len
+    bk = res["buckets"].reshape(-1, L)
+    perm = res["perm"].reshape(-1, L)
+    inv = res["inv"].reshape(-1, L)
+    wl = res["win_lo"].reshape(-1, L)
+    assert bk.min() >= 0 and bk.max() < cfg.n_buckets
+    ar = np.arange(L)
+    for s in range(bk.shape[0]):
+        p = perm[s]
+        assert np.array_equal(np.sort(p), ar), "perm is not a permutation"
+        assert np.array_equal(inv[s][p], ar), "inv is not perm^-1"
+        sb = bk[s][p]
+        assert np.all(np.diff(sb) >= 0), "not sorted by bucket"
+        assert np.all(np.diff(p)[np.diff(sb) == 0] > 0), "not stable"
+        first = np.searchsorted(sb, sb, side="left")       # first sorted index of each sorted row's bucket
+        start_of_pos = np.empty(L, np.int64)
+        start_of_pos[p] = first
+        want = np.maximum(start_of_pos, (inv[s] // m - 1) * m)
+        assert np.array_equal(wl[s], want), "win_lo"
+
+
+def compare_slices(x, res, slices, backward=True, check_rounds=True):
+    """Bit-exact hash/sort and toleranced outputs against the oracle for (b, h) slices."""
+    cfg = x["cfg"]
+    tol = TOL[cfg.dtype]
+    ores = ora.run_inputs(x, slices=slices, backward=backward)
+    for (b, h), o in ores.items():
+        tag = f"{cfg.name}[b={b},h={h}]"
+        for k in ("buckets", "perm", "inv", "win_lo"):
+            got = res[k][b, h]
+            if not np.array_equal(got, o[k]):
+                n = int((got != o[k]).sum())
+                raise AssertionError(f"{tag} {k}: {n} mismatches")
+        assert_close(tag + " out", res["out"][b, h], o["out"], tol)
+        assert_close(tag + " lse", res["lse"][b, h], o["lse"], tol)
+        if backward:
+            assert_close(tag + " dq", res["dq"][b, h], o["dq"], tol)
+            assert_close(tag + " dv", res["dv"][b, h], o["dv"], tol)
+    return ores

@@ -1,0 +1,88 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every symbol that include/lsh.h declares, and validates arguments before
+launching anything (all calls here return before touching a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lsh_sparse_attention_amd import _lib
+import lsh_sparse_attention_amd as lsh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lsh.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(lsh_[a-z_]+)\s*\(", src))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    declared = _declared()
+    assert declared == set(_lib.SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_status_strings_and_version():
+    L = _lib.lib()
+    assert L.lsh_version() >= 100
+    assert L.lsh_status_string(0) == b"ok"
+    assert b"unsupported" in L.lsh_status_string(2)
+    assert L.lsh_status_string(99) == b"unknown status"
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=2, seq_len=256, head_dim=64, n_hashes=2, n_buckets=16, chunk_len=32)
+    base.update(kw)
+    return lsh.problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_buckets=15), 1), (dict(n_buckets=0), 1), (dict(chunk_len=48), 1), (dict(seq_len=0), 1),
+    (dict(head_dim=48), 2), (dict(seq_len=65536 * 2, chunk_len=64), 2), (dict(n_hashes=17), 2),
+    (dict(n_buckets=8192), 2),
+])
+def test_invalid_problems_rejected_before_launch(kw, status):
+    p = _prob(**kw)
+    L = _lib.lib()
+    dummy = ctypes.c_void_p(256)
+    assert L.lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == status
+    assert L.lsh_workspace_bytes(ctypes.byref(p), 0) == 0
+
+
+def test_non_causal_is_unsupported():
+    p = _prob()
+    p.causal = 0
+    dummy = ctypes.c_void_p(256)
+    assert _lib.lib().lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == 2
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = _prob()
+    L = _lib.lib()
+    ok = ctypes.c_void_p(1 << 20)
+    assert L.lsh_hash(ctypes.byref(p), None, ok, ok, None) == 1
+    assert L.lsh_hash(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), ok, ok, None) == 1
+    ws = L.lsh_workspace_bytes(ctypes.byref(p), _lib.LSH_WS_SORT)
+    assert ws > 0
+    # too small a workspace, or one that is not 256-byte aligned
+    assert L.lsh_sort(ctypes.byref(p), ok, ok, ok, ok, ok, ctypes.c_size_t(ws - 1), None) == 1
+    assert L.lsh_sort(ctypes.byref(p), ok, ok, ok, ok, ctypes.c_void_p((1 << 20) + 16), ctypes.c_size_t(ws),
+                      None) == 1
+    assert L.lsh_attn_fwd(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, None, ctypes.c_size_t(0), None) == 1
+    assert L.lsh_attn_bwd(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ctypes.c_size_t(1),
+                          None) == 1
+    assert L.lsh_combine(ctypes.byref(p), ok, ok, None, ok, ok, ok, None) == 1
+    assert L.lsh_attn_fwd(None, ok, ok, ok, ok, ok, ok, ok, ok, ctypes.c_size_t(1 << 30), None) == 1
+
+
+def test_workspace_sizes_grow_with_problem():
+    small = _prob()
+    big = _prob(batch=4)
+    for k in (0, 1, 2):
+        assert 0 < lsh.workspace_bytes(small, k) < lsh.workspace_bytes(big, k)
+        assert lsh.workspace_bytes(small, k) % 256 == 0
