@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark: shared-QK LSH attention forward + backward on one MI355X.
+
+One step is the whole hot path over one batch of synthetic input already
+resident in HBM: hash, sort, per-round chunk attention (with the unsort),
+logsumexp combine, and the backward (per-round query- and key-side gradients,
+reduction over rounds, key normalisation).  The default workload is the
+64K-token text-shaped case (B=1, H=8, L=65536, d=128, 1024 buckets, 4 hash
+rounds, chunk 128, bf16).
+
+Prints one JSON line: tokens/s (B*L per step), the roofline of the dominant
+kernel (its HIP-event-timed average launch against MI355X peak), and the fp64
+CPU oracle timed on the host cores on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config text]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSH-attention fwd+bwd tokens/s at L=64K on 1 MI355X; % MFMA / HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+WORKLOAD_NAMES = {
+    "tiny": "tiny fp32 forward+backward (L=1024)",
+    "mid": "mid-size (B=8, H=8, L=4096)",
+    "image": "image-generation-shaped (L=12288 = 64x64x3)",
+    "text": "long-text-shaped (L=65536)",
+    "stress": "stress: 256-cluster Gaussian mixture (B=4, L=65536)",
+}
+# source file of each kernel, for matching stored counter measurements
+KERNEL_SOURCE = {
+    "hash": "hash.hip", "sort_hist": "sort.hip", "sort_scan": "sort.hip", "sort_scatter": "sort.hip",
+    "prep": "attn_generic.hip", "attn_fwd": "attn_generic.hip", "combine": "attn_generic.hip",
+    "bwd_dq": "attn_generic.hip", "bwd_dkv": "attn_generic.hip", "bwd_reduce": "attn_generic.hip",
+}
+
+
+def algorithmic_work(name: str, cfg) -> tuple[float, float]:
+    """(flops, bytes) that one launch of kernel `name` must do for `cfg`.
+
+    Counts the minimal data movement of each kernel (every input read once,
+    every output written once) and the dense-tile flops of the method
+    (nominal m x 2m chunk tiles, chunk 0 sees m keys)."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    B, H, L, d, nh, nb, m = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets, cfg.chunk_len
+    T = B * H * L
+    Tr = T * nh
+    S = B * H * nh
+    ntiles = -(-L // 2048)
+    tile_pairs = (8.0 * m * L * d - 4.0 * m * m * d) * B * H * nh / (4.0 * d)   # query-key pairs per launch
+    if name == "hash":
+        return 2.0 * T * nh * (nb // 2) * d, T * d * s + nh * d * (nb // 2) * s + Tr * 4
+    if name == "sort_hist":
+        return 0.0, Tr * 4 + S * ntiles * nb * 4
+    if name == "sort_scan":
+        return 0.0, 4 * S * ntiles * nb * 4 + S * nb * 4
+    if name == "sort_scatter":
+        return 0.0, Tr * 4 + S * ntiles * nb * 4 + Tr * 12
+    if name == "prep":
+        return 0.0, T * d * s + Tr * 16 + T * 4 + 2 * T * d * s + T * 4
+    if name == "attn_fwd":
+        return 4.0 * d * tile_pairs, Tr * (3 * d * s + 8 + 4 * nh)
+    if name == "combine":
+        return 0.0, Tr * (d * s + 4) + T * (d * s + 4)
+    if name == "bwd_dq":
+        return 6.0 * d * tile_pairs, Tr * (4 * d * s + 4 * d + 16 + 4 * nh)
+    if name == "bwd_dkv":
+        return 8.0 * d * tile_pairs, Tr * (4 * d * s + 8 * d + 16 + 4 * nh)
+    if name == "bwd_reduce":
+        return 0.0, Tr * 12 * d + T * (4 * d * s + 4 + 4 * nh)
+    raise KeyError(name)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (the process's own runtime)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        if self.h.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.h.hipEventDestroy(ev)
+
+
+def source_sha(kernel: str) -> str:
+    path = os.path.join(ROOT, "lsh_sparse_attention_amd", "csrc", KERNEL_SOURCE[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(x, heads: int):
+    from oracle import oracle as ora
+    cfg = x["cfg"]
+    heads = max(1, min(heads, cfg.heads))
+    slices = [(0, h) for h in range(heads)]
+    t0 = time.perf_counter()
+    ora.run_inputs(x, slices=slices, backward=True)
+    dt = time.perf_counter() - t0
+    tokens = cfg.seq_len * heads / cfg.heads      # the work of all heads of that many tokens
+    return {
+        "value": tokens / dt, "unit": "tokens/s", "cores": ora.threads(), "kind": "oracle",
+        "sample": (f"batch 0, heads 0..{heads - 1} of {cfg.heads} at full L={cfg.seq_len}: hash, sort, "
+                   f"forward and backward in fp64; {dt:.1f} s; tokens counted as L*{heads}/{cfg.heads}"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="text")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads of batch 0 the oracle times (0: skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the path is per-(batch, head) independent and is not sharded here.", file=sys.stderr)
+        return 2
+
+    import torch
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    from lsh_sparse_attention_amd import inputs as gen
+
+    cfg = gen.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    x = gen.generate(cfg, with_grad=True)
+    print(f"[bench] generated {cfg.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    def dev(a):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, v, rot, do = dev(x["q"]), dev(x["v"]), dev(x["rot"]), dev(x["dout"])
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype)
+    mod = lsh.LshAttention(prob)
+    L = _lib.lib()
+    hip = Hip()
+    nk = len(_lib.KERNELS)
+
+    def step():
+        mod.forward(q, v, rot)
+        mod.backward(q, v, do)
+
+    for _ in range(max(0, args.warmup - 1)):
+        step()
+    torch.cuda.synchronize()
+    # last warmup step: every kernel bracketed, to find the dominant one
+    evs = [(hip.event(), hip.event()) for _ in range(nk)]
+    for k, (a, b) in enumerate(evs):
+        L.lsh_profile_kernel(k, a, b)
+    step()
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for k, (a, b) in enumerate(evs):
+        per_kernel[_lib.KERNELS[k]] = hip.elapsed_ms(a, b) * 1e3
+        L.lsh_profile_kernel(k, None, None)
+    dominant = max(per_kernel, key=per_kernel.get)
+    dk = _lib.KERNELS.index(dominant)
+
+    # timed region: K steps, the dominant kernel bracketed by HIP events on
+    # the stream it is launched on (the current torch stream)
+    pairs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        L.lsh_profile_kernel(dk, a, b)
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    L.lsh_profile_kernel(dk, None, None)
+    kern_ms = sum(hip.elapsed_ms(a, b) for a, b in pairs) / len(pairs)
+    for a, b in pairs + evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = cfg.batch * cfg.seq_len * args.steps / elapsed
+    flops, nbytes = algorithmic_work(dominant, cfg)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma > t_hbm:
+        roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[cfg.dtype],
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(dominant, cfg.name)
+    roof["kernel"] = dominant
+    roof["kernel_us"] = kern_ms * 1e3
+    roof["algorithmic"] = {"flops": flops, "bytes": nbytes}
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES.get(cfg.name, cfg.name), "name": cfg.name, "batch": cfg.batch,
+                   "heads": cfg.heads, "seq_len": cfg.seq_len, "head_dim": cfg.head_dim,
+                   "n_buckets": cfg.n_buckets, "n_hashes": cfg.n_hashes, "chunk_len": cfg.chunk_len,
+                   "causal": True, "clustered_inputs": cfg.clustered},
+        "roofline": roof,
+        "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+    }
+    del mod
+    torch.cuda.empty_cache()
+    if args.cpu_heads > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -167,6 +167,40 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
                  const int32_t *win_lo, void *dq, void *dv, void *ws, size_t ws_bytes,
                  void *stream);
 
+/*
+ * Instrumentation (not needed to compute anything).
+ *
+ * Kernels of the library, for lsh_profile_kernel and lsh_kernel_name.
+ */
+typedef enum {
+    LSH_KERNEL_HASH = 0,        /* lsh_hash: rotation + argmax                      */
+    LSH_KERNEL_SORT_HIST = 1,   /* lsh_sort: per-tile bucket counts                 */
+    LSH_KERNEL_SORT_SCAN = 2,   /* lsh_sort: offsets of (tile, bucket) runs         */
+    LSH_KERNEL_SORT_SCATTER = 3,/* lsh_sort: stable ranks, perm / inv / win_lo      */
+    LSH_KERNEL_PREP = 4,        /* lsh_attn_fwd / lsh_attn_bwd: packed records,
+                                   inverse norms (and dO . O in the backward)      */
+    LSH_KERNEL_FWD = 5,         /* lsh_attn_fwd: per-round chunk attention          */
+    LSH_KERNEL_COMBINE = 6,     /* lsh_combine                                      */
+    LSH_KERNEL_BWD_DQ = 7,      /* lsh_attn_bwd: query-side gradient per round      */
+    LSH_KERNEL_BWD_DKV = 8,     /* lsh_attn_bwd: key-side gradients per round       */
+    LSH_KERNEL_BWD_REDUCE = 9,  /* lsh_attn_bwd: sum over rounds, key normalisation */
+    LSH_KERNEL_COUNT = 10
+} lsh_kernel_t;
+
+/* Name of a kernel id (static storage), or NULL for an unknown id. */
+const char *lsh_kernel_name(int kernel);
+
+/*
+ * lsh_profile_kernel -- bracket every later launch of `kernel` with
+ * hipEventRecord(start_event) before it and hipEventRecord(stop_event) after
+ * it, on the stream the kernel is launched on.  start_event and stop_event
+ * are hipEvent_t handles owned by the caller; passing NULL for either clears
+ * the bracket.  The setting is process-wide and not synchronised: set it from
+ * the thread that launches, between calls.  Returns LSH_ERR_INVALID for an
+ * unknown kernel id.
+ */
+int lsh_profile_kernel(int kernel, void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

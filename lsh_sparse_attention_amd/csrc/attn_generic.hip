@@ -469,6 +469,7 @@ hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32
                    uint32_t *srec, float *rnorm, const void *out, const void *dout, float *Dv, hipStream_t st)
 {
     dim3 grid((P.L + kThreads - 1) / kThreads, P.BH());
+    ProfScope prof(LSH_KERNEL_PREP, st);
     hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, (const T *)q, inv, win_lo,
                        meta, srec, rnorm, (const T *)out, (const T *)dout, Dv);
     return hipGetLastError();
@@ -480,6 +481,7 @@ hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *m
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
+    ProfScope prof(LSH_KERNEL_FWD, st);
     hipLaunchKernelGGL((fwd_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
                        (const T *)v, meta, srec, rnorm, (T *)o_rounds, lse_rounds);
     return hipGetLastError();
@@ -491,6 +493,7 @@ hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o
 {
     const int ntok = P.BH() * P.L;
     dim3 grid((ntok + kWaves - 1) / kWaves);
+    ProfScope prof(LSH_KERNEL_COMBINE, st);
     hipLaunchKernelGGL((combine_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, ntok, P.scale,
                        (const T *)q, (const T *)v, (const T *)o_rounds, lse_rounds, (T *)out, lse);
     return hipGetLastError();
@@ -503,16 +506,23 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                       (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dq_part);
+    {
+        ProfScope prof(LSH_KERNEL_BWD_DQ, st);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dq_part);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                       (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dk_part, dv_part);
+    {
+        ProfScope prof(LSH_KERNEL_BWD_DKV, st);
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dk_part, dv_part);
+    }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int ntok = P.BH() * P.L;
+    ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
     hipLaunchKernelGGL((bwd_reduce_kernel<T, D>), dim3((ntok + kWaves - 1) / kWaves), dim3(kThreads), 0, st,
                        P.L, P.nh, ntok, (const T *)q, (const T *)dout, meta, rnorm, dq_part, dk_part, dv_part,
                        (T *)dq, (T *)dv);

@@ -78,6 +78,17 @@ inline Dims dims_of(const lsh_problem_t *p)
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Instrumentation brackets around kernel launches (see lsh_profile_kernel).
+void prof_begin(int kernel, hipStream_t st);
+void prof_end(int kernel, hipStream_t st);
+
+struct ProfScope {
+    int k;
+    hipStream_t s;
+    ProfScope(int kernel, hipStream_t st) : k(kernel), s(st) { prof_begin(k, s); }
+    ~ProfScope() { prof_end(k, s); }
+};
+
 // Launch helpers implemented per kernel file; all return hipError_t.
 hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, int32_t *buckets,
                        hipStream_t);

@@ -72,6 +72,7 @@ template <typename T, int D>
 hipError_t go(const Dims &P, const void *q, const void *rot, int32_t *buckets, hipStream_t st)
 {
     dim3 grid((P.L + kHashThreads - 1) / kHashThreads, P.nh, P.BH());
+    ProfScope prof(LSH_KERNEL_HASH, st);
     hipLaunchKernelGGL((hash_generic<T, D>), grid, dim3(kHashThreads), 0, st, P.L, P.nh, P.nb / 2,
                        (const T *)q, (const T *)rot, buckets);
     return hipGetLastError();

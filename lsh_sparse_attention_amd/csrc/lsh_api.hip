@@ -8,6 +8,33 @@ using namespace lsh;
 
 namespace {
 
+hipEvent_t g_prof_start[LSH_KERNEL_COUNT];
+hipEvent_t g_prof_stop[LSH_KERNEL_COUNT];
+
+const char *const kKernelNames[LSH_KERNEL_COUNT] = {
+    "hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq", "bwd_dkv",
+    "bwd_reduce"};
+
+}  // namespace
+
+namespace lsh {
+
+void prof_begin(int k, hipStream_t st)
+{
+    if (g_prof_start[k])
+        (void)hipEventRecord(g_prof_start[k], st);
+}
+
+void prof_end(int k, hipStream_t st)
+{
+    if (g_prof_stop[k])
+        (void)hipEventRecord(g_prof_stop[k], st);
+}
+
+}  // namespace lsh
+
+namespace {
+
 constexpr int kMaxHashes = 16;
 constexpr int kMaxLen = 65536;   // sorted indices and positions are packed in 16 bits
 constexpr int kMaxBucketsAbi = 4096;
@@ -95,6 +122,24 @@ const char *lsh_status_string(int status)
 }
 
 int lsh_version(void) { return 100; }
+
+const char *lsh_kernel_name(int kernel)
+{
+    return (kernel >= 0 && kernel < LSH_KERNEL_COUNT) ? kKernelNames[kernel] : nullptr;
+}
+
+int lsh_profile_kernel(int kernel, void *start_event, void *stop_event)
+{
+    if (kernel < 0 || kernel >= LSH_KERNEL_COUNT)
+        return LSH_ERR_INVALID;
+    if (!start_event || !stop_event) {
+        g_prof_start[kernel] = g_prof_stop[kernel] = nullptr;
+    } else {
+        g_prof_start[kernel] = (hipEvent_t)start_event;
+        g_prof_stop[kernel] = (hipEvent_t)stop_event;
+    }
+    return LSH_OK;
+}
 
 size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
 {

@@ -197,14 +197,22 @@ hipError_t launch_sort(const Dims &P, const int32_t *buckets, int32_t *perm, int
     while ((1 << nbits) < P.nb)
         ++nbits;
     const size_t lds_hist = (size_t)P.nb * sizeof(int32_t);
-    hipLaunchKernelGGL(sort_hist, dim3(nt, S), dim3(kScatterThreads), lds_hist, st, P.L, P.nb, nt, buckets, cnt);
+    {
+        ProfScope prof(LSH_KERNEL_SORT_HIST, st);
+        hipLaunchKernelGGL(sort_hist, dim3(nt, S), dim3(kScatterThreads), lds_hist, st, P.L, P.nb, nt, buckets,
+                           cnt);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(sort_scan, dim3(S), dim3(kScanThreads), 0, st, P.nb, nt, cnt, bstart);
+    {
+        ProfScope prof(LSH_KERNEL_SORT_SCAN, st);
+        hipLaunchKernelGGL(sort_scan, dim3(S), dim3(kScanThreads), 0, st, P.nb, nt, cnt, bstart);
+    }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const size_t lds_scatter = (size_t)(kScatterThreads / kWave) * P.nb * sizeof(int32_t);
+    ProfScope prof(LSH_KERNEL_SORT_SCATTER, st);
     hipLaunchKernelGGL(sort_scatter, dim3(nt, S), dim3(kScatterThreads), lds_scatter, st, P.L, P.nb, nbits, P.m,
                        nt, buckets, (const int32_t *)cnt, (const int32_t *)bstart, perm, inv, win_lo);
     return hipGetLastError();

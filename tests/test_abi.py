@@ -86,3 +86,12 @@ def test_workspace_sizes_grow_with_problem():
     for k in (0, 1, 2):
         assert 0 < lsh.workspace_bytes(small, k) < lsh.workspace_bytes(big, k)
         assert lsh.workspace_bytes(small, k) % 256 == 0
+
+
+def test_kernel_names_and_profile_hook():
+    L = _lib.lib()
+    names = [L.lsh_kernel_name(k).decode() for k in range(len(_lib.KERNELS))]
+    assert tuple(names) == _lib.KERNELS
+    assert L.lsh_kernel_name(len(_lib.KERNELS)) is None
+    assert L.lsh_profile_kernel(len(_lib.KERNELS), None, None) == 1
+    assert L.lsh_profile_kernel(0, None, None) == 0      # clearing needs no GPU
