@@ -500,6 +500,11 @@ hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o
 }
 
 template <typename T, int D>
+hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const float *rnorm,
+                     const float *dq_part, const float *dk_part, const float *dv_part, void *dq, void *dv,
+                     hipStream_t st);
+
+template <typename T, int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
                   const float *Dv, const uint32_t *meta, const uint32_t *srec, const float *rnorm, float *dq_part,
                   float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t st)
@@ -521,6 +526,14 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
+    return reduce_go<T, D>(P, q, dout, meta, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
+}
+
+template <typename T, int D>
+hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const float *rnorm,
+                     const float *dq_part, const float *dk_part, const float *dv_part, void *dq, void *dv,
+                     hipStream_t st)
+{
     const int ntok = P.BH() * P.L;
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
     hipLaunchKernelGGL((bwd_reduce_kernel<T, D>), dim3((ntok + kWaves - 1) / kWaves), dim3(kThreads), 0, st,
@@ -564,6 +577,13 @@ hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v
                           const float *lse_rounds, void *out, float *lse, hipStream_t st)
 {
     LSH_DISPATCH(dtype, P.d, (combine_go<T, D>(P, q, v, o_rounds, lse_rounds, out, lse, st)));
+}
+
+hipError_t launch_bwd_reduce(const Dims &P, int dtype, const void *q, const void *dout, const uint32_t *meta,
+                             const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,
+                             void *dq, void *dv, hipStream_t st)
+{
+    LSH_DISPATCH(dtype, P.d, (reduce_go<T, D>(P, q, dout, meta, rnorm, dq_part, dk_part, dv_part, dq, dv, st)));
 }
 
 hipError_t launch_attn_bwd(const Dims &P, int dtype, const void *q, const void *v, const void *dout,

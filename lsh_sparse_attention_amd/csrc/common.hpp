@@ -147,3 +147,50 @@ __device__ __forceinline__ void wave_lds_sync()
 }
 
 }  // namespace lsh
+
+namespace lsh {
+
+// MFMA operand types (gfx950 bf16 matrix instructions).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// plain 16-byte vector (HIP's uint4 is a struct that defeats register promotion of arrays)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies A[l%32][8(l/32) .. +7] and
+// B[8(l/32) .. +7][l%32]; it receives C[8g + 4(l/32) + t][l%32] in acc[4g+t].
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8(l/16) .. +7] and
+// B[8(l/16) .. +7][l%16]; it receives C[4(l/16) + t][l%16] in acc[t].
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
+
+// two fp32 -> packed bf16 pair (round to nearest even)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)from_f<bf16>(lo).bits | ((uint32_t)from_f<bf16>(hi).bits << 16);
+}
+
+hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const uint32_t *meta,
+                                const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
+                                hipStream_t);
+bool mfma_path_ok(const Dims &, int dtype);
+hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
+                                const float *D, const uint32_t *meta, const uint32_t *srec, const float *rnorm,
+                                float *dq_part, float *dk_part, float *dv_part, hipStream_t);
+hipError_t launch_bwd_reduce(const Dims &, int dtype, const void *q, const void *dout, const uint32_t *meta,
+                             const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,
+                             void *dq, void *dv, hipStream_t);
+
+}  // namespace lsh

@@ -192,8 +192,12 @@ int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, nullptr, nullptr,
                                nullptr, s);
-    if (e == hipSuccess)
-        e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
+    if (e == hipSuccess) {
+        if (mfma_path_ok(P, prob->dtype))
+            e = launch_attn_fwd_mfma(P, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
+        else
+            e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
+    }
     return hip_status(e);
 }
 
@@ -227,9 +231,18 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
         return LSH_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, out, dout, w.D, s);
-    if (e == hipSuccess)
-        e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part, w.dk_part,
-                            w.dv_part, dq, dv, s);
+    if (e == hipSuccess) {
+        if (mfma_path_ok(P, prob->dtype)) {
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part, w.dk_part,
+                                     w.dv_part, s);
+            if (e == hipSuccess)
+                e = launch_bwd_reduce(P, prob->dtype, q, dout, w.meta, w.rnorm, w.dq_part, w.dk_part, w.dv_part,
+                                      dq, dv, s);
+        } else {
+            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part,
+                                w.dk_part, w.dv_part, dq, dv, s);
+        }
+    }
     return hip_status(e);
 }
 
