@@ -1,5 +1,7 @@
 // hash.hip -- angular LSH by random rotation: bucket = argmax([qR_r ; -qR_r]).
 // "Reformer: The Efficient Transformer", §2 (random projections).
+// fp32 problems use a per-thread fp32 kernel; bf16 problems use the matrix
+// cores (exact bf16 products, fp32 sums).
 #include "common.hpp"
 
 namespace lsh {
@@ -68,6 +70,108 @@ __global__ __launch_bounds__(kHashThreads) void hash_generic(int L, int nh, int 
     buckets[((size_t)bh * nh + r) * L + t] = (best_pos >= best_neg) ? arg_pos : half + arg_neg;
 }
 
+// bf16 path on the matrix cores.  A workgroup (4 waves) owns 256 rows of one
+// (batch, head); a wave owns 64 rows as two 32-row MFMA column tiles.  For
+// every round, the rotation is walked in tiles of 32 columns, staged
+// transposed in LDS; Y^T = R^T Q^T comes out with lane = row and 16 columns
+// per lane, so the running argmax of +y and of -y stays in registers, in
+// increasing column order (strict comparisons keep the first index).  The two
+// lane halves that share a row are merged at the end.  bf16 products are exact
+// in the fp32 accumulator.
+constexpr int kHashRows = 256;
+
+template <int D>
+__global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, int half, const bf16 *__restrict__ q,
+                                                                 const bf16 *__restrict__ rot,
+                                                                 int32_t *__restrict__ buckets)
+{
+    constexpr int P = D + 8;
+    __shared__ __align__(16) uint16_t RT[32 * P];   // [column j][d]
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int h = lane / 32, c = lane % 32;
+    const int bh = blockIdx.y;
+    const int row0 = blockIdx.x * kHashRows + wave * 64;
+
+    bf16x8_t qop[2][D / 16];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int row = min(row0 + 32 * ct + c, L - 1);
+        const bf16 *qrow = q + ((size_t)bh * L + row) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qop[ct][ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
+    }
+    const uint16_t *Rbits = reinterpret_cast<const uint16_t *>(rot);
+    for (int r = 0; r < nh; ++r) {
+        const uint16_t *R = Rbits + (size_t)r * D * half;
+        float bp[2] = {-INFINITY, -INFINITY}, bn[2] = {-INFINITY, -INFINITY};
+        int ip[2] = {0, 0}, in[2] = {0, 0};
+        for (int j0 = 0; j0 < half; j0 += 32) {
+            __syncthreads();
+            // RT[jj][d] = R[d][j0 + jj], zero past the last column
+            for (int i = tid; i < D * 4; i += kHashThreads) {
+                const int d = i / 4, ch = i % 4;
+                const int j = j0 + 8 * ch;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    RT[(8 * ch + e) * P + d] = (j + e < half) ? R[(size_t)d * half + j + e] : (uint16_t)0;
+            }
+            __syncthreads();
+            const bool full = j0 + 32 <= half;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x16_t acc = f32x16_t{};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    acc = mfma32(as_bf16x8(ld16(&RT[c * P + 16 * ks + 8 * h])), qop[ct][ks], acc);
+                // acc[4 g + t] = y[column j0 + 8 g + 4 h + t] of row c
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int j = j0 + 8 * (e / 4) + 4 * h + (e % 4);
+                    const float y = acc[e];
+                    if (full || j < half) {
+                        if (y > bp[ct]) {
+                            bp[ct] = y;
+                            ip[ct] = j;
+                        }
+                        if (-y > bn[ct]) {
+                            bn[ct] = -y;
+                            in[ct] = j;
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            // merge with the other half of the row (first index on ties)
+            const float obp = __shfl_xor(bp[ct], 32, kWave), obn = __shfl_xor(bn[ct], 32, kWave);
+            const int oip = __shfl_xor(ip[ct], 32, kWave), oin = __shfl_xor(in[ct], 32, kWave);
+            if (obp > bp[ct] || (obp == bp[ct] && oip < ip[ct])) {
+                bp[ct] = obp;
+                ip[ct] = oip;
+            }
+            if (obn > bn[ct] || (obn == bn[ct] && oin < in[ct])) {
+                bn[ct] = obn;
+                in[ct] = oin;
+            }
+            const int row = row0 + 32 * ct + c;
+            if (h == 0 && row < L)
+                buckets[((size_t)bh * nh + r) * L + row] = (bp[ct] >= bn[ct]) ? ip[ct] : half + in[ct];
+        }
+    }
+}
+
+template <int D>
+hipError_t go_mfma(const Dims &P, const void *q, const void *rot, int32_t *buckets, hipStream_t st)
+{
+    dim3 grid((P.L + kHashRows - 1) / kHashRows, P.BH());
+    ProfScope prof(LSH_KERNEL_HASH, st);
+    hipLaunchKernelGGL((hash_mfma_kernel<D>), grid, dim3(kHashThreads), 0, st, P.L, P.nh, P.nb / 2,
+                       (const bf16 *)q, (const bf16 *)rot, buckets);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t go(const Dims &P, const void *q, const void *rot, int32_t *buckets, hipStream_t st)
 {
@@ -85,9 +189,9 @@ hipError_t launch_hash(const Dims &P, int dtype, const void *q, const void *rot,
 {
     if (dtype == LSH_BF16) {
         switch (P.d) {
-        case 32: return go<bf16, 32>(P, q, rot, buckets, st);
-        case 64: return go<bf16, 64>(P, q, rot, buckets, st);
-        case 128: return go<bf16, 128>(P, q, rot, buckets, st);
+        case 32: return go_mfma<32>(P, q, rot, buckets, st);
+        case 64: return go_mfma<64>(P, q, rot, buckets, st);
+        case 128: return go_mfma<128>(P, q, rot, buckets, st);
         }
     } else {
         switch (P.d) {
