@@ -13,7 +13,7 @@
 // keys that are in the query's set of an earlier round are dropped.
 //
 // Two kernels per call, each over all rounds, each writing complete per-round
-// results (no atomics, deterministic):
+// results as bf16 (no atomics, deterministic), then a reduction over rounds:
 //   bwd_dq_mfma   a workgroup owns 128 sorted query rows (wave: 32); keys
 //                 stream in blocks of 32 (lane = query, as in the forward);
 //                 dQ^T += K^T (G^T scaled per key) on the MFMA.
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
                                                                const uint32_t *__restrict__ meta,
                                                                const uint32_t *__restrict__ srec,
                                                                const float *__restrict__ rnorm,
-                                                               float *__restrict__ dq_part)
+                                                               bf16 *__restrict__ dq_part)
 {
     constexpr int P = D + 8;
     __shared__ __align__(16) uint16_t Ks[kBlk * P];
@@ -209,14 +209,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
         }
     }
 
-    // dq lane c: d = 32 dt + 8 g + 4 h + t
-    float *out = dq_part + (((size_t)bh * nh + r) * L + qpos) * D;
+    // dq lane c: d = 32 dt + 8 g + 4 h + t; stored as bf16
+    bf16 *out = dq_part + (((size_t)bh * nh + r) * L + qpos) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4 *>(out + 32 * dt + 8 * g + 4 * h) =
-                make_float4(acc[dt][4 * g + 0], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+        for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[dt][4 * g + 0], acc[dt][4 * g + 1]);
+            w.y = pack_bf16x2(acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+            *reinterpret_cast<uint2 *>(out + 32 * dt + 8 * g + 4 * h) = w;
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -232,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
                                                                 const uint32_t *__restrict__ meta,
                                                                 const uint32_t *__restrict__ srec,
                                                                 const float *__restrict__ rnorm,
-                                                                float *__restrict__ dk_part,
-                                                                float *__restrict__ dv_part)
+                                                                bf16 *__restrict__ dqk_part,
+                                                                bf16 *__restrict__ dv_part)
 {
     constexpr int P = D + 8;
     __shared__ __align__(16) uint16_t Qs[kBlk * P];
@@ -397,24 +400,99 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
         }
     }
 
+    // Through the key normalisation k = q rn: the query-side gradient of dk is
+    // (dk - k (k . dk)) rn = (dk - q rn^2 (q . dk)) rn, formed here in fp32
+    // while dk is complete for this round; lane c holds d = 32 dt + 8 g + 4 h + t.
+    const float rn = rnorm[tok0 + kpos];
+    const bf16 *krow = q + (tok0 + kpos) * D;
+    float qv[D / 32][16];
+    float qd = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(krow + 32 * dt + 8 * g + 4 * h);
+            qv[dt][4 * g + 0] = __uint_as_float(u.x << 16);
+            qv[dt][4 * g + 1] = __uint_as_float(u.x & 0xffff0000u);
+            qv[dt][4 * g + 2] = __uint_as_float(u.y << 16);
+            qv[dt][4 * g + 3] = __uint_as_float(u.y & 0xffff0000u);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                qd = fmaf(qv[dt][4 * g + t], dka[dt][4 * g + t], qd);
+        }
+    qd += __shfl_xor(qd, 32, kWave);
+    const float proj = rn * rn * qd;
     const size_t row = (((size_t)bh * nh + r) * L + kpos) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d0 = 32 * dt + 8 * g + 4 * h;
-            *reinterpret_cast<float4 *>(dk_part + row + d0) =
-                make_float4(dka[dt][4 * g + 0], dka[dt][4 * g + 1], dka[dt][4 * g + 2], dka[dt][4 * g + 3]);
-            *reinterpret_cast<float4 *>(dv_part + row + d0) =
-                make_float4(dva[dt][4 * g + 0], dva[dt][4 * g + 1], dva[dt][4 * g + 2], dva[dt][4 * g + 3]);
+            float e[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                e[t] = (dka[dt][4 * g + t] - qv[dt][4 * g + t] * proj) * rn;
+            uint2 w;
+            w.x = pack_bf16x2(e[0], e[1]);
+            w.y = pack_bf16x2(e[2], e[3]);
+            *reinterpret_cast<uint2 *>(dqk_part + row + d0) = w;
+            w.x = pack_bf16x2(dva[dt][4 * g + 0], dva[dt][4 * g + 1]);
+            w.y = pack_bf16x2(dva[dt][4 * g + 2], dva[dt][4 * g + 3]);
+            *reinterpret_cast<uint2 *>(dv_part + row + d0) = w;
         }
+}
+
+// Sum of the per-round partials: dQ = sum_r (dq_r + dqk_r), dV = sum_r dv_r,
+// plus dO for tokens that attend only to themselves (o = v).  D/8 lanes per
+// token, 8 elements each.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_reduce_mfma_kernel(int L, int nh, int ntok,
+                                                                   const bf16 *__restrict__ dout,
+                                                                   const uint32_t *__restrict__ meta,
+                                                                   const bf16 *__restrict__ dq_part,
+                                                                   const bf16 *__restrict__ dqk_part,
+                                                                   const bf16 *__restrict__ dv_part,
+                                                                   bf16 *__restrict__ dq, bf16 *__restrict__ dv)
+{
+    constexpr int CPT = D / 8, TPB = kThreads / CPT;
+    const int grp = threadIdx.x / CPT, ch = threadIdx.x % CPT;
+    const int tok = blockIdx.x * TPB + grp;
+    if (tok >= ntok)
+        return;
+    const int bh = tok / L, t = tok % L;
+    float aq[8] = {}, av[8] = {};
+    bool alone = true;
+    for (int r = 0; r < nh; ++r) {
+        alone = alone && rec_hi(meta[(size_t)tok * nh + r]) == 0u;
+        const size_t off = (((size_t)bh * nh + r) * L + t) * D + ch * 8;
+        float x[8], y[8], z[8];
+        load8(dq_part + off, x);
+        load8(dqk_part + off, y);
+        load8(dv_part + off, z);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            aq[k] += x[k] + y[k];
+            av[k] += z[k];
+        }
+    }
+    if (alone) {
+        float x[8];
+        load8(dout + (size_t)tok * D + ch * 8, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            av[k] += x[k];
+    }
+    store8(dq + (size_t)tok * D + ch * 8, aq);
+    store8(dv + (size_t)tok * D + ch * 8, av);
 }
 
 template <int D>
 hipError_t go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-              const uint32_t *meta, const uint32_t *srec, const float *rnorm, float *dq_part, float *dk_part,
-              float *dv_part, hipStream_t st)
+              const uint32_t *meta, const uint32_t *srec, const float *rnorm, void *part, void *dq, void *dv,
+              hipStream_t st)
 {
+    const size_t n = (size_t)P.BH() * P.nh * P.L * D;
+    bf16 *dq_part = (bf16 *)part, *dqk_part = dq_part + n, *dv_part = dqk_part + n;
     dim3 grid(P.L / kRows, P.nh, P.BH());
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
@@ -425,21 +503,33 @@ hipError_t go(const Dims &P, const void *q, const void *v, const void *dout, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    ProfScope prof(LSH_KERNEL_BWD_DKV, st);
-    hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
-                       (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, rnorm, dk_part, dv_part);
+    {
+        ProfScope prof(LSH_KERNEL_BWD_DKV, st);
+        hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale,
+                           (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, rnorm,
+                           dqk_part, dv_part);
+    }
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    const int ntok = P.BH() * P.L;
+    constexpr int TPB = kThreads / (D / 8);
+    ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
+    hipLaunchKernelGGL((bwd_reduce_mfma_kernel<D>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh,
+                       ntok, (const bf16 *)dout, meta, dq_part, dqk_part, dv_part, (bf16 *)dq, (bf16 *)dv);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t bwd_mfma_part_bytes(const Dims &P) { return 3 * (size_t)P.BH() * P.nh * P.L * P.d * sizeof(uint16_t); }
+
 hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
                                 const float *Dv, const uint32_t *meta, const uint32_t *srec, const float *rnorm,
-                                float *dq_part, float *dk_part, float *dv_part, hipStream_t st)
+                                void *part, void *dq, void *dv, hipStream_t st)
 {
     if (P.d == 128)
-        return go<128>(P, q, v, dout, lse, Dv, meta, srec, rnorm, dq_part, dk_part, dv_part, st);
-    return go<64>(P, q, v, dout, lse, Dv, meta, srec, rnorm, dq_part, dk_part, dv_part, st);
+        return go<128>(P, q, v, dout, lse, Dv, meta, srec, rnorm, part, dq, dv, st);
+    return go<64>(P, q, v, dout, lse, Dv, meta, srec, rnorm, part, dq, dv, st);
 }
 
 }  // namespace lsh

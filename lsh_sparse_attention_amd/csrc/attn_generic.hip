@@ -34,40 +34,45 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *
                                                         float *__restrict__ rnorm, const T *__restrict__ out,
                                                         const T *__restrict__ dout, float *__restrict__ Dvec)
 {
-    const int t = blockIdx.x * kThreads + threadIdx.x;
+    // D/8 lanes per token, each on 8 consecutive elements
+    constexpr int CPT = D / 8, TPB = kThreads / CPT;
+    const int grp = threadIdx.x / CPT, ch = threadIdx.x % CPT;
+    const int t = blockIdx.x * TPB + grp;
     const int bh = blockIdx.y;
-    if (t >= L)
-        return;
-    const size_t tok = (size_t)bh * L + t;
+    const bool valid = t < L;
+    const size_t tok = (size_t)bh * L + (valid ? t : 0);
+    float x[8], y[8];
     float ss = 0.f;
-    const T *row = q + tok * D;
-    for (int c = 0; c < D; c += 8) {
-        float x[8];
-        load8(row + c, x);
+    if (valid) {
+        load8(q + tok * D + ch * 8, x);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             ss = fmaf(x[k], x[k], ss);
     }
-    rnorm[tok] = 1.0f / sqrtf(ss);
-    for (int r = 0; r < nh; ++r) {
-        const size_t idx = ((size_t)bh * nh + r) * L + t;
-        const uint32_t s = (uint32_t)inv[idx];
-        const uint32_t w = s - (uint32_t)win_lo[idx];
-        meta[tok * nh + r] = s | (w << 16);
-        srec[((size_t)bh * nh + r) * L + s] = (uint32_t)t | (w << 16);
+    ss = group_sum(ss, CPT);
+    if (valid && ch == 0)
+        rnorm[tok] = 1.0f / sqrtf(ss);
+    if (valid) {
+        for (int r = ch; r < nh; r += CPT) {
+            const size_t idx = ((size_t)bh * nh + r) * L + t;
+            const uint32_t s = (uint32_t)inv[idx];
+            const uint32_t w = s - (uint32_t)win_lo[idx];
+            meta[tok * nh + r] = s | (w << 16);
+            srec[((size_t)bh * nh + r) * L + s] = (uint32_t)t | (w << 16);
+        }
     }
     if (Dvec) {
-        const T *o = out + tok * D, *g = dout + tok * D;
         float acc = 0.f;
-        for (int c = 0; c < D; c += 8) {
-            float x[8], y[8];
-            load8(o + c, x);
-            load8(g + c, y);
+        if (valid) {
+            load8(out + tok * D + ch * 8, x);
+            load8(dout + tok * D + ch * 8, y);
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 acc = fmaf(x[k], y[k], acc);
         }
-        Dvec[tok] = acc;
+        acc = group_sum(acc, CPT);
+        if (valid && ch == 0)
+            Dvec[tok] = acc;
     }
 }
 
@@ -187,60 +192,56 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int L, int nh, int nt
                                                            const float *__restrict__ lse_rounds,
                                                            T *__restrict__ out, float *__restrict__ lse)
 {
-    constexpr int NC = (D + 63) / 64;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int tok = blockIdx.x * kWaves + wave;
-    if (tok >= ntok)
-        return;
-    const int bh = tok / L, t = tok % L;
+    // D/8 lanes per token, each on 8 consecutive elements
+    constexpr int CPT = D / 8, TPB = kThreads / CPT;
+    const int grp = threadIdx.x / CPT, ch = threadIdx.x % CPT;
+    const int tok = blockIdx.x * TPB + grp;
+    const bool valid = tok < ntok;
+    const int tk = valid ? tok : 0;
+    const int bh = tk / L, t = tk % L;
     float M = -INFINITY;
     for (int r = 0; r < nh; ++r)
         M = fmaxf(M, lse_rounds[((size_t)bh * nh + r) * L + t]);
-    if (M == -INFINITY) {
+    const bool alone = valid && M == -INFINITY;
+    if (__ballot(alone) != 0ull) {
         // no member in any round: the token attends only to itself
+        float x[8];
         float ss = 0.f;
+        if (alone) {
+            load8(q + (size_t)tk * D + ch * 8, x);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int e = c * 64 + lane;
-            if (e < D) {
-                const float x = ld(q, (size_t)tok * D + e);
-                ss = fmaf(x, x, ss);
-                out[(size_t)tok * D + e] = v[(size_t)tok * D + e];
-            }
+            for (int k = 0; k < 8; ++k)
+                ss = fmaf(x[k], x[k], ss);
         }
-        ss = wave_sum(ss);
-        if (lane == 0)
-            lse[tok] = scale * sqrtf(ss);
-        return;
+        ss = group_sum(ss, CPT);
+        if (alone) {
+            load8(v + (size_t)tk * D + ch * 8, x);
+            store8(out + (size_t)tk * D + ch * 8, x);
+            if (ch == 0)
+                lse[tk] = scale * sqrtf(ss);
+        }
     }
+    if (!valid || alone)
+        return;
     float den = 0.f;
     for (int r = 0; r < nh; ++r)
         den += expf(lse_rounds[((size_t)bh * nh + r) * L + t] - M);
     const float total = M + logf(den);
-    float acc[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-        acc[c] = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < nh; ++r) {
         const size_t orow = ((size_t)bh * nh + r) * L + t;
         const float wgt = expf(lse_rounds[orow] - total);
         if (wgt == 0.f)
             continue;
+        float x[8];
+        load8(o_rounds + orow * D + ch * 8, x);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int e = c * 64 + lane;
-            if (e < D)
-                acc[c] = fmaf(wgt, ld(o_rounds, orow * D + e), acc[c]);
-        }
+        for (int k = 0; k < 8; ++k)
+            acc[k] = fmaf(wgt, x[k], acc[k]);
     }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int e = c * 64 + lane;
-        if (e < D)
-            out[(size_t)tok * D + e] = from_f<T>(acc[c]);
-    }
-    if (lane == 0)
-        lse[tok] = total;
+    store8(out + (size_t)tk * D + ch * 8, acc);
+    if (ch == 0)
+        lse[tk] = total;
 }
 
 // ---------------------------------------------------------------------------
@@ -468,7 +469,8 @@ template <typename T, int D>
 hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32_t *win_lo, uint32_t *meta,
                    uint32_t *srec, float *rnorm, const void *out, const void *dout, float *Dv, hipStream_t st)
 {
-    dim3 grid((P.L + kThreads - 1) / kThreads, P.BH());
+    constexpr int TPB = kThreads / (D / 8);
+    dim3 grid((P.L + TPB - 1) / TPB, P.BH());
     ProfScope prof(LSH_KERNEL_PREP, st);
     hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, (const T *)q, inv, win_lo,
                        meta, srec, rnorm, (const T *)out, (const T *)dout, Dv);
@@ -492,7 +494,8 @@ hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o
                       void *out, float *lse, hipStream_t st)
 {
     const int ntok = P.BH() * P.L;
-    dim3 grid((ntok + kWaves - 1) / kWaves);
+    constexpr int TPB = kThreads / (D / 8);
+    dim3 grid((ntok + TPB - 1) / TPB);
     ProfScope prof(LSH_KERNEL_COMBINE, st);
     hipLaunchKernelGGL((combine_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, ntok, P.scale,
                        (const T *)q, (const T *)v, (const T *)o_rounds, lse_rounds, (T *)out, lse);

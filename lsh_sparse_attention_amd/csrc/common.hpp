@@ -132,6 +132,32 @@ __device__ __forceinline__ void load8(const float *p, float out[8])
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// Store 8 consecutive elements.
+__device__ __forceinline__ void store8(bf16 *p, const float x[8])
+{
+    uint4 u;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)from_f<bf16>(x[2 * k]).bits | ((uint32_t)from_f<bf16>(x[2 * k + 1]).bits << 16);
+    u.x = w[0]; u.y = w[1]; u.z = w[2]; u.w = w[3];
+    *reinterpret_cast<uint4 *>(p) = u;
+}
+
+__device__ __forceinline__ void store8(float *p, const float x[8])
+{
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// Sum over aligned groups of n lanes (n a power of two dividing 64).
+__device__ __forceinline__ float group_sum(float x, int n)
+{
+    for (int o = n / 2; o > 0; o >>= 1)
+        x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
 __device__ __forceinline__ float readlane(float x, int lane)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
@@ -186,9 +212,12 @@ hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, cons
                                 const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
                                 hipStream_t);
 bool mfma_path_ok(const Dims &, int dtype);
+// bf16 per-round partials dq, dqk (key side, already through the key
+// normalisation) and dv, each [B][H][nh][L][d], in one buffer of this size
+size_t bwd_mfma_part_bytes(const Dims &);
 hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
                                 const float *D, const uint32_t *meta, const uint32_t *srec, const float *rnorm,
-                                float *dq_part, float *dk_part, float *dv_part, hipStream_t);
+                                void *part, void *dq, void *dv, hipStream_t);
 hipError_t launch_bwd_reduce(const Dims &, int dtype, const void *q, const void *dout, const uint32_t *meta,
                              const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,
                              void *dq, void *dv, hipStream_t);

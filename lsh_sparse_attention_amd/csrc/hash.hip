@@ -102,62 +102,101 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
             qop[ct][ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
     }
     const uint16_t *Rbits = reinterpret_cast<const uint16_t *>(rot);
-    for (int r = 0; r < nh; ++r) {
+    // Staging of one 32-column tile: item i = (row d = i / 4, columns
+    // 8 (i % 4) .. +7), kItems per thread, fetched one tile ahead.
+    constexpr int kItems = (D * 4 + kHashThreads - 1) / kHashThreads;
+    const int ntile = (half + 31) / 32;
+    const bool vec = (half % 8) == 0;
+    u32x4_t pre[kItems];
+    auto fetch = [&](int tile) __attribute__((always_inline)) {
+        const int r = tile / ntile, j0 = (tile % ntile) * 32;
         const uint16_t *R = Rbits + (size_t)r * D * half;
-        float bp[2] = {-INFINITY, -INFINITY}, bn[2] = {-INFINITY, -INFINITY};
-        int ip[2] = {0, 0}, in[2] = {0, 0};
-        for (int j0 = 0; j0 < half; j0 += 32) {
-            __syncthreads();
-            // RT[jj][d] = R[d][j0 + jj], zero past the last column
-            for (int i = tid; i < D * 4; i += kHashThreads) {
-                const int d = i / 4, ch = i % 4;
-                const int j = j0 + 8 * ch;
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = tid + it * kHashThreads;
+            const int d = i / 4, j = j0 + 8 * (i % 4);
+            u32x4_t u = {0u, 0u, 0u, 0u};
+            if (i < D * 4) {
+                if (vec && j + 8 <= half) {
+                    u = ld16(R + (size_t)d * half + j);
+                } else {
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (j + e < half)
+                            w[e / 2] |= (uint32_t)R[(size_t)d * half + j + e] << (16 * (e % 2));
+                    u = u32x4_t{w[0], w[1], w[2], w[3]};
+                }
+            }
+            pre[it] = u;
+        }
+    };
+
+    float bp[2] = {-INFINITY, -INFINITY}, bn[2] = {-INFINITY, -INFINITY};
+    int ip[2] = {0, 0}, in[2] = {0, 0};
+    fetch(0);
+    for (int tile = 0; tile < nh * ntile; ++tile) {
+        const int r = tile / ntile, j0 = (tile % ntile) * 32;
+        __syncthreads();
+        // RT[jj][d] = R[d][j0 + jj] (zero past the last column)
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = tid + it * kHashThreads;
+            if (i < D * 4) {
+                const int d = i / 4, jj = 8 * (i % 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    RT[(8 * ch + e) * P + d] = (j + e < half) ? R[(size_t)d * half + j + e] : (uint16_t)0;
+                    RT[(jj + e) * P + d] = (uint16_t)(pre[it][e / 2] >> (16 * (e % 2)));
             }
-            __syncthreads();
-            const bool full = j0 + 32 <= half;
+        }
+        __syncthreads();
+        if (tile + 1 < nh * ntile)
+            fetch(tile + 1);
+        const bool full = j0 + 32 <= half;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                f32x16_t acc = f32x16_t{};
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x16_t acc = f32x16_t{};
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
-                    acc = mfma32(as_bf16x8(ld16(&RT[c * P + 16 * ks + 8 * h])), qop[ct][ks], acc);
-                // acc[4 g + t] = y[column j0 + 8 g + 4 h + t] of row c
+            for (int ks = 0; ks < D / 16; ++ks)
+                acc = mfma32(as_bf16x8(ld16(&RT[c * P + 16 * ks + 8 * h])), qop[ct][ks], acc);
+            // acc[4 g + t] = y[column j0 + 8 g + 4 h + t] of row c
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = j0 + 8 * (e / 4) + 4 * h + (e % 4);
-                    const float y = acc[e];
-                    if (full || j < half) {
-                        if (y > bp[ct]) {
-                            bp[ct] = y;
-                            ip[ct] = j;
-                        }
-                        if (-y > bn[ct]) {
-                            bn[ct] = -y;
-                            in[ct] = j;
-                        }
+            for (int e = 0; e < 16; ++e) {
+                const int j = j0 + 8 * (e / 4) + 4 * h + (e % 4);
+                const float y = acc[e];
+                if (full || j < half) {
+                    if (y > bp[ct]) {
+                        bp[ct] = y;
+                        ip[ct] = j;
+                    }
+                    if (-y > bn[ct]) {
+                        bn[ct] = -y;
+                        in[ct] = j;
                     }
                 }
             }
         }
+        if (j0 + 32 >= half) {
+            // last tile of round r
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            // merge with the other half of the row (first index on ties)
-            const float obp = __shfl_xor(bp[ct], 32, kWave), obn = __shfl_xor(bn[ct], 32, kWave);
-            const int oip = __shfl_xor(ip[ct], 32, kWave), oin = __shfl_xor(in[ct], 32, kWave);
-            if (obp > bp[ct] || (obp == bp[ct] && oip < ip[ct])) {
-                bp[ct] = obp;
-                ip[ct] = oip;
+            for (int ct = 0; ct < 2; ++ct) {
+                // merge with the other half of the row (first index on ties)
+                const float obp = __shfl_xor(bp[ct], 32, kWave), obn = __shfl_xor(bn[ct], 32, kWave);
+                const int oip = __shfl_xor(ip[ct], 32, kWave), oin = __shfl_xor(in[ct], 32, kWave);
+                if (obp > bp[ct] || (obp == bp[ct] && oip < ip[ct])) {
+                    bp[ct] = obp;
+                    ip[ct] = oip;
+                }
+                if (obn > bn[ct] || (obn == bn[ct] && oin < in[ct])) {
+                    bn[ct] = obn;
+                    in[ct] = oin;
+                }
+                const int row = row0 + 32 * ct + c;
+                if (h == 0 && row < L)
+                    buckets[((size_t)bh * nh + r) * L + row] = (bp[ct] >= bn[ct]) ? ip[ct] : half + in[ct];
+                bp[ct] = bn[ct] = -INFINITY;
+                ip[ct] = in[ct] = 0;
             }
-            if (obn > bn[ct] || (obn == bn[ct] && oin < in[ct])) {
-                bn[ct] = obn;
-                in[ct] = oin;
-            }
-            const int row = row0 + 32 * ct + c;
-            if (h == 0 && row < L)
-                buckets[((size_t)bh * nh + r) * L + row] = (bp[ct] >= bn[ct]) ? ip[ct] : half + in[ct];
         }
     }
 }

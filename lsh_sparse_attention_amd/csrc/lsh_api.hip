@@ -233,11 +233,7 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, out, dout, w.D, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype)) {
-            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part, w.dk_part,
-                                     w.dv_part, s);
-            if (e == hipSuccess)
-                e = launch_bwd_reduce(P, prob->dtype, q, dout, w.meta, w.rnorm, w.dq_part, w.dk_part, w.dv_part,
-                                      dq, dv, s);
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part, dq, dv, s);
         } else {
             e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part,
                                 w.dk_part, w.dv_part, dq, dv, s);
