@@ -29,24 +29,9 @@ constexpr int kRows = 128;     // rows owned by a workgroup
 constexpr int kBlk = 32;       // streamed rows per block
 constexpr int kThreads = 256;
 constexpr int kMaxRounds = 16;
+constexpr int kRecCache = 512;  // sorted records of a workgroup's streamed range kept in LDS
 constexpr int kMetaPerThread = (kBlk * (kMaxRounds - 1) + kThreads - 1) / kThreads;
 constexpr float kLog2e = 1.4426950408889634f;
-
-// A-operand of an MFMA read as a transposed 32-row tile of a row-major LDS
-// array: lane (row d = col, half h) takes rows 16 j + 4 h + {0..3} and
-// 16 j + 8 + 4 h + {0..3} of column col, matching the B operand built from
-// accumulator values 8 j .. 8 j + 7 of the other operand.
-template <int P>
-__device__ __forceinline__ bf16x8_t tile_t(const uint16_t *base, int j, int h, int col)
-{
-    const int k0 = 16 * j + 4 * h;
-    u32x4_t a;
-    a.x = (uint32_t)base[(k0 + 0) * P + col] | ((uint32_t)base[(k0 + 1) * P + col] << 16);
-    a.y = (uint32_t)base[(k0 + 2) * P + col] | ((uint32_t)base[(k0 + 3) * P + col] << 16);
-    a.z = (uint32_t)base[(k0 + 8) * P + col] | ((uint32_t)base[(k0 + 9) * P + col] << 16);
-    a.w = (uint32_t)base[(k0 + 10) * P + col] | ((uint32_t)base[(k0 + 11) * P + col] << 16);
-    return as_bf16x8(a);
-}
 
 __device__ __forceinline__ bf16x8_t pack8(const float *x)
 {
@@ -76,13 +61,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
     __shared__ __align__(16) uint16_t Ks[kBlk * P];
     __shared__ __align__(16) uint16_t Vs[kBlk * P];
     __shared__ __align__(16) float rnk[kBlk];
-    __shared__ __align__(16) uint32_t kmeta[kMaxRounds - 1][kBlk];
+    __shared__ __align__(16) uint16_t kmeta[kMaxRounds - 1][kBlk];
     __shared__ uint32_t qmeta[kThreads / kWave][kMaxRounds - 1][32];
+    __shared__ uint32_t krec[kRecCache];
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int h = lane / 32, c = lane % 32;
-    const int r = blockIdx.y, bh = blockIdx.z;
-    const int s0 = blockIdx.x * kRows;
+    const int nblk = L / kRows;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = (lb / nblk) % nh, bh = lb / (nblk * nh);
+    const int s0 = (lb % nblk) * kRows;
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
     const float scale_log2 = scale * kLog2e;
@@ -118,6 +106,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
     const int kb_end = s0 + kRows;
 
     constexpr int kChunks = kBlk * (D / 8) / kThreads;
+    const bool cached = kb_end - kb_first <= kRecCache;
+    if (cached)
+        for (int i = tid; i < kb_end - kb_first; i += kThreads)
+            krec[i] = sr[kb_first + i];
+    __syncthreads();
+    auto key_pos = [&](int s) __attribute__((always_inline)) {
+        return rec_lo(cached ? krec[s - kb_first] : sr[s]);
+    };
     u32x4_t pk[kChunks], pv[kChunks];
     float prn = 0.f;
     uint32_t pkm[kMetaPerThread];
@@ -126,18 +122,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
         for (int i = 0; i < kChunks; ++i) {
             const int idx = tid + i * kThreads;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            const size_t pos = tok0 + rec_lo(sr[kb + row]);
+            const size_t pos = tok0 + key_pos(kb + row);
             pk[i] = ld16(q + pos * D + ch * 8);
             pv[i] = ld16(v + pos * D + ch * 8);
         }
         if (tid < kBlk)
-            prn = rnorm[tok0 + rec_lo(sr[kb + tid])];
+            prn = rnorm[tok0 + key_pos(kb + tid)];
 #pragma unroll
         for (int i = 0; i < kMetaPerThread; ++i) {
             const int idx = tid + i * kThreads;
             pkm[i] = 0u;
             if (idx < kBlk * r)
-                pkm[i] = rec_lo(meta[(tok0 + rec_lo(sr[kb + idx % kBlk])) * nh + idx / kBlk]);
+                pkm[i] = rec_lo(meta[(tok0 + key_pos(kb + idx % kBlk)) * nh + idx / kBlk]);
         }
     };
 
@@ -175,16 +171,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             ok[e] = (unsigned)(kb + 8 * (e / 4) + 4 * h + (e % 4) - qlo) < (unsigned)qw;
-        for (int rr = 0; rr < r; ++rr) {
-            const uint32_t qmr = qmeta[wave][rr][c];
+        if (r > 0) {
+            uint32_t hit[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            for (int rr = 0; rr < r; ++rr) {
+                const uint32_t qmr = qmeta[wave][rr][c];
+                const uint32_t si1p = bcast16(rec_lo(qmr) - 1u), wp = bcast16(rec_hi(qmr));
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x4_t km = ld16(&kmeta[rr][8 * g + 4 * h]);
-                ok[4 * g + 0] = ok[4 * g + 0] && !in_window(qmr, km.x);
-                ok[4 * g + 1] = ok[4 * g + 1] && !in_window(qmr, km.y);
-                ok[4 * g + 2] = ok[4 * g + 2] && !in_window(qmr, km.z);
-                ok[4 * g + 3] = ok[4 * g + 3] && !in_window(qmr, km.w);
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 kp = *reinterpret_cast<const uint2 *>(&kmeta[rr][8 * g + 4 * h]);
+                    hit[2 * g] |= win_hits2(si1p, wp, kp.x);
+                    hit[2 * g + 1] |= win_hits2(si1p, wp, kp.y);
+                }
             }
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
         }
         // g^T scaled by scale * rnorm_k (the key is q_j rnorm_j)
         float gs[16];
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int e = 4 * g + t;
-                const float pr = ok[e] ? exp2f(sacc[e] * rn[t] * scale_log2 - lse2) : 0.f;
+                const float pr = ok[e] ? fast_exp2(sacc[e] * rn[t] * scale_log2 - lse2) : 0.f;
                 gs[e] = pr * (pacc[e] - Di) * (scale * rn[t]);
             }
         }
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_mfma_kernel(int L, int nh, fl
             const bf16x8_t gb = pack8(gs + 8 * j);
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
-                acc[dt] = mfma32(tile_t<P>(Ks, j, h, 32 * dt + c), gb, acc[dt]);
+                acc[dt] = mfma32(tile_t<P>(Ks, j, 32 * dt, lane), gb, acc[dt]);
         }
     }
 
@@ -245,13 +246,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
     __shared__ __align__(16) float qD[kBlk];
     __shared__ __align__(16) int qlo_s[kBlk];
     __shared__ __align__(16) int qw_s[kBlk];
-    __shared__ __align__(16) uint32_t qmeta[kMaxRounds - 1][kBlk];   // query records of earlier rounds
+    __shared__ __align__(16) uint16_t qsi1[kMaxRounds - 1][kBlk];    // query sorted index - 1, earlier rounds
+    __shared__ __align__(16) uint16_t qw16[kMaxRounds - 1][kBlk];    // query window length, earlier rounds
     __shared__ uint32_t kmeta[kThreads / kWave][kMaxRounds - 1][32];  // key sorted index in earlier rounds
+    __shared__ uint32_t qrec_s[kRecCache];                             // sorted records from k0 on
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int h = lane / 32, c = lane % 32;
-    const int r = blockIdx.y, bh = blockIdx.z;
-    const int k0 = blockIdx.x * kRows;
+    const int nblk = L / kRows;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = (lb / nblk) % nh, bh = lb / (nblk * nh);
+    const int k0 = (lb % nblk) * kRows;
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
 
@@ -282,6 +287,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
     const int k_last = k0 + kRows - 1;
 
     constexpr int kChunks = kBlk * (D / 8) / kThreads;
+    const int cache_end = min(L, k0 + kRecCache);
+    for (int i = tid; i < cache_end - k0; i += kThreads)
+        qrec_s[i] = sr[k0 + i];
+    __syncthreads();
+    auto qrec_of = [&](int s) __attribute__((always_inline)) { return s < cache_end ? qrec_s[s - k0] : sr[s]; };
     u32x4_t pq[kChunks], pg[kChunks];
     float plse = 0.f, pD = 0.f;
     int plo = 0, pw = 0;
@@ -291,12 +301,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
         for (int i = 0; i < kChunks; ++i) {
             const int idx = tid + i * kThreads;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            const size_t pos = tok0 + rec_lo(sr[qb + row]);
+            const size_t pos = tok0 + rec_lo(qrec_of(qb + row));
             pq[i] = ld16(q + pos * D + ch * 8);
             pg[i] = ld16(dout + pos * D + ch * 8);
         }
         if (tid < kBlk) {
-            const uint32_t rec = sr[qb + tid];
+            const uint32_t rec = qrec_of(qb + tid);
             const size_t pos = tok0 + rec_lo(rec);
             plse = lse[pos] * kLog2e;
             pD = Dvec[pos];
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
             const int idx = tid + i * kThreads;
             pqm[i] = 0u;
             if (idx < kBlk * r)
-                pqm[i] = meta[(tok0 + rec_lo(sr[qb + idx % kBlk])) * nh + idx / kBlk];
+                pqm[i] = meta[(tok0 + rec_lo(qrec_of(qb + idx % kBlk))) * nh + idx / kBlk];
         }
     };
 
@@ -331,8 +341,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
 #pragma unroll
         for (int i = 0; i < kMetaPerThread; ++i) {
             const int idx = tid + i * kThreads;
-            if (idx < kBlk * r)
-                qmeta[idx / kBlk][idx % kBlk] = pqm[i];
+            if (idx < kBlk * r) {
+                qsi1[idx / kBlk][idx % kBlk] = (uint16_t)(rec_lo(pqm[i]) - 1u);
+                qw16[idx / kBlk][idx % kBlk] = (uint16_t)rec_hi(pqm[i]);
+            }
         }
         __syncthreads();
         // win_lo is non-decreasing, so the block's first row has its smallest
@@ -364,16 +376,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
             ok[4 * g + 2] = (unsigned)(sk - lo4.z) < (unsigned)w4.z;
             ok[4 * g + 3] = (unsigned)(sk - lo4.w) < (unsigned)w4.w;
         }
-        for (int rr = 0; rr < r; ++rr) {
-            const uint32_t ksr = kmeta[wave][rr][c];
+        if (r > 0) {
+            uint32_t hit[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            for (int rr = 0; rr < r; ++rr) {
+                const uint32_t skp = bcast16(kmeta[wave][rr][c]);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x4_t qm = ld16(&qmeta[rr][8 * g + 4 * h]);
-                ok[4 * g + 0] = ok[4 * g + 0] && !in_window(qm.x, ksr);
-                ok[4 * g + 1] = ok[4 * g + 1] && !in_window(qm.y, ksr);
-                ok[4 * g + 2] = ok[4 * g + 2] && !in_window(qm.z, ksr);
-                ok[4 * g + 3] = ok[4 * g + 3] && !in_window(qm.w, ksr);
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 s1 = *reinterpret_cast<const uint2 *>(&qsi1[rr][8 * g + 4 * h]);
+                    const uint2 ww = *reinterpret_cast<const uint2 *>(&qw16[rr][8 * g + 4 * h]);
+                    hit[2 * g] |= win_hits2(s1.x, ww.x, skp);
+                    hit[2 * g + 1] |= win_hits2(s1.y, ww.y, skp);
+                }
             }
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
         }
         float pr[16], gr[16];
 #pragma unroll
@@ -384,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int e = 4 * g + t;
-                pr[e] = ok[e] ? exp2f(sacc[e] * krn2 - lv[t]) : 0.f;
+                pr[e] = ok[e] ? fast_exp2(sacc[e] * krn2 - lv[t]) : 0.f;
                 gr[e] = pr[e] * (pacc[e] - dv[t]) * scale;
             }
         }
@@ -394,8 +411,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_mfma_kernel(int L, int nh, f
             const bf16x8_t pb = pack8(pr + 8 * j), gb = pack8(gr + 8 * j);
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-                dva[dt] = mfma32(tile_t<P>(Gs, j, h, 32 * dt + c), pb, dva[dt]);
-                dka[dt] = mfma32(tile_t<P>(Qs, j, h, 32 * dt + c), gb, dka[dt]);
+                dva[dt] = mfma32(tile_t<P>(Gs, j, 32 * dt, lane), pb, dva[dt]);
+                dka[dt] = mfma32(tile_t<P>(Qs, j, 32 * dt, lane), gb, dka[dt]);
             }
         }
     }
@@ -493,7 +510,7 @@ hipError_t go(const Dims &P, const void *q, const void *v, const void *dout, con
 {
     const size_t n = (size_t)P.BH() * P.nh * P.L * D;
     bf16 *dq_part = (bf16 *)part, *dqk_part = dq_part + n, *dv_part = dqk_part + n;
-    dim3 grid(P.L / kRows, P.nh, P.BH());
+    dim3 grid((P.L / kRows) * P.nh * P.BH());
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         hipLaunchKernelGGL((bwd_dq_mfma_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale,

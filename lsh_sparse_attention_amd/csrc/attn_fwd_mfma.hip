@@ -30,6 +30,7 @@ constexpr int kKB = 32;       // keys per block
 constexpr int kThreads = 256;
 constexpr int kMaxRounds = 16;
 
+constexpr int kRecCache = 512;  // sorted records of a workgroup's key range kept in LDS
 constexpr int kMetaPerThread = (kKB * (kMaxRounds - 1) + kThreads - 1) / kThreads;
 // The running max of a query row is only raised when a block's max exceeds it
 // by more than this many log2 units; exp2 arguments stay <= kLazy, so the
@@ -49,13 +50,17 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int L, int nh, float
     __shared__ __align__(16) uint16_t Ks[kKB * P];
     __shared__ __align__(16) uint16_t Vs[kKB * P];
     __shared__ __align__(16) float rnk[kKB];
-    __shared__ __align__(16) uint32_t kmeta[kMaxRounds - 1][kKB];   // key sorted index in earlier rounds
+    __shared__ __align__(16) uint16_t kmeta[kMaxRounds - 1][kKB];   // key sorted index in earlier rounds
     __shared__ uint32_t qmeta[kThreads / kWave][kMaxRounds - 1][32];  // query records of earlier rounds
+    __shared__ uint32_t krec[kRecCache];                                 // sorted records of the key range
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int h = lane / 32, c = lane % 32;
-    const int r = blockIdx.y, bh = blockIdx.z;
-    const int s0 = blockIdx.x * kQB;
+    // 1-D grid in XCD-friendly order: row blocks fastest, then round, then (b, h)
+    const int nblk = L / kQB;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = (lb / nblk) % nh, bh = lb / (nblk * nh);
+    const int s0 = (lb % nblk) * kQB;
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
 
@@ -90,6 +95,15 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int L, int nh, float
     const int kb_end = s0 + kQB;
 
     constexpr int kChunks = kKB * (D / 8) / kThreads;  // 16-byte chunks per thread per tensor
+    // the key range's sorted records, in LDS when they fit
+    const bool cached = kb_end - kb_first <= kRecCache;
+    if (cached)
+        for (int i = tid; i < kb_end - kb_first; i += kThreads)
+            krec[i] = sr[kb_first + i];
+    __syncthreads();
+    auto key_pos = [&](int s) __attribute__((always_inline)) {
+        return rec_lo(cached ? krec[s - kb_first] : sr[s]);
+    };
     u32x4_t pk[kChunks], pv[kChunks];
     float prn = 0.f;
     uint32_t pkm[kMetaPerThread];
@@ -98,18 +112,18 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int L, int nh, float
         for (int i = 0; i < kChunks; ++i) {
             const int idx = tid + i * kThreads;
             const int row = idx / (D / 8), ch = idx % (D / 8);
-            const size_t pos = tok0 + rec_lo(sr[kb + row]);
+            const size_t pos = tok0 + key_pos(kb + row);
             pk[i] = ld16(q + pos * D + ch * 8);
             pv[i] = ld16(v + pos * D + ch * 8);
         }
         if (tid < kKB)
-            prn = rnorm[tok0 + rec_lo(sr[kb + tid])] * scale_log2;
+            prn = rnorm[tok0 + key_pos(kb + tid)] * scale_log2;
 #pragma unroll
         for (int i = 0; i < kMetaPerThread; ++i) {
             const int idx = tid + i * kThreads;
             pkm[i] = 0u;
             if (idx < kKB * r)
-                pkm[i] = rec_lo(meta[(tok0 + rec_lo(sr[kb + idx % kKB])) * nh + idx / kKB]);
+                pkm[i] = rec_lo(meta[(tok0 + key_pos(kb + idx % kKB)) * nh + idx / kKB]);
         }
     };
 
@@ -154,17 +168,23 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int L, int nh, float
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             ok[e] = (unsigned)(kb + 8 * (e / 4) + 4 * h + (e % 4) - qlo) < (unsigned)qw;
-        // first-owner mask: drop keys that are in the query's set of an earlier round
-        for (int rr = 0; rr < r; ++rr) {
-            const uint32_t qmr = qmeta[wave][rr][c];
+        // first-owner mask: drop keys that are in the query's set of an earlier
+        // round (two keys per packed 16-bit test)
+        if (r > 0) {
+            uint32_t hit[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            for (int rr = 0; rr < r; ++rr) {
+                const uint32_t qmr = qmeta[wave][rr][c];
+                const uint32_t si1p = bcast16(rec_lo(qmr) - 1u), wp = bcast16(rec_hi(qmr));
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x4_t km = ld16(&kmeta[rr][8 * g + 4 * h]);
-                ok[4 * g + 0] = ok[4 * g + 0] && !in_window(qmr, km.x);
-                ok[4 * g + 1] = ok[4 * g + 1] && !in_window(qmr, km.y);
-                ok[4 * g + 2] = ok[4 * g + 2] && !in_window(qmr, km.z);
-                ok[4 * g + 3] = ok[4 * g + 3] && !in_window(qmr, km.w);
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 kp = *reinterpret_cast<const uint2 *>(&kmeta[rr][8 * g + 4 * h]);
+                    hit[2 * g] |= win_hits2(si1p, wp, kp.x);
+                    hit[2 * g + 1] |= win_hits2(si1p, wp, kp.y);
+                }
             }
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
         }
         // logits in log2 units
         float x[16];
@@ -190,12 +210,12 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int L, int nh, float
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            x[e] = exp2f(x[e] - mref);
+            x[e] = fast_exp2(x[e] - mref);
             ps += x[e];
         }
         ps += __shfl_xor(ps, 32, kWave);
         if (__ballot(raise) != 0ull) {
-            const float corr = raise ? exp2f(mrun - mref) : 1.f;
+            const float corr = raise ? fast_exp2(mrun - mref) : 1.f;
             lrun *= corr;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
@@ -215,17 +235,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(int L, int nh, float
             pu.z = pack_bf16x2(p[8 * j + 4], p[8 * j + 5]);
             pu.w = pack_bf16x2(p[8 * j + 6], p[8 * j + 7]);
             const bf16x8_t pb = as_bf16x8(pu);
-            const int k0 = 16 * j + 4 * h;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const int col = 32 * dt + c;
-                u32x4_t au;
-                au.x = (uint32_t)Vs[(k0 + 0) * P + col] | ((uint32_t)Vs[(k0 + 1) * P + col] << 16);
-                au.y = (uint32_t)Vs[(k0 + 2) * P + col] | ((uint32_t)Vs[(k0 + 3) * P + col] << 16);
-                au.z = (uint32_t)Vs[(k0 + 8) * P + col] | ((uint32_t)Vs[(k0 + 9) * P + col] << 16);
-                au.w = (uint32_t)Vs[(k0 + 10) * P + col] | ((uint32_t)Vs[(k0 + 11) * P + col] << 16);
-                oacc[dt] = mfma32(as_bf16x8(au), pb, oacc[dt]);
-            }
+            for (int dt = 0; dt < D / 32; ++dt)
+                oacc[dt] = mfma32(tile_t<P>(Vs, j, 32 * dt, lane), pb, oacc[dt]);
         }
     }
 
@@ -257,7 +269,7 @@ hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, con
                                 const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
                                 hipStream_t st)
 {
-    dim3 grid(P.L / kQB, P.nh, P.BH());
+    dim3 grid((P.L / kQB) * P.nh * P.BH());
     const float scale_log2 = P.scale * 1.4426950408889634f;
     ProfScope prof(LSH_KERNEL_FWD, st);
     if (P.d == 128)

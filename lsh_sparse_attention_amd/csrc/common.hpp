@@ -202,10 +202,68 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_
 __device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 
-// two fp32 -> packed bf16 pair (round to nearest even)
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return (uint32_t)from_f<bf16>(lo).bits | ((uint32_t)from_f<bf16>(hi).bits << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives in slot
+// k element i % 4 of the 4-element chunk addressed by lane 4 k + i / 4.  If
+// lane m of the group addresses row R0 + m / 4, columns C0 + 4 (m % 4) .. +3 of
+// a row-major bf16 tile, lane i receives rows R0 .. R0 + 3 of column C0 + i:
+// a transposed read.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p)
+{
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// A operand of v_mfma_f32_32x32x16_bf16 read transposed from a row-major LDS
+// tile T[row][col] (pitch P elements): lane l (column col0 + l % 32, half
+// h = l / 32) receives rows 16 j + 4 h + {0..3} in slots 0..3 and
+// 16 j + 8 + 4 h + {0..3} in slots 4..7.  This matches a B operand whose slot s
+// holds accumulator value 8 j + s of a 32x32 tile (rows 8 g + 4 h + t).
+template <int P>
+__device__ __forceinline__ bf16x8_t tile_t(const uint16_t *T, int j, int col0, int lane)
+{
+    const int g = lane / 16, m = lane % 16;
+    const int row = 16 * j + 4 * (g / 2) + m / 4;
+    const int col = col0 + 16 * (g % 2) + 4 * (m % 4);
+    const uint2 a = lds_read_tr16(T + row * P + col);
+    const uint2 b = lds_read_tr16(T + (row + 8) * P + col);
+    const u32x4_t u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// exp2 on the transcendental unit (v_exp_f32, denormal results flushed)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Packed 16-bit window test for two keys at once.  With si1 = s_i - 1 and
+// w_i of query i in some round (both broadcast to the two halves), and the two
+// keys' sorted indices sk in that round, a half of the result is nonzero iff
+// that key lies in the sorted window [s_i - w_i, s_i - 1] (wrapping 16-bit
+// subtraction, then saturating: w - (si1 - sk) > 0  <=>  si1 - sk < w).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t win_hits2(uint32_t si1p, uint32_t wp, uint32_t skp)
+{
+    const u16x2_t x = __builtin_bit_cast(u16x2_t, si1p) - __builtin_bit_cast(u16x2_t, skp);
+    const u16x2_t z = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, wp), x);
+    return __builtin_bit_cast(uint32_t, z);
+}
+__device__ __forceinline__ uint32_t bcast16(uint32_t x) { return (x & 0xffffu) * 0x10001u; }
+
+// Workgroup index remapped so that consecutive logical blocks run on the same
+// XCD (the hardware deals workgroups round-robin over the 8 XCDs, each with
+// its own L2): logical = (i % 8) * (n / 8) + i / 8 when 8 divides n.
+__device__ __forceinline__ int xcd_block(int i, int n)
+{
+    return (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
 }
 
 hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const uint32_t *meta,
