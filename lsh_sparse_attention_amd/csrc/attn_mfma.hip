@@ -1,0 +1,890 @@
+// attn_mfma.hip -- per-round chunked LSH attention, forward and backward, on
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16) with direct global-to-LDS loads.
+//
+// Method: "Reformer: The Efficient Transformer" §2 (attention over chunks of
+// the sorted order: each query sees the keys of its own bucket in its own
+// chunk and the one before, not after itself; self only as a fallback) and
+// App. A (a query attends to the union of its round sets; duplicates are
+// masked so each member counts once; per-round outputs are combined by
+// logsumexp weights).  Backward with bucket assignment and sort order held
+// fixed (no gradient through hashing or sorting, as the Reformer authors
+// state in Hacker News thread 22095523).
+//
+// Round r, query at sorted index s attends to the sorted keys [s - w, s - 1]
+// (w = s - win_lo), minus those that belong to its set in an earlier round
+// r' < r (the first round that holds a member counts it).  The band needs
+// no chunk arithmetic: win_lo carries it.
+//
+// Dataflow, common to the three attention kernels: a workgroup (4 waves)
+// owns 128 consecutive sorted rows of one (batch, head, round); the other
+// operand streams through LDS in blocks of 32 sorted rows.  Rows are fetched
+// by position straight into LDS with global_load_lds_dwordx4 (no staging
+// registers) into a 3-deep ring, two blocks ahead of the block in use; each
+// wave waits on its own outstanding loads with s_waitcnt vmcnt and a
+// workgroup barrier publishes the block.  Tiles are stored unpadded with the
+// 16-byte chunks of row r XOR-swizzled by r, so that both the row reads
+// (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) spread over
+// the LDS banks.  Per-block metadata (inverse key norms, the keys' sorted
+// indices in earlier rounds; for the key side also lse, D and the queries'
+// windows) comes from tiles that the prep kernel lays out per 32 sorted rows,
+// so it arrives with the same kind of contiguous load.
+#include "common.hpp"
+
+namespace lsh {
+namespace {
+
+constexpr int kRows = 128;     // rows owned by a workgroup
+constexpr int kBlk = 32;       // streamed rows per block
+constexpr int kThreads = 256;
+constexpr int kStages = 3;
+constexpr int kRecCache = 1024;           // sorted records of a workgroup's streamed range
+constexpr int kMaxEarlier = 13;           // earlier rounds a tile holds (n_hashes <= 14)
+constexpr int kKTile = 1024;              // key tile: rn[32] f32, sk[13][32] u16
+constexpr int kQTile = 2048;              // query tile: lse2[32], D[32] f32, w[32] u16, (si1, w)[13][32] u16
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;             // lazy running-max threshold (log2 units)
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// 16-byte global -> LDS copy (global_load_lds_dwordx4); lane l lands at
+// lds_wave_base + 16 l (the base is wave-uniform and goes through M0).  The
+// instruction has no register result.  It is issued from inline assembly so
+// that the compiler neither orders it against unrelated LDS reads nor drains
+// it with its own waits: completion is waited for explicitly with wait_vm,
+// followed by a workgroup barrier, before the LDS data is read.
+__device__ __forceinline__ void dma16(const void *g, void *lds_wave_base)
+{
+    const uint32_t lds = (uint32_t)(uintptr_t)((LDS_AS void *)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Workgroup barrier that orders memory operations for the compiler only; the
+// hardware waits are the explicit wait_vm before it (LDS reads of the previous
+// block have been consumed by the time a wave reaches the barrier).
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// element offset of (row, col) in an unpadded D-wide bf16 tile whose 16-byte
+// chunks are XOR-swizzled by row
+template <int D>
+__device__ __forceinline__ int swz(int row, int col)
+{
+    constexpr int CPR = D / 8;
+    return row * D + ((((col >> 3) ^ (row & (CPR - 1)))) << 3) + (col & 7);
+}
+
+// A operand (row = tile row c, 8 consecutive columns starting at k0) of a swizzled tile
+template <int D>
+__device__ __forceinline__ bf16x8_t tile_row(const uint16_t *T, int row, int k0)
+{
+    return as_bf16x8(ld16(T + swz<D>(row, k0)));
+}
+
+// A operand read transposed from a swizzled tile (see tile_t in common.hpp):
+// lane (column col0 + l % 32, half h) gets rows 16 j + 4 h + {0..3}, 16 j + 8 + 4 h + {0..3}
+template <int D>
+__device__ __forceinline__ bf16x8_t tile_tr(const uint16_t *T, int j, int col0, int lane)
+{
+    const int g = lane / 16, m = lane % 16;
+    const int row = 16 * j + 4 * (g / 2) + m / 4;
+    const int col = col0 + 16 * (g % 2) + 4 * (m % 4);
+    const uint2 a = lds_read_tr16(T + swz<D>(row, col));
+    const uint2 b = lds_read_tr16(T + swz<D>(row + 8, col));
+    const u32x4_t u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ bf16x8_t pack8(const float *x)
+{
+    u32x4_t u;
+    u.x = pack_bf16x2(x[0], x[1]);
+    u.y = pack_bf16x2(x[2], x[3]);
+    u.z = pack_bf16x2(x[4], x[5]);
+    u.w = pack_bf16x2(x[6], x[7]);
+    return as_bf16x8(u);
+}
+
+// Issue this thread's part of one block: rows [kb, kb + 32) of tensors a and
+// b (positions from the record cache) into stage buffers A and B.
+template <int D>
+__device__ __forceinline__ void dma_rows(const bf16 *__restrict__ a, const bf16 *__restrict__ b, uint16_t *A,
+                                         uint16_t *B, const uint32_t *rec, int kb, size_t tok0, int tid, int wave)
+// rec[kb + row] is the sorted record of streamed row kb + row (kb relative to the cache start)
+{
+    constexpr int CPR = D / 8, KPT = D / 64;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int qc = i * kThreads + tid;            // linear 16-byte chunk of the tile
+        const int row = qc / CPR, p = qc % CPR;
+        const int lc = p ^ (row & (CPR - 1));         // logical chunk stored at physical p
+        const size_t off = (tok0 + rec_lo(rec[kb + row])) * D + lc * 8;
+        const int base = (i * kThreads + wave * kWave) * 8;   // elements
+        dma16(a + off, A + base);
+        dma16(b + off, B + base);
+    }
+}
+
+// packed earlier-round test over 16 scores; ok[e] cleared where the key is in
+// the query's set of round rr.  qrec: (si1, w) pairs (query side) and
+// skp: key sorted-index pairs, arranged by the caller.
+__device__ __forceinline__ void clear_hits(bool (&ok)[16], const uint32_t (&hit)[8])
+{
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+}
+
+// ---------------------------------------------------------------------------
+// metadata tiles, per 32 sorted rows of each (b, h, round)
+
+__global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, const int32_t *__restrict__ inv,
+                                                             const int32_t *__restrict__ win_lo,
+                                                             const float *__restrict__ rnorm,
+                                                             const float *__restrict__ lse,
+                                                             const float *__restrict__ Dvec,
+                                                             uint8_t *__restrict__ ktile, uint8_t *__restrict__ qtile)
+{
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    const int r = blockIdx.y, bh = blockIdx.z;
+    if (t >= L)
+        return;
+    const size_t tok = (size_t)bh * L + t;
+    const int s = inv[((size_t)bh * nh + r) * L + t];
+    const size_t tidx = ((size_t)bh * nh + r) * (L / kBlk) + s / kBlk;
+    const int k = s % kBlk;
+    uint8_t *kt = ktile + tidx * kKTile;
+    reinterpret_cast<float *>(kt)[k] = rnorm[tok];
+    uint8_t *qt = qtile ? qtile + tidx * kQTile : nullptr;
+    if (qt) {
+        reinterpret_cast<float *>(qt)[k] = lse[tok] * kLog2e;
+        reinterpret_cast<float *>(qt + 128)[k] = Dvec[tok];
+        reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)(s - win_lo[((size_t)bh * nh + r) * L + t]);
+    }
+    for (int rr = 0; rr < r && rr < kMaxEarlier; ++rr) {
+        const size_t i2 = ((size_t)bh * nh + rr) * L + t;
+        const int s2 = inv[i2];
+        reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] = (uint16_t)s2;
+        if (qt) {
+            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(s2 - 1);
+            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)(s2 - win_lo[i2]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// common workgroup prologue: which (b, h, round, row block), and the sorted
+// records of the streamed range in LDS
+
+struct Where {
+    int r, bh, s0;
+};
+
+__device__ __forceinline__ Where where_of(int L, int nh)
+{
+    const int nblk = L / kRows;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    return Where{(lb / nblk) % nh, lb / (nblk * nh), (lb % nblk) * kRows};
+}
+
+// ---------------------------------------------------------------------------
+// forward (query-owned)
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(int L, int nh, float scale_log2, const bf16 *__restrict__ q,
+                                                       const bf16 *__restrict__ v, const uint32_t *__restrict__ meta,
+                                                       const uint32_t *__restrict__ srec,
+                                                       const uint8_t *__restrict__ ktile,
+                                                       bf16 *__restrict__ o_rounds, float *__restrict__ lse_rounds)
+{
+    constexpr int KPT = D / 64;
+    __shared__ __align__(16) uint16_t Ks[kStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Vs[kStages][kBlk * D];
+    __shared__ __align__(16) uint8_t Ts[kStages][kKTile];
+    __shared__ uint32_t krec[kRecCache];
+    __shared__ uint32_t qmeta[kThreads / kWave][kMaxEarlier][32];
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int h = lane / 32, c = lane % 32;
+    const Where W = where_of(L, nh);
+    const int r = W.r, bh = W.bh, s0 = W.s0;
+    const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
+    const size_t tok0 = (size_t)bh * L;
+
+    const int wq0 = s0 + wave * 32;
+    const int sq = wq0 + c;
+    const uint32_t qrec = sr[sq];
+    const int qpos = (int)rec_lo(qrec), qw = (int)rec_hi(qrec);
+    const int qlo = sq - qw;
+    const int wlo = __builtin_amdgcn_readlane(qlo, 0);
+    if (h == 0)
+        for (int rr = 0; rr < r; ++rr)
+            qmeta[wave][rr][c] = meta[(tok0 + qpos) * nh + rr];
+    bf16x8_t qop[D / 16];
+    {
+        const bf16 *qrow = q + (tok0 + qpos) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qop[ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
+    }
+    const int kb_first = (s0 - (int)rec_hi(sr[s0])) & ~(kBlk - 1);
+    const int nblocks = (s0 + kRows - kb_first) / kBlk;
+    for (int i = tid; i < nblocks * kBlk; i += kThreads)
+        krec[i] = sr[kb_first + i];
+    __syncthreads();
+    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
+
+    auto issue = [&](int b) __attribute__((always_inline)) {
+        const int kb = kb_first + b * kBlk, st = b % kStages;
+        dma_rows<D>(q, v, Ks[st], Vs[st], krec, b * kBlk, tok0, tid, wave);
+        if (wave == 0)
+            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
+    };
+
+    f32x16_t oacc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+        oacc[dt] = f32x16_t{};
+    float mrun = -INFINITY, lrun = 0.f;
+
+    // operands loaded into registers above are complete before the ring starts,
+    // so no wait inside the loop has to cover them
+    wait_vm<0>();
+    issue(0);
+    if (nblocks > 1)
+        issue(1);
+    for (int b = 0; b < nblocks; ++b) {
+        if (b + 1 < nblocks) {
+            if (wave == 0)
+                wait_vm<2 * KPT + 1>();
+            else
+                wait_vm<2 * KPT>();
+        } else {
+            wait_vm<0>();
+        }
+        block_barrier();
+        if (b + 2 < nblocks)
+            issue(b + 2);
+        const int kb = kb_first + b * kBlk, st = b % kStages;
+        // keys [kb, kb+31] against this wave's windows
+        if (kb > wq0 || kb + kBlk - 1 < wlo)
+            continue;
+        const uint16_t *K = Ks[st], *V = Vs[st];
+        const float *rnk = reinterpret_cast<const float *>(Ts[st]);
+        const uint16_t *skm = reinterpret_cast<const uint16_t *>(Ts[st] + 128);
+
+        // S^T = K Q^T (lane = query c; keys 8 g + 4 h + t)
+        f32x16_t sacc = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            sacc = mfma32(tile_row<D>(K, c, 16 * ks + 8 * h), qop[ks], sacc);
+
+        bool ok[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            ok[e] = (unsigned)(kb + 8 * (e / 4) + 4 * h + (e % 4) - qlo) < (unsigned)qw;
+        if (r > 0) {
+            uint32_t hit[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            for (int rr = 0; rr < r; ++rr) {
+                const uint32_t qmr = qmeta[wave][rr][c];
+                const uint32_t si1p = bcast16(rec_lo(qmr) - 1u), wp = bcast16(rec_hi(qmr));
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 kp = *reinterpret_cast<const uint2 *>(skm + 32 * rr + 8 * g + 4 * h);
+                    hit[2 * g] |= win_hits2(si1p, wp, kp.x);
+                    hit[2 * g + 1] |= win_hits2(si1p, wp, kp.y);
+                }
+            }
+            clear_hits(ok, hit);
+        }
+        float x[16];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 rn4 = *reinterpret_cast<const float4 *>(rnk + 8 * g + 4 * h);
+            const float rn[4] = {rn4.x * scale_log2, rn4.y * scale_log2, rn4.z * scale_log2, rn4.w * scale_log2};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x[4 * g + t] = ok[4 * g + t] ? sacc[4 * g + t] * rn[t] : -INFINITY;
+                bm = fmaxf(bm, x[4 * g + t]);
+            }
+        }
+        bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+        const bool raise = bm > mrun + kLazy;
+        const float mnew = raise ? bm : mrun;
+        const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            x[e] = fast_exp2(x[e] - mref);
+            ps += x[e];
+        }
+        ps += __shfl_xor(ps, 32, kWave);
+        if (__ballot(raise) != 0ull) {
+            const float corr = raise ? fast_exp2(mrun - mref) : 1.f;
+            lrun *= corr;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                oacc[dt] *= corr;
+        }
+        lrun += ps;
+        mrun = mnew;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8_t pb = pack8(x + 8 * j);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                oacc[dt] = mfma32(tile_tr<D>(V, j, 32 * dt, lane), pb, oacc[dt]);
+        }
+    }
+
+    const size_t orow = ((size_t)bh * nh + r) * L + qpos;
+    const float inv_l = lrun > 0.f ? 1.f / lrun : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack_bf16x2(oacc[dt][4 * g + 0] * inv_l, oacc[dt][4 * g + 1] * inv_l);
+            w.y = pack_bf16x2(oacc[dt][4 * g + 2] * inv_l, oacc[dt][4 * g + 3] * inv_l);
+            *reinterpret_cast<uint2 *>(o_rounds + orow * D + 32 * dt + 8 * g + 4 * h) = w;
+        }
+    if (h == 0)
+        lse_rounds[orow] = lrun > 0.f ? (mrun + __log2f(lrun)) * 0.69314718055994531f : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// backward, query side: dq of each round (query-owned, as the forward)
+//   p = exp(scale q_i.k_j - lse_i) with the global lse, g = p (dO_i.v_j - D_i),
+//   dq_i += scale g k_j = scale g rn_j q_j
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(int L, int nh, float scale, const bf16 *__restrict__ q,
+                                                      const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
+                                                      const float *__restrict__ lse, const float *__restrict__ Dvec,
+                                                      const uint32_t *__restrict__ meta,
+                                                      const uint32_t *__restrict__ srec,
+                                                      const uint8_t *__restrict__ ktile, bf16 *__restrict__ dq_part)
+{
+    constexpr int KPT = D / 64;
+    __shared__ __align__(16) uint16_t Ks[kStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Vs[kStages][kBlk * D];
+    __shared__ __align__(16) uint8_t Ts[kStages][kKTile];
+    __shared__ uint32_t krec[kRecCache];
+    __shared__ uint32_t qmeta[kThreads / kWave][kMaxEarlier][32];
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int h = lane / 32, c = lane % 32;
+    const Where W = where_of(L, nh);
+    const int r = W.r, bh = W.bh, s0 = W.s0;
+    const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
+    const size_t tok0 = (size_t)bh * L;
+    const float scale_log2 = scale * kLog2e;
+
+    const int wq0 = s0 + wave * 32;
+    const int sq = wq0 + c;
+    const uint32_t qrec = sr[sq];
+    const int qpos = (int)rec_lo(qrec), qw = (int)rec_hi(qrec);
+    const int qlo = sq - qw;
+    const int wlo = __builtin_amdgcn_readlane(qlo, 0);
+    if (h == 0)
+        for (int rr = 0; rr < r; ++rr)
+            qmeta[wave][rr][c] = meta[(tok0 + qpos) * nh + rr];
+    const float lse2 = lse[tok0 + qpos] * kLog2e;
+    const float Di = Dvec[tok0 + qpos];
+    bf16x8_t qop[D / 16], gop[D / 16];
+    {
+        const bf16 *qrow = q + (tok0 + qpos) * D, *grow = dout + (tok0 + qpos) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            qop[ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
+            gop[ks] = as_bf16x8(ld16(grow + 16 * ks + 8 * h));
+        }
+    }
+    const int kb_first = (s0 - (int)rec_hi(sr[s0])) & ~(kBlk - 1);
+    const int nblocks = (s0 + kRows - kb_first) / kBlk;
+    for (int i = tid; i < nblocks * kBlk; i += kThreads)
+        krec[i] = sr[kb_first + i];
+    __syncthreads();
+    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
+
+    auto issue = [&](int b) __attribute__((always_inline)) {
+        const int kb = kb_first + b * kBlk, st = b % kStages;
+        dma_rows<D>(q, v, Ks[st], Vs[st], krec, b * kBlk, tok0, tid, wave);
+        if (wave == 0)
+            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
+    };
+
+    f32x16_t acc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = f32x16_t{};
+
+    // operands loaded into registers above are complete before the ring starts,
+    // so no wait inside the loop has to cover them
+    wait_vm<0>();
+    issue(0);
+    if (nblocks > 1)
+        issue(1);
+    for (int b = 0; b < nblocks; ++b) {
+        if (b + 1 < nblocks) {
+            if (wave == 0)
+                wait_vm<2 * KPT + 1>();
+            else
+                wait_vm<2 * KPT>();
+        } else {
+            wait_vm<0>();
+        }
+        block_barrier();
+        if (b + 2 < nblocks)
+            issue(b + 2);
+        const int kb = kb_first + b * kBlk, st = b % kStages;
+        if (kb > wq0 || kb + kBlk - 1 < wlo)
+            continue;
+        const uint16_t *K = Ks[st], *V = Vs[st];
+        const float *rnk = reinterpret_cast<const float *>(Ts[st]);
+        const uint16_t *skm = reinterpret_cast<const uint16_t *>(Ts[st] + 128);
+
+        // S^T = K Q^T and dP^T = V dO^T (lane = query c, keys 8 g + 4 h + t)
+        f32x16_t sacc = f32x16_t{}, pacc = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            sacc = mfma32(tile_row<D>(K, c, 16 * ks + 8 * h), qop[ks], sacc);
+            pacc = mfma32(tile_row<D>(V, c, 16 * ks + 8 * h), gop[ks], pacc);
+        }
+        bool ok[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            ok[e] = (unsigned)(kb + 8 * (e / 4) + 4 * h + (e % 4) - qlo) < (unsigned)qw;
+        if (r > 0) {
+            uint32_t hit[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            for (int rr = 0; rr < r; ++rr) {
+                const uint32_t qmr = qmeta[wave][rr][c];
+                const uint32_t si1p = bcast16(rec_lo(qmr) - 1u), wp = bcast16(rec_hi(qmr));
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 kp = *reinterpret_cast<const uint2 *>(skm + 32 * rr + 8 * g + 4 * h);
+                    hit[2 * g] |= win_hits2(si1p, wp, kp.x);
+                    hit[2 * g + 1] |= win_hits2(si1p, wp, kp.y);
+                }
+            }
+            clear_hits(ok, hit);
+        }
+        float gs[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 rn4 = *reinterpret_cast<const float4 *>(rnk + 8 * g + 4 * h);
+            const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = 4 * g + t;
+                const float pr = ok[e] ? fast_exp2(sacc[e] * rn[t] * scale_log2 - lse2) : 0.f;
+                gs[e] = pr * (pacc[e] - Di) * (scale * rn[t]);
+            }
+        }
+        // dQ^T += K^T Gs^T
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8_t gb = pack8(gs + 8 * j);
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                acc[dt] = mfma32(tile_tr<D>(K, j, 32 * dt, lane), gb, acc[dt]);
+        }
+    }
+
+    bf16 *out = dq_part + (((size_t)bh * nh + r) * L + qpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[dt][4 * g + 0], acc[dt][4 * g + 1]);
+            w.y = pack_bf16x2(acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+            *reinterpret_cast<uint2 *>(out + 32 * dt + 8 * g + 4 * h) = w;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// backward, key side: dk and dv of each round (key-owned; queries stream)
+//   dv_j += p dO_i,  dk_j += scale g q_i,  S = Q K^T and dP = dO V^T with lane = key.
+// Runs on v_mfma_f32_16x16x32_bf16 with 16 keys per wave and 8 waves per
+// workgroup (128 keys), which halves the per-lane dK^T / dV^T accumulators
+// of a 32-key wave so that two waves fit on a SIMD.
+// 16x16x32 operands: lane l supplies A[l%16][8(l/16) .. +7] and B[8(l/16) .. +7][l%16];
+// it receives C[4(l/16) + t][l%16] in acc[t].
+
+constexpr int kKvThreads = 512;
+
+// A operand (16 rows d = col0 + l%16, 8 queries) read transposed from a
+// swizzled tile: lane group g gets rows 4 g .. 4 g + 3 and 16 + 4 g .. + 3,
+// matching a B operand made of accumulator values (half 0: t = 0..3, half 1: t = 0..3).
+template <int D>
+__device__ __forceinline__ bf16x8_t tile_tr16x(const uint16_t *T, int col0, int lane)
+{
+    const int g = lane / 16, m = lane % 16;
+    const int row = 4 * g + m / 4;
+    const int col = col0 + 4 * (m % 4);
+    const uint2 a = lds_read_tr16(T + swz<D>(row, col));
+    const uint2 b = lds_read_tr16(T + swz<D>(row + 16, col));
+    const u32x4_t u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// This thread's part of one query block for 512 threads: rows [qb, qb + 32)
+// of a (chunks 0 .. 4D-1) then of b (4D .. 8D-1); a wave's 64 chunks stay
+// within one tensor.
+template <int D>
+__device__ __forceinline__ void dma_rows512(const bf16 *__restrict__ a, const bf16 *__restrict__ b, uint16_t *A,
+                                            uint16_t *B, const uint32_t *rec, int qb, size_t tok0, int tid, int wave)
+{
+    constexpr int CPR = D / 8, PER = 8 * D / kKvThreads, TCH = 4 * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int qc = i * kKvThreads + tid;
+        const int which = qc / TCH, cc = qc % TCH;
+        const int row = cc / CPR, p = cc % CPR;
+        const int lc = p ^ (row & (CPR - 1));
+        const size_t off = (tok0 + rec_lo(rec[qb + row])) * D + lc * 8;
+        const int base = ((i * kKvThreads + wave * kWave) % TCH) * 8;
+        if (which == 0)
+            dma16(a + off, A + base);
+        else
+            dma16(b + off, B + base);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(
+    int L, int nh, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
+    const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const float *__restrict__ rnorm,
+    const uint8_t *__restrict__ qtile, bf16 *__restrict__ dqk_part, bf16 *__restrict__ dv_part)
+{
+    constexpr int PER = 8 * D / kKvThreads;   // row DMAs per thread per block
+    constexpr int NW = kKvThreads / kWave;    // 8 waves
+    __shared__ __align__(16) uint16_t Qs[kStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Gs[kStages][kBlk * D];   // dO rows
+    __shared__ __align__(16) uint8_t Ts[kStages][kQTile];
+    __shared__ uint32_t qrecs[kRecCache];
+    __shared__ uint16_t kmeta[NW][kMaxEarlier][16];
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int g = lane / 16, c = lane % 16;
+    const Where W = where_of(L, nh);
+    const int r = W.r, bh = W.bh, k0 = W.s0;
+    const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
+    const size_t tok0 = (size_t)bh * L;
+
+    const int wk0 = k0 + wave * 16;
+    const int sk = wk0 + c;                       // this lane's key (sorted)
+    const int kpos = (int)rec_lo(sr[sk]);
+    const float rn = rnorm[tok0 + kpos];
+    const float krn2 = rn * scale * kLog2e;
+    if (g == 0)
+        for (int rr = 0; rr < r; ++rr)
+            kmeta[wave][rr][c] = (uint16_t)rec_lo(meta[(tok0 + kpos) * nh + rr]);
+    bf16x8_t kop[D / 32], vop[D / 32];
+    {
+        const bf16 *krow = q + (tok0 + kpos) * D, *vrow = v + (tok0 + kpos) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            kop[ks] = as_bf16x8(ld16(krow + 32 * ks + 8 * g));
+            vop[ks] = as_bf16x8(ld16(vrow + 32 * ks + 8 * g));
+        }
+    }
+    const int k_last = k0 + kRows - 1;
+    const int cache_n = min(L - k0, kRecCache);
+    for (int i = tid; i < cache_n; i += kKvThreads)
+        qrecs[i] = sr[k0 + i];
+    __syncthreads();
+    int nblocks;
+    {
+        const int qb = k0 + tid * kBlk;
+        const bool more = qb < L && tid * kBlk < cache_n && qb - (int)rec_hi(qrecs[tid * kBlk]) <= k_last;
+        nblocks = __syncthreads_count(more);
+    }
+    const uint8_t *qtb = qtile + ((size_t)bh * nh + r) * (L / kBlk) * kQTile;
+
+    auto issue = [&](int b) __attribute__((always_inline)) {
+        const int qb = k0 + b * kBlk, st = b % kStages;
+        dma_rows512<D>(q, dout, Qs[st], Gs[st], qrecs, b * kBlk, tok0, tid, wave);
+        if (wave < 2)
+            dma16(qtb + (size_t)(qb / kBlk) * kQTile + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
+    };
+
+    f32x4_t dka[D / 16], dva[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        dka[dt] = dva[dt] = f32x4_t{};
+
+    wait_vm<0>();
+    issue(0);
+    if (nblocks > 1)
+        issue(1);
+    for (int b = 0; b < nblocks; ++b) {
+        if (b + 1 < nblocks) {
+            if (wave < 2)
+                wait_vm<PER + 1>();
+            else
+                wait_vm<PER>();
+        } else {
+            wait_vm<0>();
+        }
+        block_barrier();
+        if (b + 2 < nblocks)
+            issue(b + 2);
+        const int qb = k0 + b * kBlk, st = b % kStages;
+        const uint16_t *Qt = Qs[st], *Gt = Gs[st];
+        const float *qlse2 = reinterpret_cast<const float *>(Ts[st]);
+        const float *qD = reinterpret_cast<const float *>(Ts[st] + 128);
+        const uint16_t *qwv = reinterpret_cast<const uint16_t *>(Ts[st] + 256);
+        // this wave's keys [wk0, wk0+15]: queries after a key whose window reaches it
+        const int blk_lo = qb - (int)rec_hi(qrecs[b * kBlk]);
+        if (qb + kBlk - 1 <= wk0 || blk_lo > wk0 + 15)
+            continue;
+
+        // S = Q K^T, dP = dO V^T for the two 16-query halves (lane = key c;
+        // value t of half u is query 16 u + 4 g + t)
+        f32x4_t sacc[2], pacc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            sacc[u] = pacc[u] = f32x4_t{};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                sacc[u] = mfma16(tile_row<D>(Qt, 16 * u + c, 32 * ks + 8 * g), kop[ks], sacc[u]);
+                pacc[u] = mfma16(tile_row<D>(Gt, 16 * u + c, 32 * ks + 8 * g), vop[ks], pacc[u]);
+            }
+        }
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint2 w4 = *reinterpret_cast<const uint2 *>(qwv + 16 * u + 4 * g);
+            const int wv[4] = {(int)(w4.x & 0xffffu), (int)(w4.x >> 16), (int)(w4.y & 0xffffu), (int)(w4.y >> 16)};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int sq = qb + 16 * u + 4 * g + t;   // key in [sq - w, sq)
+                ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
+            }
+        }
+        if (r > 0) {
+            uint32_t hit[4] = {0u, 0u, 0u, 0u};
+            for (int rr = 0; rr < r; ++rr) {
+                const uint32_t skp = bcast16(kmeta[wave][rr][c]);
+                const uint16_t *s1 = reinterpret_cast<const uint16_t *>(Ts[st] + 320 + 128 * rr);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
+                    const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                    hit[2 * u] |= win_hits2(a.x, ww.x, skp);
+                    hit[2 * u + 1] |= win_hits2(a.y, ww.y, skp);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+        }
+        float pr[8], gr[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float4 l4 = *reinterpret_cast<const float4 *>(qlse2 + 16 * u + 4 * g);
+            const float4 d4 = *reinterpret_cast<const float4 *>(qD + 16 * u + 4 * g);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = 4 * u + t;
+                pr[e] = ok[e] ? fast_exp2(sacc[u][t] * krn2 - lv[t]) : 0.f;
+                gr[e] = pr[e] * (pacc[u][t] - dv[t]) * scale;
+            }
+        }
+        // dV^T += dO^T P, dK^T += Q^T G: B slot s is value s of pr / gr
+        const bf16x8_t pb = pack8(pr), gb = pack8(gr);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            dva[dt] = mfma16(tile_tr16x<D>(Gt, 16 * dt, lane), pb, dva[dt]);
+            dka[dt] = mfma16(tile_tr16x<D>(Qt, 16 * dt, lane), gb, dka[dt]);
+        }
+    }
+
+    // through the key normalisation k = q rn: (dk - q rn^2 (q . dk)) rn, in fp32
+    // while dk of this round is complete; lane (key c, group g) holds
+    // d = 16 dt + 4 g + t
+    const bf16 *krow = q + (tok0 + kpos) * D;
+    float qv[D / 16][4];
+    float qd = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(krow + 16 * dt + 4 * g);
+        qv[dt][0] = __uint_as_float(u.x << 16);
+        qv[dt][1] = __uint_as_float(u.x & 0xffff0000u);
+        qv[dt][2] = __uint_as_float(u.y << 16);
+        qv[dt][3] = __uint_as_float(u.y & 0xffff0000u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            qd = fmaf(qv[dt][t], dka[dt][t], qd);
+    }
+    qd += __shfl_xor(qd, 16, kWave);
+    qd += __shfl_xor(qd, 32, kWave);
+    const float proj = rn * rn * qd;
+    const size_t row = (((size_t)bh * nh + r) * L + kpos) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int d0 = 16 * dt + 4 * g;
+        float e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            e[t] = (dka[dt][t] - qv[dt][t] * proj) * rn;
+        uint2 w;
+        w.x = pack_bf16x2(e[0], e[1]);
+        w.y = pack_bf16x2(e[2], e[3]);
+        *reinterpret_cast<uint2 *>(dqk_part + row + d0) = w;
+        w.x = pack_bf16x2(dva[dt][0], dva[dt][1]);
+        w.y = pack_bf16x2(dva[dt][2], dva[dt][3]);
+        *reinterpret_cast<uint2 *>(dv_part + row + d0) = w;
+    }
+}
+
+// Sum of the per-round partials: dQ = sum_r (dq_r + dqk_r), dV = sum_r dv_r,
+// plus dO for tokens that attend only to themselves (o = v).  D/8 lanes per
+// token, 8 elements each.
+template <int D>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int ntok, const bf16 *__restrict__ dout,
+                                                          const uint32_t *__restrict__ meta,
+                                                          const bf16 *__restrict__ dq_part,
+                                                          const bf16 *__restrict__ dqk_part,
+                                                          const bf16 *__restrict__ dv_part, bf16 *__restrict__ dq,
+                                                          bf16 *__restrict__ dv)
+{
+    constexpr int CPT = D / 8, TPB = kThreads / CPT;
+    const int grp = threadIdx.x / CPT, ch = threadIdx.x % CPT;
+    const int tok = blockIdx.x * TPB + grp;
+    if (tok >= ntok)
+        return;
+    const int bh = tok / L, t = tok % L;
+    float aq[8] = {}, av[8] = {};
+    bool alone = true;
+    for (int r = 0; r < nh; ++r) {
+        alone = alone && rec_hi(meta[(size_t)tok * nh + r]) == 0u;
+        const size_t off = (((size_t)bh * nh + r) * L + t) * D + ch * 8;
+        float x[8], y[8], z[8];
+        load8(dq_part + off, x);
+        load8(dqk_part + off, y);
+        load8(dv_part + off, z);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            aq[k] += x[k] + y[k];
+            av[k] += z[k];
+        }
+    }
+    if (alone) {
+        float x[8];
+        load8(dout + (size_t)tok * D + ch * 8, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            av[k] += x[k];
+    }
+    store8(dq + (size_t)tok * D + ch * 8, aq);
+    store8(dv + (size_t)tok * D + ch * 8, av);
+}
+
+template <int D>
+hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
+                  const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
+{
+    ProfScope prof(LSH_KERNEL_FWD, st);
+    hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
+                       P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile, (bf16 *)o_rounds,
+                       lse_rounds);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
+                  const uint32_t *meta, const uint32_t *srec, const float *rnorm, const uint8_t *ktile,
+                  const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
+{
+    const size_t n = (size_t)P.BH() * P.nh * P.L * D;
+    bf16 *dq_part = (bf16 *)part, *dqk_part = dq_part + n, *dv_part = dqk_part + n;
+    const dim3 grid((P.L / kRows) * P.nh * P.BH());
+    {
+        ProfScope prof(LSH_KERNEL_BWD_DQ, st);
+        hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
+                           (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile, dq_part);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    {
+        ProfScope prof(LSH_KERNEL_BWD_DKV, st);
+        hipLaunchKernelGGL((dkv_kernel<D>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
+                           (const bf16 *)v, (const bf16 *)dout, meta, srec, rnorm, qtile, dqk_part, dv_part);
+    }
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    const int ntok = P.BH() * P.L;
+    constexpr int TPB = kThreads / (D / 8);
+    ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
+    hipLaunchKernelGGL((reduce_kernel<D>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok,
+                       (const bf16 *)dout, meta, dq_part, dqk_part, dv_part, (bf16 *)dq, (bf16 *)dv);
+    return hipGetLastError();
+}
+
+hipError_t tiles_go(const Dims &P, const int32_t *inv, const int32_t *win_lo, const float *rnorm, const float *lse,
+                    const float *Dv, uint8_t *ktile, uint8_t *qtile, hipStream_t st)
+{
+    ProfScope prof(LSH_KERNEL_PREP, st);
+    hipLaunchKernelGGL(tile_prep_kernel, dim3((P.L + kThreads - 1) / kThreads, P.nh, P.BH()), dim3(kThreads), 0, st,
+                       P.L, P.nh, inv, win_lo, rnorm, lse, Dv, ktile, qtile);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_path_ok(const Dims &P, int dtype)
+{
+    // the streamed range of a workgroup (at most 128 + 2 m + 31 sorted rows)
+    // must fit the LDS record cache, and the metadata tiles hold 13 earlier rounds
+    return dtype == LSH_BF16 && (P.d == 64 || P.d == 128) && P.L % kRows == 0 && P.nh <= kMaxEarlier + 1 &&
+           kRows + 2 * P.m + kBlk <= kRecCache;
+}
+
+size_t mfma_ktile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * kKTile; }
+size_t mfma_qtile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * kQTile; }
+size_t bwd_mfma_part_bytes(const Dims &P) { return 3 * (size_t)P.BH() * P.nh * P.L * P.d * sizeof(uint16_t); }
+
+hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, const int32_t *inv, const int32_t *win_lo,
+                                const uint32_t *meta, const uint32_t *srec, const float *rnorm, uint8_t *ktile,
+                                void *o_rounds, float *lse_rounds, hipStream_t st)
+{
+    hipError_t e = tiles_go(P, inv, win_lo, rnorm, nullptr, nullptr, ktile, nullptr, st);
+    if (e != hipSuccess)
+        return e;
+    if (P.d == 128)
+        return fwd_go<128>(P, q, v, meta, srec, ktile, o_rounds, lse_rounds, st);
+    return fwd_go<64>(P, q, v, meta, srec, ktile, o_rounds, lse_rounds, st);
+}
+
+hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
+                                const float *Dv, const int32_t *inv, const int32_t *win_lo, const uint32_t *meta,
+                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, uint8_t *qtile, void *part,
+                                void *dq, void *dv, hipStream_t st)
+{
+    hipError_t e = tiles_go(P, inv, win_lo, rnorm, lse, Dv, ktile, qtile, st);
+    if (e != hipSuccess)
+        return e;
+    if (P.d == 128)
+        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, rnorm, ktile, qtile, part, dq, dv, st);
+    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, rnorm, ktile, qtile, part, dq, dv, st);
+}
+
+}  // namespace lsh

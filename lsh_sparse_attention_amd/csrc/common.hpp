@@ -266,15 +266,19 @@ __device__ __forceinline__ int xcd_block(int i, int n)
     return (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
 }
 
-hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const uint32_t *meta,
-                                const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
-                                hipStream_t);
+// MFMA path (bf16, d in {64, 128}); see attn_mfma.hip
 bool mfma_path_ok(const Dims &, int dtype);
+size_t mfma_ktile_bytes(const Dims &);
+size_t mfma_qtile_bytes(const Dims &);
 // bf16 per-round partials dq, dqk (key side, already through the key
 // normalisation) and dv, each [B][H][nh][L][d], in one buffer of this size
 size_t bwd_mfma_part_bytes(const Dims &);
+hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const int32_t *inv,
+                                const int32_t *win_lo, const uint32_t *meta, const uint32_t *srec,
+                                const float *rnorm, uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t);
 hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
-                                const float *D, const uint32_t *meta, const uint32_t *srec, const float *rnorm,
+                                const float *D, const int32_t *inv, const int32_t *win_lo, const uint32_t *meta,
+                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, uint8_t *qtile,
                                 void *part, void *dq, void *dv, hipStream_t);
 hipError_t launch_bwd_reduce(const Dims &, int dtype, const void *q, const void *dout, const uint32_t *meta,
                              const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,

@@ -65,12 +65,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 struct FwdWs {
     uint32_t *meta, *srec;
     float *rnorm;
+    uint8_t *ktile;
     size_t bytes;
 };
 
 struct BwdWs {
     uint32_t *meta, *srec;
     float *rnorm, *D, *dq_part, *dk_part, *dv_part;
+    uint8_t *ktile, *qtile;
     size_t bytes;
 };
 
@@ -83,6 +85,7 @@ FwdWs fwd_layout(const Dims &P, void *base)
     w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
+    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
     w.bytes = o;
     return w;
 }
@@ -100,6 +103,8 @@ BwdWs bwd_layout(const Dims &P, void *base)
     w.dq_part = (float *)(b + o); o += align_up(part, 256);
     w.dk_part = (float *)(b + o); o += align_up(part, 256);
     w.dv_part = (float *)(b + o); o += align_up(part, 256);
+    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
+    w.qtile = (uint8_t *)(b + o); o += align_up(mfma_qtile_bytes(P), 256);
     w.bytes = o;
     return w;
 }
@@ -194,7 +199,8 @@ int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const 
                                nullptr, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype))
-            e = launch_attn_fwd_mfma(P, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
+            e = launch_attn_fwd_mfma(P, q, v, inv, win_lo, w.meta, w.srec, w.rnorm, w.ktile, o_rounds, lse_rounds,
+                                     s);
         else
             e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
     }
@@ -233,7 +239,8 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, out, dout, w.D, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype)) {
-            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part, dq, dv, s);
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, inv, win_lo, w.meta, w.srec, w.rnorm, w.ktile, w.qtile,
+                                     w.dq_part, dq, dv, s);
         } else {
             e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part,
                                 w.dk_part, w.dv_part, dq, dv, s);
