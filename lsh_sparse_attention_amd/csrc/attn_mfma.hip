@@ -149,36 +149,41 @@ __device__ __forceinline__ void clear_hits(bool (&ok)[16], const uint32_t (&hit)
 // ---------------------------------------------------------------------------
 // metadata tiles, per 32 sorted rows of each (b, h, round)
 
-__global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, const int32_t *__restrict__ inv,
-                                                             const int32_t *__restrict__ win_lo,
+// One wave per tile of 32 sorted rows: lanes 0..31 fill the key tile, lanes
+// 32..63 the query tile; every field is written as one contiguous run.
+__global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int ntiles,
+                                                             const uint32_t *__restrict__ srec,
+                                                             const uint32_t *__restrict__ meta,
                                                              const float *__restrict__ rnorm,
                                                              const float *__restrict__ lse,
                                                              const float *__restrict__ Dvec,
                                                              uint8_t *__restrict__ ktile, uint8_t *__restrict__ qtile)
 {
-    const int t = blockIdx.x * kThreads + threadIdx.x;
-    const int r = blockIdx.y, bh = blockIdx.z;
-    if (t >= L)
+    const int lane = threadIdx.x % kWave;
+    const int tile = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+    if (tile >= ntiles)
         return;
-    const size_t tok = (size_t)bh * L + t;
-    const int s = inv[((size_t)bh * nh + r) * L + t];
-    const size_t tidx = ((size_t)bh * nh + r) * (L / kBlk) + s / kBlk;
-    const int k = s % kBlk;
-    uint8_t *kt = ktile + tidx * kKTile;
-    reinterpret_cast<float *>(kt)[k] = rnorm[tok];
-    uint8_t *qt = qtile ? qtile + tidx * kQTile : nullptr;
-    if (qt) {
+    const int per = L / kBlk;
+    const int blk = tile % per, r = (tile / per) % nh, bh = tile / (per * nh);
+    const int k = lane % kBlk;
+    const uint32_t rec = srec[((size_t)bh * nh + r) * L + blk * kBlk + k];
+    const size_t tok = (size_t)bh * L + rec_lo(rec);
+    const uint32_t *m = meta + tok * nh;
+    const int nr = r < kMaxEarlier ? r : kMaxEarlier;
+    if (lane < kBlk) {
+        uint8_t *kt = ktile + (size_t)tile * kKTile;
+        reinterpret_cast<float *>(kt)[k] = rnorm[tok];
+        for (int rr = 0; rr < nr; ++rr)
+            reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] = (uint16_t)rec_lo(m[rr]);
+    } else if (qtile) {
+        uint8_t *qt = qtile + (size_t)tile * kQTile;
         reinterpret_cast<float *>(qt)[k] = lse[tok] * kLog2e;
         reinterpret_cast<float *>(qt + 128)[k] = Dvec[tok];
-        reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)(s - win_lo[((size_t)bh * nh + r) * L + t]);
-    }
-    for (int rr = 0; rr < r && rr < kMaxEarlier; ++rr) {
-        const size_t i2 = ((size_t)bh * nh + rr) * L + t;
-        const int s2 = inv[i2];
-        reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] = (uint16_t)s2;
-        if (qt) {
-            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(s2 - 1);
-            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)(s2 - win_lo[i2]);
+        reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
+        for (int rr = 0; rr < nr; ++rr) {
+            const uint32_t mr = m[rr];
+            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(rec_lo(mr) - 1u);
+            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)rec_hi(mr);
         }
     }
 }
@@ -839,12 +844,14 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     return hipGetLastError();
 }
 
-hipError_t tiles_go(const Dims &P, const int32_t *inv, const int32_t *win_lo, const float *rnorm, const float *lse,
+hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, const float *rnorm, const float *lse,
                     const float *Dv, uint8_t *ktile, uint8_t *qtile, hipStream_t st)
 {
+    const int ntiles = P.BH() * P.nh * (P.L / kBlk);
+    const int per_block = kThreads / kWave;
     ProfScope prof(LSH_KERNEL_PREP, st);
-    hipLaunchKernelGGL(tile_prep_kernel, dim3((P.L + kThreads - 1) / kThreads, P.nh, P.BH()), dim3(kThreads), 0, st,
-                       P.L, P.nh, inv, win_lo, rnorm, lse, Dv, ktile, qtile);
+    hipLaunchKernelGGL(tile_prep_kernel, dim3((ntiles + per_block - 1) / per_block), dim3(kThreads), 0, st, P.L, P.nh,
+                       ntiles, srec, meta, rnorm, lse, Dv, ktile, qtile);
     return hipGetLastError();
 }
 
@@ -866,7 +873,9 @@ hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, con
                                 const uint32_t *meta, const uint32_t *srec, const float *rnorm, uint8_t *ktile,
                                 void *o_rounds, float *lse_rounds, hipStream_t st)
 {
-    hipError_t e = tiles_go(P, inv, win_lo, rnorm, nullptr, nullptr, ktile, nullptr, st);
+    (void)inv;
+    (void)win_lo;
+    hipError_t e = tiles_go(P, srec, meta, rnorm, nullptr, nullptr, ktile, nullptr, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)
@@ -879,7 +888,9 @@ hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, con
                                 const uint32_t *srec, const float *rnorm, uint8_t *ktile, uint8_t *qtile, void *part,
                                 void *dq, void *dv, hipStream_t st)
 {
-    hipError_t e = tiles_go(P, inv, win_lo, rnorm, lse, Dv, ktile, qtile, st);
+    (void)inv;
+    (void)win_lo;
+    hipError_t e = tiles_go(P, srec, meta, rnorm, lse, Dv, ktile, qtile, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)

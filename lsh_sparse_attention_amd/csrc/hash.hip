@@ -72,23 +72,27 @@ __global__ __launch_bounds__(kHashThreads) void hash_generic(int L, int nh, int 
 
 // bf16 path on the matrix cores.  A workgroup (4 waves) owns 256 rows of one
 // (batch, head); a wave owns 64 rows as two 32-row MFMA column tiles.  For
-// every round, the rotation is walked in tiles of 32 columns, staged
-// transposed in LDS; Y^T = R^T Q^T comes out with lane = row and 16 columns
-// per lane, so the running argmax of +y and of -y stays in registers, in
-// increasing column order (strict comparisons keep the first index).  The two
-// lane halves that share a row are merged at the end.  bf16 products are exact
-// in the fp32 accumulator.
+// every round the rotation is walked in blocks of 64 columns, staged
+// row-major in LDS (fetched one block ahead) and read transposed with
+// ds_read_b64_tr_b16, so Y^T = R^T Q^T comes out with lane = row and 16
+// columns per lane per 32-column tile.  The running argmax of +y and of -y
+// stays in registers in increasing column order (strict comparisons keep the
+// first index); the column offsets are wave-uniform, so the index select
+// takes them from scalar registers and the lane's own offset 4 h is added at
+// the end.  The two lane halves that share a row are merged last.  bf16
+// products are exact in the fp32 accumulator.
 constexpr int kHashRows = 256;
+constexpr int kHashCols = 64;              // rotation columns per staged block
 
 template <int D>
 __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, int half, const bf16 *__restrict__ q,
                                                                  const bf16 *__restrict__ rot,
                                                                  int32_t *__restrict__ buckets)
 {
-    constexpr int P = D + 8;
-    __shared__ __align__(16) uint16_t RT[32 * P];   // [column j][d]
+    constexpr int P = kHashCols + 8;   // LDS pitch (elements) of the row-major [d][64] block
+    __shared__ __align__(16) uint16_t Rs[D * P];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int h = lane / 32, c = lane % 32;
+    const int h = lane / 32, c = lane % 32, grp = lane / 16, m = lane % 16;
     const int bh = blockIdx.y;
     const int row0 = blockIdx.x * kHashRows + wave * 64;
 
@@ -102,99 +106,120 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
             qop[ct][ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
     }
     const uint16_t *Rbits = reinterpret_cast<const uint16_t *>(rot);
-    // Staging of one 32-column tile: item i = (row d = i / 4, columns
-    // 8 (i % 4) .. +7), kItems per thread, fetched one tile ahead.
-    constexpr int kItems = (D * 4 + kHashThreads - 1) / kHashThreads;
-    const int ntile = (half + 31) / 32;
+    // staging: item i = (row d = i / 8, columns 8 (i % 8) .. +7 of the block)
+    constexpr int kItems = D * (kHashCols / 8) / kHashThreads;   // 4 (D=128), 2 (D=64), 1 (D=32)
+    const int nblk = (half + kHashCols - 1) / kHashCols;
     const bool vec = (half % 8) == 0;
     u32x4_t pre[kItems];
-    auto fetch = [&](int tile) __attribute__((always_inline)) {
-        const int r = tile / ntile, j0 = (tile % ntile) * 32;
+    auto fetch = [&](int blk) __attribute__((always_inline)) {
+        const int r = blk / nblk, j0 = (blk % nblk) * kHashCols;
         const uint16_t *R = Rbits + (size_t)r * D * half;
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int i = tid + it * kHashThreads;
-            const int d = i / 4, j = j0 + 8 * (i % 4);
+            const int d = i / 8, j = j0 + 8 * (i % 8);
             u32x4_t u = {0u, 0u, 0u, 0u};
-            if (i < D * 4) {
-                if (vec && j + 8 <= half) {
-                    u = ld16(R + (size_t)d * half + j);
-                } else {
-                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+            if (vec && j + 8 <= half) {
+                u = ld16(R + (size_t)d * half + j);
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (j + e < half)
-                            w[e / 2] |= (uint32_t)R[(size_t)d * half + j + e] << (16 * (e % 2));
-                    u = u32x4_t{w[0], w[1], w[2], w[3]};
-                }
+                for (int e = 0; e < 8; ++e)
+                    if (j + e < half)
+                        w[e / 2] |= (uint32_t)R[(size_t)d * half + j + e] << (16 * (e % 2));
+                u = u32x4_t{w[0], w[1], w[2], w[3]};
             }
             pre[it] = u;
         }
     };
 
-    float bp[2] = {-INFINITY, -INFINITY}, bn[2] = {-INFINITY, -INFINITY};
+    // running max of +y (bp, ip) and running min of y (mn, in): -y > -mn <=> y < mn
+    float bp[2] = {-INFINITY, -INFINITY}, mn[2] = {INFINITY, INFINITY};
     int ip[2] = {0, 0}, in[2] = {0, 0};
     fetch(0);
-    for (int tile = 0; tile < nh * ntile; ++tile) {
-        const int r = tile / ntile, j0 = (tile % ntile) * 32;
+    for (int blk = 0; blk < nh * nblk; ++blk) {
+        const int r = blk / nblk, jb = (blk % nblk) * kHashCols;
         __syncthreads();
-        // RT[jj][d] = R[d][j0 + jj] (zero past the last column)
 #pragma unroll
         for (int it = 0; it < kItems; ++it) {
             const int i = tid + it * kHashThreads;
-            if (i < D * 4) {
-                const int d = i / 4, jj = 8 * (i % 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    RT[(jj + e) * P + d] = (uint16_t)(pre[it][e / 2] >> (16 * (e % 2)));
-            }
+            st16(&Rs[(i / 8) * P + 8 * (i % 8)], pre[it]);
         }
         __syncthreads();
-        if (tile + 1 < nh * ntile)
-            fetch(tile + 1);
-        const bool full = j0 + 32 <= half;
+        if (blk + 1 < nh * nblk)
+            fetch(blk + 1);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            f32x16_t acc = f32x16_t{};
+        for (int jt = 0; jt < kHashCols / 32; ++jt) {
+            const int j0 = jb + 32 * jt;
+            if (j0 >= half)
+                break;
+            // A operand: lane (column j0 + c, half h) gets d = 16 ks + 8 h + 0..7
+            bf16x8_t aop[D / 16];
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                acc = mfma32(as_bf16x8(ld16(&RT[c * P + 16 * ks + 8 * h])), qop[ct][ks], acc);
-            // acc[4 g + t] = y[column j0 + 8 g + 4 h + t] of row c
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int dr = 16 * ks + 8 * (grp / 2) + m / 4;
+                const int col = 32 * jt + 16 * (grp % 2) + 4 * (m % 4);
+                const uint2 x = lds_read_tr16(&Rs[dr * P + col]);
+                const uint2 y = lds_read_tr16(&Rs[(dr + 4) * P + col]);
+                aop[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x.x, x.y, y.x, y.y});
+            }
+            const bool full = j0 + 32 <= half;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = j0 + 8 * (e / 4) + 4 * h + (e % 4);
-                const float y = acc[e];
-                if (full || j < half) {
-                    if (y > bp[ct]) {
-                        bp[ct] = y;
-                        ip[ct] = j;
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x16_t acc = f32x16_t{};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    acc = mfma32(aop[ks], qop[ct][ks], acc);
+                // acc[4 g + t] = y[column j0 + 8 g + 4 h + t] of row c; the
+                // uniform part j0 + 8 g + t is selected, 4 h added at the end
+                if (full) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ju = j0 + 8 * (e / 4) + (e % 4);
+                        const float yv = acc[e];
+                        const bool gp = yv > bp[ct], gn = yv < mn[ct];
+                        ip[ct] = gp ? ju : ip[ct];
+                        bp[ct] = gp ? yv : bp[ct];
+                        in[ct] = gn ? ju : in[ct];
+                        mn[ct] = gn ? yv : mn[ct];
                     }
-                    if (-y > bn[ct]) {
-                        bn[ct] = -y;
-                        in[ct] = j;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ju = j0 + 8 * (e / 4) + (e % 4);
+                        const float yv = (ju + 4 * h < half) ? acc[e] : NAN;   // NaN never wins
+                        const bool gp = yv > bp[ct], gn = yv < mn[ct];
+                        ip[ct] = gp ? ju : ip[ct];
+                        bp[ct] = gp ? yv : bp[ct];
+                        in[ct] = gn ? ju : in[ct];
+                        mn[ct] = gn ? yv : mn[ct];
                     }
                 }
             }
         }
-        if (j0 + 32 >= half) {
-            // last tile of round r
+        if (jb + kHashCols >= half) {
+            // last block of round r
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
+                ip[ct] += 4 * h;
+                in[ct] += 4 * h;
                 // merge with the other half of the row (first index on ties)
-                const float obp = __shfl_xor(bp[ct], 32, kWave), obn = __shfl_xor(bn[ct], 32, kWave);
+                const float obp = __shfl_xor(bp[ct], 32, kWave), omn = __shfl_xor(mn[ct], 32, kWave);
                 const int oip = __shfl_xor(ip[ct], 32, kWave), oin = __shfl_xor(in[ct], 32, kWave);
                 if (obp > bp[ct] || (obp == bp[ct] && oip < ip[ct])) {
                     bp[ct] = obp;
                     ip[ct] = oip;
                 }
-                if (obn > bn[ct] || (obn == bn[ct] && oin < in[ct])) {
-                    bn[ct] = obn;
+                if (omn < mn[ct] || (omn == mn[ct] && oin < in[ct])) {
+                    mn[ct] = omn;
                     in[ct] = oin;
                 }
                 const int row = row0 + 32 * ct + c;
+                // first index of the maximum over [+y ; -y]: the +y half wins ties
                 if (h == 0 && row < L)
-                    buckets[((size_t)bh * nh + r) * L + row] = (bp[ct] >= bn[ct]) ? ip[ct] : half + in[ct];
-                bp[ct] = bn[ct] = -INFINITY;
+                    buckets[((size_t)bh * nh + r) * L + row] = (bp[ct] >= -mn[ct]) ? ip[ct] : half + in[ct];
+                bp[ct] = -INFINITY;
+                mn[ct] = INFINITY;
                 ip[ct] = in[ct] = 0;
             }
         }
