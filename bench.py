@@ -37,27 +37,33 @@ WORKLOAD_NAMES = {
     "text": "long-text-shaped (L=65536)",
     "stress": "stress: 256-cluster Gaussian mixture (B=4, L=65536)",
 }
-# source file of each kernel, for matching stored counter measurements
+# source file of each kernel on the bf16 matrix-core path, for matching stored
+# counter measurements to the code they were taken on
 KERNEL_SOURCE = {
     "hash": "hash.hip", "sort_hist": "sort.hip", "sort_scan": "sort.hip", "sort_scatter": "sort.hip",
-    "prep": "attn_generic.hip", "attn_fwd": "attn_generic.hip", "combine": "attn_generic.hip",
-    "bwd_dq": "attn_generic.hip", "bwd_dkv": "attn_generic.hip", "bwd_reduce": "attn_generic.hip",
+    "prep": "attn_generic.hip", "tiles": "attn_mfma.hip", "attn_fwd": "attn_mfma.hip",
+    "combine": "attn_generic.hip", "bwd_dq": "attn_mfma.hip", "bwd_dkv": "attn_mfma.hip",
+    "bwd_reduce": "attn_mfma.hip",
 }
 
 
-def algorithmic_work(name: str, cfg) -> tuple[float, float]:
+def algorithmic_work(name: str, cfg, backward_prep: bool = True) -> tuple[float, float]:
     """(flops, bytes) that one launch of kernel `name` must do for `cfg`.
 
-    Counts the minimal data movement of each kernel (every input read once,
-    every output written once) and the dense-tile flops of the method
-    (nominal m x 2m chunk tiles, chunk 0 sees m keys)."""
+    Bytes count every input a kernel needs read once and every output written
+    once (row gathers by position count their rows once per round; a
+    per-round result is written once).  Flops count the method's dense chunk
+    tiles: m x 2m query-key pairs per chunk (chunk 0 sees m keys), 2 d flops
+    per product per pair.  Per-round gradient partials are bf16 on this path.
+    """
     s = 2 if cfg.dtype == "bf16" else 4
     B, H, L, d, nh, nb, m = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets, cfg.chunk_len
     T = B * H * L
     Tr = T * nh
     S = B * H * nh
     ntiles = -(-L // 2048)
-    tile_pairs = (8.0 * m * L * d - 4.0 * m * m * d) * B * H * nh / (4.0 * d)   # query-key pairs per launch
+    pairs = (2.0 * m * L - m * m) * B * H * nh      # query-key pairs of the dense chunk tiles
+    meta = 4 * nh                                   # one packed record per round
     if name == "hash":
         return 2.0 * T * nh * (nb // 2) * d, T * d * s + nh * d * (nb // 2) * s + Tr * 4
     if name == "sort_hist":
@@ -66,18 +72,20 @@ def algorithmic_work(name: str, cfg) -> tuple[float, float]:
         return 0.0, 4 * S * ntiles * nb * 4 + S * nb * 4
     if name == "sort_scatter":
         return 0.0, Tr * 4 + S * ntiles * nb * 4 + Tr * 12
-    if name == "prep":
-        return 0.0, T * d * s + Tr * 16 + T * 4 + 2 * T * d * s + T * 4
-    if name == "attn_fwd":
-        return 4.0 * d * tile_pairs, Tr * (3 * d * s + 8 + 4 * nh)
+    if name == "prep":   # backward prep: q for norms, out and dout for D; records in/out
+        return 0.0, T * d * s * (3 if backward_prep else 1) + Tr * 16 + T * 8
+    if name == "tiles":  # backward tiles: key and query tiles per 32 sorted rows
+        return 0.0, Tr * (4 + meta + 12) + Tr * (32 + 64)
+    if name == "attn_fwd":   # q, v rows; o row and lse written
+        return 2.0 * 2 * d * pairs, Tr * (3 * d * s + 4 + 4 + 32)
     if name == "combine":
         return 0.0, Tr * (d * s + 4) + T * (d * s + 4)
-    if name == "bwd_dq":
-        return 6.0 * d * tile_pairs, Tr * (4 * d * s + 4 * d + 16 + 4 * nh)
-    if name == "bwd_dkv":
-        return 8.0 * d * tile_pairs, Tr * (4 * d * s + 8 * d + 16 + 4 * nh)
-    if name == "bwd_reduce":
-        return 0.0, Tr * 12 * d + T * (4 * d * s + 4 + 4 * nh)
+    if name == "bwd_dq":     # q, v, dout rows; bf16 dq partial
+        return 3.0 * 2 * d * pairs, Tr * (3 * d * s + 2 * d + 12 + 32)
+    if name == "bwd_dkv":    # q, v, dout rows; bf16 dqk and dv partials
+        return 4.0 * 2 * d * pairs, Tr * (3 * d * s + 4 * d + 12 + 64)
+    if name == "bwd_reduce":  # three bf16 partials per round in; dq, dv out
+        return 0.0, Tr * 3 * 2 * d + T * (2 * d * s + meta)
     raise KeyError(name)
 
 

@@ -184,7 +184,9 @@ typedef enum {
     LSH_KERNEL_BWD_DQ = 7,      /* lsh_attn_bwd: query-side gradient per round      */
     LSH_KERNEL_BWD_DKV = 8,     /* lsh_attn_bwd: key-side gradients per round       */
     LSH_KERNEL_BWD_REDUCE = 9,  /* lsh_attn_bwd: sum over rounds, key normalisation */
-    LSH_KERNEL_COUNT = 10
+    LSH_KERNEL_TILES = 10,      /* lsh_attn_fwd / lsh_attn_bwd (bf16 matrix-core
+                                   path): per-32-row metadata tiles             */
+    LSH_KERNEL_COUNT = 11
 } lsh_kernel_t;
 
 /* Name of a kernel id (static storage), or NULL for an unknown id. */

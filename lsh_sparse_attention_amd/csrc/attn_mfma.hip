@@ -849,7 +849,7 @@ hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, c
 {
     const int ntiles = P.BH() * P.nh * (P.L / kBlk);
     const int per_block = kThreads / kWave;
-    ProfScope prof(LSH_KERNEL_PREP, st);
+    ProfScope prof(LSH_KERNEL_TILES, st);
     hipLaunchKernelGGL(tile_prep_kernel, dim3((ntiles + per_block - 1) / per_block), dim3(kThreads), 0, st, P.L, P.nh,
                        ntiles, srec, meta, rnorm, lse, Dv, ktile, qtile);
     return hipGetLastError();

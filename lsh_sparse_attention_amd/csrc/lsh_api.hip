@@ -13,7 +13,7 @@ hipEvent_t g_prof_stop[LSH_KERNEL_COUNT];
 
 const char *const kKernelNames[LSH_KERNEL_COUNT] = {
     "hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq", "bwd_dkv",
-    "bwd_reduce"};
+    "bwd_reduce", "tiles"};
 
 }  // namespace
 
