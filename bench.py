@@ -115,9 +115,12 @@ class Hip:
 
 
 def source_sha(kernel: str) -> str:
-    path = os.path.join(ROOT, "lsh_sparse_attention_amd", "csrc", KERNEL_SOURCE[kernel])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the sources a kernel is compiled from (its file and the shared header)."""
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCE[kernel], "common.hpp"):
+        with open(os.path.join(ROOT, "lsh_sparse_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel: str, workload: str):
@@ -156,7 +159,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="text")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="heads of batch 0 the oracle times (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads of batch 0 the oracle times (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three device copies of 1 GiB (reference point for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -165,6 +170,16 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_calibration:
+        n = 1 << 28                                   # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n, "copies": 3}}), flush=True)
+        return 0
     import lsh_sparse_attention_amd as lsh
     from lsh_sparse_attention_amd import _lib
     from lsh_sparse_attention_amd import inputs as gen
