@@ -19,7 +19,10 @@
 // owns 128 consecutive sorted rows of one (batch, head, round); the other
 // operand streams through LDS in blocks of 32 sorted rows.  Rows are fetched
 // by position straight into LDS with global_load_lds_dwordx4 (no staging
-// registers) into a 3-deep ring, two blocks ahead of the block in use; each
+// registers) into a ring of LDS stages, several blocks ahead of the block in
+// use, so that enough bytes are in flight per CU to cover the loaded memory
+// latency (the query-owned kernels run two workgroups per CU, the key-owned
+// one a single workgroup with a deeper ring); each
 // wave waits on its own outstanding loads with s_waitcnt vmcnt and a
 // workgroup barrier publishes the block.  Tiles are stored unpadded with the
 // 16-byte chunks of row r XOR-swizzled by r, so that both the row reads
@@ -36,7 +39,8 @@ namespace {
 constexpr int kRows = 128;     // rows owned by a workgroup
 constexpr int kBlk = 32;       // streamed rows per block
 constexpr int kThreads = 256;
-constexpr int kStages = 3;
+constexpr int kQStages = 4;     // ring depth of the query-owned kernels (two workgroups per CU)
+constexpr int kKvStages = 8;    // blocks resident at once in the key-owned kernel (one workgroup per CU)
 constexpr int kRecCache = 1024;           // sorted records of a workgroup's streamed range
 constexpr int kMaxEarlier = 13;           // earlier rounds a tile holds (n_hashes <= 14)
 constexpr int kKTile = 1024;              // key tile: rn[32] f32, sk[13][32] u16
@@ -68,12 +72,37 @@ __device__ __forceinline__ void block_barrier()
     asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier after this wave's own LDS stores (ds_write) must be
+// visible to the other waves; vector-memory loads are not waited for.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // wait until at most N vector-memory operations of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
     static_assert(N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait for the oldest block of the ring: n younger blocks (OPS loads each)
+// may stay in flight.  n is wave-uniform and at most MAXN.
+template <int OPS, int MAXN>
+__device__ __forceinline__ void wait_ring(int n)
+{
+    if constexpr (MAXN == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= MAXN)
+            wait_vm<MAXN * OPS>();
+        else
+            wait_ring<OPS, MAXN - 1>(n);
+    }
 }
 
 // element offset of (row, col) in an unpadded D-wide bf16 tile whose 16-byte
@@ -207,16 +236,16 @@ __device__ __forceinline__ Where where_of(int L, int nh)
 // forward (query-owned)
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(int L, int nh, float scale_log2, const bf16 *__restrict__ q,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(int L, int nh, int maxw, float scale_log2, const bf16 *__restrict__ q,
                                                        const bf16 *__restrict__ v, const uint32_t *__restrict__ meta,
                                                        const uint32_t *__restrict__ srec,
                                                        const uint8_t *__restrict__ ktile,
                                                        bf16 *__restrict__ o_rounds, float *__restrict__ lse_rounds)
 {
     constexpr int KPT = D / 64;
-    __shared__ __align__(16) uint16_t Ks[kStages][kBlk * D];
-    __shared__ __align__(16) uint16_t Vs[kStages][kBlk * D];
-    __shared__ __align__(16) uint8_t Ts[kStages][kKTile];
+    __shared__ __align__(16) uint16_t Ks[kQStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Vs[kQStages][kBlk * D];
+    __shared__ __align__(16) uint8_t Ts[kQStages][kKTile];
     __shared__ uint32_t krec[kRecCache];
     __shared__ uint32_t qmeta[kThreads / kWave][kMaxEarlier][32];
 
@@ -227,12 +256,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
 
+    // Prologue, two dependent memory round trips: (1) the sorted records of
+    // every row the workgroup can touch, [s0 - maxw, s0 + 128) (maxw bounds
+    // a window); (2) the first key blocks (straight into LDS) together with
+    // this lane's query row and its earlier-round records.
+    const int c0 = s0 - min(s0, maxw);
+    const int cache_n = s0 + kRows - c0;
+    for (int i = tid; i < cache_n; i += kThreads)
+        krec[i] = sr[c0 + i];
+    wait_vm<0>();
+    lds_barrier();
     const int wq0 = s0 + wave * 32;
     const int sq = wq0 + c;
-    const uint32_t qrec = sr[sq];
+    const uint32_t qrec = krec[sq - c0];
     const int qpos = (int)rec_lo(qrec), qw = (int)rec_hi(qrec);
     const int qlo = sq - qw;
     const int wlo = __builtin_amdgcn_readlane(qlo, 0);
+    const int kb_first = (s0 - (int)rec_hi(krec[s0 - c0])) & ~(kBlk - 1);
+    const int nblocks = (s0 + kRows - kb_first) / kBlk;
+    const uint32_t *kr = krec + (kb_first - c0);
+    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
+
+    auto issue = [&](int b) __attribute__((always_inline)) {
+        const int kb = kb_first + b * kBlk, st = b % kQStages;
+        dma_rows<D>(q, v, Ks[st], Vs[st], kr, b * kBlk, tok0, tid, wave);
+        if (wave == 0)
+            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
+    };
+    constexpr int AHEAD = kQStages - 1;
+    for (int b = 0; b < AHEAD && b < nblocks; ++b)
+        issue(b);
+
     if (h == 0)
         for (int rr = 0; rr < r; ++rr)
             qmeta[wave][rr][c] = meta[(tok0 + qpos) * nh + rr];
@@ -243,19 +297,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int ks = 0; ks < D / 16; ++ks)
             qop[ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
     }
-    const int kb_first = (s0 - (int)rec_hi(sr[s0])) & ~(kBlk - 1);
-    const int nblocks = (s0 + kRows - kb_first) / kBlk;
-    for (int i = tid; i < nblocks * kBlk; i += kThreads)
-        krec[i] = sr[kb_first + i];
-    __syncthreads();
-    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
-
-    auto issue = [&](int b) __attribute__((always_inline)) {
-        const int kb = kb_first + b * kBlk, st = b % kStages;
-        dma_rows<D>(q, v, Ks[st], Vs[st], krec, b * kBlk, tok0, tid, wave);
-        if (wave == 0)
-            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
-    };
 
     f32x16_t oacc[D / 32];
 #pragma unroll
@@ -263,25 +304,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         oacc[dt] = f32x16_t{};
     float mrun = -INFINITY, lrun = 0.f;
 
-    // operands loaded into registers above are complete before the ring starts,
-    // so no wait inside the loop has to cover them
+    // the register operands and the first blocks are complete before the
+    // ring turns, so no wait inside the loop has to cover a register load
     wait_vm<0>();
-    issue(0);
-    if (nblocks > 1)
-        issue(1);
     for (int b = 0; b < nblocks; ++b) {
-        if (b + 1 < nblocks) {
-            if (wave == 0)
-                wait_vm<2 * KPT + 1>();
-            else
-                wait_vm<2 * KPT>();
-        } else {
-            wait_vm<0>();
-        }
+        const int younger = min(AHEAD - 1, nblocks - 1 - b);
+        if (wave == 0)
+            wait_ring<2 * KPT + 1, AHEAD - 1>(younger);
+        else
+            wait_ring<2 * KPT, AHEAD - 1>(younger);
         block_barrier();
-        if (b + 2 < nblocks)
-            issue(b + 2);
-        const int kb = kb_first + b * kBlk, st = b % kStages;
+        if (b + AHEAD < nblocks)
+            issue(b + AHEAD);
+        const int kb = kb_first + b * kBlk, st = b % kQStages;
         // keys [kb, kb+31] against this wave's windows
         if (kb > wq0 || kb + kBlk - 1 < wlo)
             continue;
@@ -376,7 +411,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 //   dq_i += scale g k_j = scale g rn_j q_j
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(int L, int nh, float scale, const bf16 *__restrict__ q,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(int L, int nh, int maxw, float scale, const bf16 *__restrict__ q,
                                                       const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
                                                       const float *__restrict__ lse, const float *__restrict__ Dvec,
                                                       const uint32_t *__restrict__ meta,
@@ -384,9 +419,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                                       const uint8_t *__restrict__ ktile, bf16 *__restrict__ dq_part)
 {
     constexpr int KPT = D / 64;
-    __shared__ __align__(16) uint16_t Ks[kStages][kBlk * D];
-    __shared__ __align__(16) uint16_t Vs[kStages][kBlk * D];
-    __shared__ __align__(16) uint8_t Ts[kStages][kKTile];
+    __shared__ __align__(16) uint16_t Ks[kQStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Vs[kQStages][kBlk * D];
+    __shared__ __align__(16) uint8_t Ts[kQStages][kKTile];
     __shared__ uint32_t krec[kRecCache];
     __shared__ uint32_t qmeta[kThreads / kWave][kMaxEarlier][32];
 
@@ -398,12 +433,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const size_t tok0 = (size_t)bh * L;
     const float scale_log2 = scale * kLog2e;
 
+    // Prologue in two dependent memory round trips, as in the forward.
+    const int c0 = s0 - min(s0, maxw);
+    const int cache_n = s0 + kRows - c0;
+    for (int i = tid; i < cache_n; i += kThreads)
+        krec[i] = sr[c0 + i];
+    wait_vm<0>();
+    lds_barrier();
     const int wq0 = s0 + wave * 32;
     const int sq = wq0 + c;
-    const uint32_t qrec = sr[sq];
+    const uint32_t qrec = krec[sq - c0];
     const int qpos = (int)rec_lo(qrec), qw = (int)rec_hi(qrec);
     const int qlo = sq - qw;
     const int wlo = __builtin_amdgcn_readlane(qlo, 0);
+    const int kb_first = (s0 - (int)rec_hi(krec[s0 - c0])) & ~(kBlk - 1);
+    const int nblocks = (s0 + kRows - kb_first) / kBlk;
+    const uint32_t *kr = krec + (kb_first - c0);
+    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
+
+    auto issue = [&](int b) __attribute__((always_inline)) {
+        const int kb = kb_first + b * kBlk, st = b % kQStages;
+        dma_rows<D>(q, v, Ks[st], Vs[st], kr, b * kBlk, tok0, tid, wave);
+        if (wave == 0)
+            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
+    };
+    constexpr int AHEAD = kQStages - 1;
+    for (int b = 0; b < AHEAD && b < nblocks; ++b)
+        issue(b);
+
     if (h == 0)
         for (int rr = 0; rr < r; ++rr)
             qmeta[wave][rr][c] = meta[(tok0 + qpos) * nh + rr];
@@ -418,44 +475,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             gop[ks] = as_bf16x8(ld16(grow + 16 * ks + 8 * h));
         }
     }
-    const int kb_first = (s0 - (int)rec_hi(sr[s0])) & ~(kBlk - 1);
-    const int nblocks = (s0 + kRows - kb_first) / kBlk;
-    for (int i = tid; i < nblocks * kBlk; i += kThreads)
-        krec[i] = sr[kb_first + i];
-    __syncthreads();
-    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
-
-    auto issue = [&](int b) __attribute__((always_inline)) {
-        const int kb = kb_first + b * kBlk, st = b % kStages;
-        dma_rows<D>(q, v, Ks[st], Vs[st], krec, b * kBlk, tok0, tid, wave);
-        if (wave == 0)
-            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
-    };
 
     f32x16_t acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
         acc[dt] = f32x16_t{};
 
-    // operands loaded into registers above are complete before the ring starts,
-    // so no wait inside the loop has to cover them
+    // the register operands and the first blocks are complete before the
+    // ring turns, so no wait inside the loop has to cover a register load
     wait_vm<0>();
-    issue(0);
-    if (nblocks > 1)
-        issue(1);
     for (int b = 0; b < nblocks; ++b) {
-        if (b + 1 < nblocks) {
-            if (wave == 0)
-                wait_vm<2 * KPT + 1>();
-            else
-                wait_vm<2 * KPT>();
-        } else {
-            wait_vm<0>();
-        }
+        const int younger = min(AHEAD - 1, nblocks - 1 - b);
+        if (wave == 0)
+            wait_ring<2 * KPT + 1, AHEAD - 1>(younger);
+        else
+            wait_ring<2 * KPT, AHEAD - 1>(younger);
         block_barrier();
-        if (b + 2 < nblocks)
-            issue(b + 2);
-        const int kb = kb_first + b * kBlk, st = b % kStages;
+        if (b + AHEAD < nblocks)
+            issue(b + AHEAD);
+        const int kb = kb_first + b * kBlk, st = b % kQStages;
         if (kb > wq0 || kb + kBlk - 1 < wlo)
             continue;
         const uint16_t *K = Ks[st], *V = Vs[st];
@@ -573,16 +611,14 @@ __device__ __forceinline__ void dma_rows512(const bf16 *__restrict__ a, const bf
 template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(
     int L, int nh, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
-    const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const float *__restrict__ rnorm,
-    const uint8_t *__restrict__ qtile, bf16 *__restrict__ dqk_part, bf16 *__restrict__ dv_part)
+    const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile, const uint8_t *__restrict__ qtile,
+    bf16 *__restrict__ dkr_part, bf16 *__restrict__ dv_part)
 {
-    constexpr int PER = 8 * D / kKvThreads;   // row DMAs per thread per block
-    constexpr int NW = kKvThreads / kWave;    // 8 waves
-    __shared__ __align__(16) uint16_t Qs[kStages][kBlk * D];
-    __shared__ __align__(16) uint16_t Gs[kStages][kBlk * D];   // dO rows
-    __shared__ __align__(16) uint8_t Ts[kStages][kQTile];
+    __shared__ __align__(16) uint16_t Qs[kKvStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Gs[kKvStages][kBlk * D];   // dO rows
+    __shared__ __align__(16) uint8_t Ts[kKvStages][kQTile];
+    __shared__ __align__(16) uint8_t Kt[kRows / kBlk][kKTile];    // key tiles of the owned keys
     __shared__ uint32_t qrecs[kRecCache];
-    __shared__ uint16_t kmeta[NW][kMaxEarlier][16];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int g = lane / 16, c = lane % 16;
@@ -590,15 +626,41 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int r = W.r, bh = W.bh, k0 = W.s0;
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
+    const uint8_t *qtb = qtile + ((size_t)bh * nh + r) * (L / kBlk) * kQTile;
+
+    // Prologue, two dependent memory round trips: (1) the sorted records of
+    // the streamed range and the key tiles of the owned keys; (2) the query
+    // blocks (straight into LDS) together with this lane's key and value rows.
+    if (wave < kRows / kBlk)
+        dma16(ktile + (((size_t)bh * nh + r) * (L / kBlk) + k0 / kBlk + wave) * kKTile + 16 * lane, Kt[wave]);
+    const int cache_n = min(L - k0, kRecCache);
+    for (int i = tid; i < cache_n; i += kKvThreads)
+        qrecs[i] = sr[k0 + i];
+    wait_vm<0>();
+    lds_barrier();
 
     const int wk0 = k0 + wave * 16;
     const int sk = wk0 + c;                       // this lane's key (sorted)
-    const int kpos = (int)rec_lo(sr[sk]);
-    const float rn = rnorm[tok0 + kpos];
+    const int kpos = (int)rec_lo(qrecs[sk - k0]);
+    const uint8_t *kt = Kt[wave / 2];             // this wave's 16 keys are entries 16 (wave % 2) + c
+    const int ke = 16 * (wave % 2) + c;
+    const float rn = reinterpret_cast<const float *>(kt)[ke];
     const float krn2 = rn * scale * kLog2e;
-    if (g == 0)
-        for (int rr = 0; rr < r; ++rr)
-            kmeta[wave][rr][c] = (uint16_t)rec_lo(meta[(tok0 + kpos) * nh + rr]);
+    // query blocks [k0 + 32 b, +32) whose first query's window reaches the owned keys
+    // (window starts do not decrease along the sorted order)
+    const int k_last = k0 + kRows - 1;
+    const int nblocks = __builtin_popcountll(__ballot(kBlk * lane < cache_n &&
+                                                      k0 + kBlk * lane - (int)rec_hi(qrecs[min(kBlk * lane, cache_n - 1)]) <= k_last));
+
+    auto issue = [&](int b, int st) __attribute__((always_inline)) {
+        const int qb = k0 + b * kBlk;
+        dma_rows512<D>(q, dout, Qs[st], Gs[st], qrecs, b * kBlk, tok0, tid, wave);
+        if (wave < 2)
+            dma16(qtb + (size_t)(qb / kBlk) * kQTile + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
+    };
+    for (int i = 0; i < kKvStages && i < nblocks; ++i)
+        issue(i, i);
+
     bf16x8_t kop[D / 32], vop[D / 32];
     {
         const bf16 *krow = q + (tok0 + kpos) * D, *vrow = v + (tok0 + kpos) * D;
@@ -608,165 +670,414 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             vop[ks] = as_bf16x8(ld16(vrow + 32 * ks + 8 * g));
         }
     }
-    const int k_last = k0 + kRows - 1;
-    const int cache_n = min(L - k0, kRecCache);
-    for (int i = tid; i < cache_n; i += kKvThreads)
-        qrecs[i] = sr[k0 + i];
-    __syncthreads();
-    int nblocks;
-    {
-        const int qb = k0 + tid * kBlk;
-        const bool more = qb < L && tid * kBlk < cache_n && qb - (int)rec_hi(qrecs[tid * kBlk]) <= k_last;
-        nblocks = __syncthreads_count(more);
-    }
-    const uint8_t *qtb = qtile + ((size_t)bh * nh + r) * (L / kBlk) * kQTile;
-
-    auto issue = [&](int b) __attribute__((always_inline)) {
-        const int qb = k0 + b * kBlk, st = b % kStages;
-        dma_rows512<D>(q, dout, Qs[st], Gs[st], qrecs, b * kBlk, tok0, tid, wave);
-        if (wave < 2)
-            dma16(qtb + (size_t)(qb / kBlk) * kQTile + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
-    };
 
     f32x4_t dka[D / 16], dva[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
         dka[dt] = dva[dt] = f32x4_t{};
 
-    wait_vm<0>();
-    issue(0);
-    if (nblocks > 1)
-        issue(1);
-    for (int b = 0; b < nblocks; ++b) {
-        if (b + 1 < nblocks) {
-            if (wave < 2)
-                wait_vm<PER + 1>();
-            else
-                wait_vm<PER>();
-        } else {
-            wait_vm<0>();
+    // Blocks are loaded kKvStages at a time (every block of the window at
+    // once when 128 + 2 m <= 32 kKvStages); a wave then works through the
+    // blocks that reach its keys without waiting for the other waves.
+    for (int base = 0; base < nblocks; base += kKvStages) {
+        const int nb = min(kKvStages, nblocks - base);
+        if (base > 0) {
+            block_barrier();                      // the previous group's stages are no longer read
+            for (int i = 0; i < nb; ++i)
+                issue(base + i, i);
         }
+        wait_vm<0>();
         block_barrier();
-        if (b + 2 < nblocks)
-            issue(b + 2);
-        const int qb = k0 + b * kBlk, st = b % kStages;
-        const uint16_t *Qt = Qs[st], *Gt = Gs[st];
-        const float *qlse2 = reinterpret_cast<const float *>(Ts[st]);
-        const float *qD = reinterpret_cast<const float *>(Ts[st] + 128);
-        const uint16_t *qwv = reinterpret_cast<const uint16_t *>(Ts[st] + 256);
-        // this wave's keys [wk0, wk0+15]: queries after a key whose window reaches it
-        const int blk_lo = qb - (int)rec_hi(qrecs[b * kBlk]);
-        if (qb + kBlk - 1 <= wk0 || blk_lo > wk0 + 15)
-            continue;
+        for (int i = 0; i < nb; ++i) {
+            const int b = base + i, qb = k0 + b * kBlk;
+            const uint16_t *Qt = Qs[i], *Gt = Gs[i];
+            const float *qlse2 = reinterpret_cast<const float *>(Ts[i]);
+            const float *qD = reinterpret_cast<const float *>(Ts[i] + 128);
+            const uint16_t *qwv = reinterpret_cast<const uint16_t *>(Ts[i] + 256);
+            // this wave's keys [wk0, wk0+15]: queries after a key whose window reaches it
+            const int blk_lo = qb - (int)rec_hi(qrecs[b * kBlk]);
+            if (qb + kBlk - 1 <= wk0 || blk_lo > wk0 + 15)
+                continue;
 
-        // S = Q K^T, dP = dO V^T for the two 16-query halves (lane = key c;
-        // value t of half u is query 16 u + 4 g + t)
-        f32x4_t sacc[2], pacc[2];
+            // S = Q K^T, dP = dO V^T for the two 16-query halves (lane = key c;
+            // value t of half u is query 16 u + 4 g + t).  All operand reads
+            // are issued before the first product so their latencies overlap.
+            bf16x8_t qa[2][D / 32], ga[2][D / 32];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            sacc[u] = pacc[u] = f32x4_t{};
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                sacc[u] = mfma16(tile_row<D>(Qt, 16 * u + c, 32 * ks + 8 * g), kop[ks], sacc[u]);
-                pacc[u] = mfma16(tile_row<D>(Gt, 16 * u + c, 32 * ks + 8 * g), vop[ks], pacc[u]);
-            }
-        }
-        bool ok[8];
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    qa[u][ks] = tile_row<D>(Qt, 16 * u + c, 32 * ks + 8 * g);
+                    ga[u][ks] = tile_row<D>(Gt, 16 * u + c, 32 * ks + 8 * g);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t sacc[2], pacc[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint2 w4 = *reinterpret_cast<const uint2 *>(qwv + 16 * u + 4 * g);
-            const int wv[4] = {(int)(w4.x & 0xffffu), (int)(w4.x >> 16), (int)(w4.y & 0xffffu), (int)(w4.y >> 16)};
+            for (int u = 0; u < 2; ++u) {
+                sacc[u] = pacc[u] = f32x4_t{};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int sq = qb + 16 * u + 4 * g + t;   // key in [sq - w, sq)
-                ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
-            }
-        }
-        if (r > 0) {
-            uint32_t hit[4] = {0u, 0u, 0u, 0u};
-            for (int rr = 0; rr < r; ++rr) {
-                const uint32_t skp = bcast16(kmeta[wave][rr][c]);
-                const uint16_t *s1 = reinterpret_cast<const uint16_t *>(Ts[st] + 320 + 128 * rr);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
-                    const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
-                    hit[2 * u] |= win_hits2(a.x, ww.x, skp);
-                    hit[2 * u + 1] |= win_hits2(a.y, ww.y, skp);
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    sacc[u] = mfma16(qa[u][ks], kop[ks], sacc[u]);
+                    pacc[u] = mfma16(ga[u][ks], vop[ks], pacc[u]);
                 }
             }
+            bool ok[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
-        }
-        float pr[8], gr[8];
+            for (int u = 0; u < 2; ++u) {
+                const uint2 w4 = *reinterpret_cast<const uint2 *>(qwv + 16 * u + 4 * g);
+                const int wv[4] = {(int)(w4.x & 0xffffu), (int)(w4.x >> 16), (int)(w4.y & 0xffffu), (int)(w4.y >> 16)};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float4 l4 = *reinterpret_cast<const float4 *>(qlse2 + 16 * u + 4 * g);
-            const float4 d4 = *reinterpret_cast<const float4 *>(qD + 16 * u + 4 * g);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int e = 4 * u + t;
-                pr[e] = ok[e] ? fast_exp2(sacc[u][t] * krn2 - lv[t]) : 0.f;
-                gr[e] = pr[e] * (pacc[u][t] - dv[t]) * scale;
+                for (int t = 0; t < 4; ++t) {
+                    const int sq = qb + 16 * u + 4 * g + t;   // key in [sq - w, sq)
+                    ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
+                }
             }
-        }
-        // dV^T += dO^T P, dK^T += Q^T G: B slot s is value s of pr / gr
-        const bf16x8_t pb = pack8(pr), gb = pack8(gr);
+            if (r > 0) {
+                uint32_t hit[4] = {0u, 0u, 0u, 0u};
+                for (int rr = 0; rr < r; ++rr) {
+                    const uint32_t skp = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
+                    const uint16_t *s1 = reinterpret_cast<const uint16_t *>(Ts[i] + 320 + 128 * rr);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            dva[dt] = mfma16(tile_tr16x<D>(Gt, 16 * dt, lane), pb, dva[dt]);
-            dka[dt] = mfma16(tile_tr16x<D>(Qt, 16 * dt, lane), gb, dka[dt]);
+                    for (int u = 0; u < 2; ++u) {
+                        const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
+                        const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                        hit[2 * u] |= win_hits2(a.x, ww.x, skp);
+                        hit[2 * u + 1] |= win_hits2(a.y, ww.y, skp);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+            }
+            float pr[8], gr[8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float4 l4 = *reinterpret_cast<const float4 *>(qlse2 + 16 * u + 4 * g);
+                const float4 d4 = *reinterpret_cast<const float4 *>(qD + 16 * u + 4 * g);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int e = 4 * u + t;
+                    pr[e] = ok[e] ? fast_exp2(sacc[u][t] * krn2 - lv[t]) : 0.f;
+                    gr[e] = pr[e] * (pacc[u][t] - dv[t]) * scale;
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T G: B slot s is value s of pr / gr
+            const bf16x8_t pb = pack8(pr), gb = pack8(gr);
+            bf16x8_t gt[D / 16], qt[D / 16];
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                gt[dt] = tile_tr16x<D>(Gt, 16 * dt, lane);
+                qt[dt] = tile_tr16x<D>(Qt, 16 * dt, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                dva[dt] = mfma16(gt[dt], pb, dva[dt]);
+                dka[dt] = mfma16(qt[dt], gb, dka[dt]);
+            }
         }
     }
 
-    // through the key normalisation k = q rn: (dk - q rn^2 (q . dk)) rn, in fp32
-    // while dk of this round is complete; lane (key c, group g) holds
-    // d = 16 dt + 4 g + t
-    const bf16 *krow = q + (tok0 + kpos) * D;
-    float qv[D / 16][4];
-    float qd = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(krow + 16 * dt + 4 * g);
-        qv[dt][0] = __uint_as_float(u.x << 16);
-        qv[dt][1] = __uint_as_float(u.x & 0xffff0000u);
-        qv[dt][2] = __uint_as_float(u.y << 16);
-        qv[dt][3] = __uint_as_float(u.y & 0xffff0000u);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            qd = fmaf(qv[dt][t], dka[dt][t], qd);
-    }
-    qd += __shfl_xor(qd, 16, kWave);
-    qd += __shfl_xor(qd, 32, kWave);
-    const float proj = rn * rn * qd;
+    // dk of this round times the key's inverse norm; the projection through
+    // the normalisation k = q rn is linear, so it is applied once to the sum
+    // over rounds (reduce_kernel).  Lane (key c, group g) holds d = 16 dt + 4 g + t.
     const size_t row = (((size_t)bh * nh + r) * L + kpos) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
         const int d0 = 16 * dt + 4 * g;
-        float e[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            e[t] = (dka[dt][t] - qv[dt][t] * proj) * rn;
         uint2 w;
-        w.x = pack_bf16x2(e[0], e[1]);
-        w.y = pack_bf16x2(e[2], e[3]);
-        *reinterpret_cast<uint2 *>(dqk_part + row + d0) = w;
+        w.x = pack_bf16x2(dka[dt][0] * rn, dka[dt][1] * rn);
+        w.y = pack_bf16x2(dka[dt][2] * rn, dka[dt][3] * rn);
+        *reinterpret_cast<uint2 *>(dkr_part + row + d0) = w;
         w.x = pack_bf16x2(dva[dt][0], dva[dt][1]);
         w.y = pack_bf16x2(dva[dt][2], dva[dt][3]);
         *reinterpret_cast<uint2 *>(dv_part + row + d0) = w;
     }
 }
 
-// Sum of the per-round partials: dQ = sum_r (dq_r + dqk_r), dV = sum_r dv_r,
+// ---------------------------------------------------------------------------
+// backward, key side, persistent form for chunk lengths that divide 128.
+//
+// A key tile [k0, k0 + 128) is then reached only by queries in [k0, k0 + 256)
+// (a key is seen from its own chunk and the next one), i.e. by query blocks
+// k0/32 + 0..7, and the next tile needs this tile's blocks 4..7 plus four new
+// ones.  A workgroup walks a run of consecutive tiles of one (b, h, round)
+// with those eight blocks resident in LDS stages indexed by absolute block
+// mod 8.  Once the waves are through blocks 0..3 of a tile, the freed stages
+// receive the next tile's new blocks while blocks 4..7 are worked on, so the
+// loads of tile j+1 overlap the work of tile j.  The owned keys' rows come
+// from the resident query blocks (shared QK); their value rows are loaded
+// one tile ahead into registers; per-32-row key tiles and the sorted
+// records arrive by the same direct-to-LDS loads.
+
+constexpr int kStreamStages = 8;
+constexpr int kRecRing = 512;                 // records of sorted rows x at x mod 512
+
+template <int D>
+__device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt, const uint8_t *T, const uint8_t *kt,
+                                          int ke, int r, int qb, int sk, int g, int c, int lane, float krn2,
+                                          float scale, const bf16x8_t (&kop)[D / 32], const bf16x8_t (&vop)[D / 32],
+                                          f32x4_t (&dka)[D / 16], f32x4_t (&dva)[D / 16])
+{
+    const float *qlse2 = reinterpret_cast<const float *>(T);
+    const float *qD = reinterpret_cast<const float *>(T + 128);
+    const uint16_t *qwv = reinterpret_cast<const uint16_t *>(T + 256);
+    bf16x8_t qa[2][D / 32], ga[2][D / 32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            qa[u][ks] = tile_row<D>(Qt, 16 * u + c, 32 * ks + 8 * g);
+            ga[u][ks] = tile_row<D>(Gt, 16 * u + c, 32 * ks + 8 * g);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t sacc[2], pacc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        sacc[u] = pacc[u] = f32x4_t{};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            sacc[u] = mfma16(qa[u][ks], kop[ks], sacc[u]);
+            pacc[u] = mfma16(ga[u][ks], vop[ks], pacc[u]);
+        }
+    }
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint2 w4 = *reinterpret_cast<const uint2 *>(qwv + 16 * u + 4 * g);
+        const int wv[4] = {(int)(w4.x & 0xffffu), (int)(w4.x >> 16), (int)(w4.y & 0xffffu), (int)(w4.y >> 16)};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int sq = qb + 16 * u + 4 * g + t;   // key in [sq - w, sq)
+            ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
+        }
+    }
+    if (r > 0) {
+        uint32_t hit[4] = {0u, 0u, 0u, 0u};
+        for (int rr = 0; rr < r; ++rr) {
+            const uint32_t skp = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
+            const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
+                const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                hit[2 * u] |= win_hits2(a.x, ww.x, skp);
+                hit[2 * u + 1] |= win_hits2(a.y, ww.y, skp);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+    }
+    float pr[8], gr[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float4 l4 = *reinterpret_cast<const float4 *>(qlse2 + 16 * u + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4 *>(qD + 16 * u + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int e = 4 * u + t;
+            pr[e] = ok[e] ? fast_exp2(sacc[u][t] * krn2 - lv[t]) : 0.f;
+            gr[e] = pr[e] * (pacc[u][t] - dv[t]) * scale;
+        }
+    }
+    const bf16x8_t pb = pack8(pr), gb = pack8(gr);
+    bf16x8_t gt[D / 16], qt[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        gt[dt] = tile_tr16x<D>(Gt, 16 * dt, lane);
+        qt[dt] = tile_tr16x<D>(Qt, 16 * dt, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        dva[dt] = mfma16(gt[dt], pb, dva[dt]);
+        dka[dt] = mfma16(qt[dt], gb, dka[dt]);
+    }
+}
+
+// stores dk rn and dv of one key (lane: key c, d = 16 dt + 4 g + t)
+template <int D>
+__device__ __forceinline__ void dkv_store(bf16 *dkr_part, bf16 *dv_part, size_t row, int g, float rn,
+                                          const f32x4_t (&dka)[D / 16], const f32x4_t (&dva)[D / 16])
+{
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int d0 = 16 * dt + 4 * g;
+        uint2 w;
+        w.x = pack_bf16x2(dka[dt][0] * rn, dka[dt][1] * rn);
+        w.y = pack_bf16x2(dka[dt][2] * rn, dka[dt][3] * rn);
+        *reinterpret_cast<uint2 *>(dkr_part + row + d0) = w;
+        w.x = pack_bf16x2(dva[dt][0], dva[dt][1]);
+        w.y = pack_bf16x2(dva[dt][2], dva[dt][3]);
+        *reinterpret_cast<uint2 *>(dv_part + row + d0) = w;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_stream_kernel(
+    int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
+    const uint8_t *__restrict__ qtile, bf16 *__restrict__ dkr_part, bf16 *__restrict__ dv_part)
+{
+    __shared__ __align__(16) uint16_t Qs[kStreamStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Gs[kStreamStages][kBlk * D];   // dO rows
+    __shared__ __align__(16) uint8_t Ts[kStreamStages][kQTile];
+    __shared__ __align__(16) uint8_t Kt[3][kRows / kBlk][kKTile];     // key tiles, two tiles ahead
+    __shared__ __align__(16) uint32_t recs[kRecRing];
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int g = lane / 16, c = lane % 16;
+    // 16-key group of this wave: waves w and w + 4 share a SIMD, and the
+    // early key groups (reached by more query blocks) pair with late ones
+    const int kg = wave < 4 ? wave : 11 - wave;
+    const int nt = L / kRows, nblk = L / kBlk;
+    const int rps = (nt + T - 1) / T;                      // runs per (b, h, round)
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int seg = lb / rps, run = lb % rps;
+    const int r = seg % nh, bh = seg / nh;
+    const int t_begin = run * T, t_end = min(nt, t_begin + T);
+    const uint32_t *sr = srec + (size_t)seg * L;
+    const size_t tok0 = (size_t)bh * L;
+    const size_t part0 = (size_t)seg * L;
+    const uint8_t *qtb = qtile + (size_t)seg * nblk * kQTile;
+    const uint8_t *ktb = ktile + (size_t)seg * nblk * kKTile;
+
+    // absolute query block a: its rows of q and dO, and its query tile
+    auto issue_block = [&](int a) __attribute__((always_inline)) {
+        const int st = a % kStreamStages;
+        dma_rows512<D>(q, dout, Qs[st], Gs[st], recs + (a * kBlk) % kRecRing, 0, tok0, tid, wave);
+        if (wave < 2)
+            dma16(qtb + (size_t)a * kQTile + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
+    };
+    // key tiles of tile t into buffer buf (waves 2..5, one 32-row tile each)
+    auto issue_ktiles = [&](int t, int buf) __attribute__((always_inline)) {
+        if (wave >= 2 && wave < 6)
+            dma16(ktb + ((size_t)t * (kRows / kBlk) + (wave - 2)) * kKTile + 16 * lane, Kt[buf][wave - 2]);
+    };
+    // records of rows [row0, row0 + 128) (row0 a multiple of 128), by wave wv
+    auto issue_recs = [&](int row0, int wv) __attribute__((always_inline)) {
+        if (wave == wv && lane < kRows / 4)
+            dma16(sr + row0 + 4 * lane, recs + row0 % kRecRing);
+    };
+
+    // prologue: records of the first tile's window and the one after, the
+    // key tiles of the first two tiles; then the first tile's eight query
+    // blocks and the value rows of its keys
+    {
+        const int k0 = t_begin * kRows;
+        issue_recs(k0, 6);
+        if (k0 + kRows < L)
+            issue_recs(k0 + kRows, 7);
+        if (k0 + 2 * kRows < L)
+            issue_recs(k0 + 2 * kRows, 6);
+        issue_ktiles(t_begin, 0);
+        if (t_begin + 1 < t_end)
+            issue_ktiles(t_begin + 1, 1);
+        wait_vm<0>();
+        block_barrier();
+        for (int i = 0; i < kStreamStages; ++i)
+            if (k0 / kBlk + i < nblk)
+                issue_block(k0 / kBlk + i);
+    }
+    bf16x8_t vop[D / 32];
+    {
+        const int kpos = (int)rec_lo(recs[(t_begin * kRows + kg * 16 + c) % kRecRing]);
+        const bf16 *vrow = v + (tok0 + kpos) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            vop[ks] = as_bf16x8(ld16(vrow + 32 * ks + 8 * g));
+    }
+    wait_vm<0>();
+    block_barrier();
+
+    f32x4_t dka[D / 16], dva[D / 16];
+    int kpos_prev = 0;
+    float rn_prev = 0.f;
+    for (int t = t_begin; t < t_end; ++t) {
+        const int k0 = t * kRows, a0 = k0 / kBlk, j = t - t_begin;
+        if (t > t_begin)
+            dkv_store<D>(dkr_part, dv_part, (part0 + kpos_prev) * D, g, rn_prev, dka, dva);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            dka[dt] = dva[dt] = f32x4_t{};
+
+        const int sk = k0 + kg * 16 + c;                      // this lane's key (sorted)
+        const int kpos = (int)rec_lo(recs[sk % kRecRing]);
+        const uint8_t *kt = Kt[j % 3][kg / 2];                // entries 16 (kg % 2) + c
+        const int ke = 16 * (kg % 2) + c;
+        const float rn = reinterpret_cast<const float *>(kt)[ke];
+        const float krn2 = rn * scale * kLog2e;
+        bf16x8_t kop[D / 32];
+        {
+            const uint16_t *Kq = Qs[(a0 + kg / 2) % kStreamStages];
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                kop[ks] = tile_row<D>(Kq, ke, 32 * ks + 8 * g);
+        }
+        // query blocks whose first query's window reaches the tile (window
+        // starts do not decrease along the sorted order)
+        const int x = k0 + kBlk * lane;
+        const int nb = __builtin_popcountll(__ballot(lane < kStreamStages && x < L &&
+                                                     x - (int)rec_hi(recs[min(x, L - 1) % kRecRing]) <= k0 + kRows - 1));
+        const int wk0 = k0 + kg * 16;
+        auto work = [&](int b) __attribute__((always_inline)) {
+            const int qb = k0 + b * kBlk, st = (a0 + b) % kStreamStages;
+            const int blk_lo = qb - (int)rec_hi(recs[qb % kRecRing]);
+            if (qb + kBlk - 1 <= wk0 || blk_lo > wk0 + 15)
+                return;
+            dkv_block<D>(Qs[st], Gs[st], Ts[st], kt, ke, r, qb, sk, g, c, lane, krn2, scale, kop, vop, dka, dva);
+        };
+        for (int b = 0; b < 4 && b < nb; ++b)
+            work(b);
+        // Every wave is through blocks 0..3 of this tile (and the previous
+        // tile); everything issued during the previous tile has landed.
+        wait_vm<0>();
+        block_barrier();
+        bf16x8_t vnext[D / 32];
+        if (t + 1 < t_end) {
+            // value rows of the next tile's keys first, so that waiting for
+            // them does not wait for the block loads issued after them
+            const int kn = (int)rec_lo(recs[(k0 + kRows + kg * 16 + c) % kRecRing]);
+            const bf16 *vrow = v + (tok0 + kn) * D;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                vnext[ks] = as_bf16x8(ld16(vrow + 32 * ks + 8 * g));
+            for (int i = 0; i < 4; ++i)
+                if (a0 + 8 + i < nblk)
+                    issue_block(a0 + 8 + i);
+            if (t + 2 < t_end)
+                issue_ktiles(t + 2, (j + 2) % 3);
+            if (k0 + 3 * kRows < L)
+                issue_recs(k0 + 3 * kRows, 6);
+        }
+        for (int b = 4; b < nb; ++b)
+            work(b);
+        kpos_prev = kpos;
+        rn_prev = rn;
+        if (t + 1 < t_end) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                vop[ks] = vnext[ks];
+        }
+    }
+    dkv_store<D>(dkr_part, dv_part, (part0 + kpos_prev) * D, g, rn_prev, dka, dva);
+}
+
+// Sum of the per-round partials and the key-normalisation backward:
+//   a = sum_r dq_r,  b = sum_r dk_r rn  (rn = 1/|q|),  k = q rn,
+//   dQ = a + b - k (k . b),  dV = sum_r dv_r,
 // plus dO for tokens that attend only to themselves (o = v).  D/8 lanes per
 // token, 8 elements each.
 template <int D>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int ntok, const bf16 *__restrict__ dout,
+__global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int ntok, const bf16 *__restrict__ q,
+                                                          const float *__restrict__ rnorm,
+                                                          const bf16 *__restrict__ dout,
                                                           const uint32_t *__restrict__ meta,
                                                           const bf16 *__restrict__ dq_part,
-                                                          const bf16 *__restrict__ dqk_part,
+                                                          const bf16 *__restrict__ dkr_part,
                                                           const bf16 *__restrict__ dv_part, bf16 *__restrict__ dq,
                                                           bf16 *__restrict__ dv)
 {
@@ -776,21 +1087,34 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
     if (tok >= ntok)
         return;
     const int bh = tok / L, t = tok % L;
-    float aq[8] = {}, av[8] = {};
+    float aq[8] = {}, ak[8] = {}, av[8] = {};
     bool alone = true;
     for (int r = 0; r < nh; ++r) {
         alone = alone && rec_hi(meta[(size_t)tok * nh + r]) == 0u;
         const size_t off = (((size_t)bh * nh + r) * L + t) * D + ch * 8;
         float x[8], y[8], z[8];
         load8(dq_part + off, x);
-        load8(dqk_part + off, y);
+        load8(dkr_part + off, y);
         load8(dv_part + off, z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            aq[k] += x[k] + y[k];
+            aq[k] += x[k];
+            ak[k] += y[k];
             av[k] += z[k];
         }
     }
+    float qv[8];
+    load8(q + (size_t)tok * D + ch * 8, qv);
+    float qb = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        qb = fmaf(qv[k], ak[k], qb);
+    qb = group_sum(qb, CPT);
+    const float rn = rnorm[tok];
+    const float proj = rn * rn * qb;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        aq[k] += ak[k] - qv[k] * proj;
     if (alone) {
         float x[8];
         load8(dout + (size_t)tok * D + ch * 8, x);
@@ -802,13 +1126,28 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
     store8(dv + (size_t)tok * D + ch * 8, av);
 }
 
+// Tiles per run of the persistent kernels: about one run per CU in total
+// (a workgroup of these kernels fills a CU), runs within one (b, h, round).
+int stream_run_tiles(int nt, int segs)
+{
+    constexpr int kCUs = 256;
+    const long total = (long)nt * segs;
+    int T = (int)((total + kCUs - 1) / kCUs);
+    return T < 1 ? 1 : (T > nt ? nt : T);
+}
+
+// Rows before a workgroup's first row that its first row's window can reach:
+// a window lies in the query's chunk and the one before, so it is shorter
+// than 2 m; rounded up to whole blocks.
+int max_window(const Dims &P) { return (2 * P.m + kBlk - 1) / kBlk * kBlk; }
+
 template <int D>
 hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
                   const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     ProfScope prof(LSH_KERNEL_FWD, st);
     hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
-                       P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile, (bf16 *)o_rounds,
+                       max_window(P), P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile, (bf16 *)o_rounds,
                        lse_rounds);
     return hipGetLastError();
 }
@@ -819,11 +1158,11 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
                   const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
 {
     const size_t n = (size_t)P.BH() * P.nh * P.L * D;
-    bf16 *dq_part = (bf16 *)part, *dqk_part = dq_part + n, *dv_part = dqk_part + n;
+    bf16 *dq_part = (bf16 *)part, *dkr_part = dq_part + n, *dv_part = dkr_part + n;
     const dim3 grid((P.L / kRows) * P.nh * P.BH());
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
-        hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
+        hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, max_window(P), P.scale, (const bf16 *)q,
                            (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile, dq_part);
     }
     hipError_t e = hipGetLastError();
@@ -831,8 +1170,17 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
         return e;
     {
         ProfScope prof(LSH_KERNEL_BWD_DKV, st);
-        hipLaunchKernelGGL((dkv_kernel<D>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
-                           (const bf16 *)v, (const bf16 *)dout, meta, srec, rnorm, qtile, dqk_part, dv_part);
+        if (kRows % P.m == 0) {
+            const int nt = P.L / kRows, segs = P.BH() * P.nh;
+            const int T = stream_run_tiles(nt, segs);
+            const int runs = segs * ((nt + T - 1) / T);
+            hipLaunchKernelGGL((dkv_stream_kernel<D>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,
+                               (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part,
+                               dv_part);
+        } else {
+            hipLaunchKernelGGL((dkv_kernel<D>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
+                               (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part, dv_part);
+        }
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
@@ -840,7 +1188,8 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     constexpr int TPB = kThreads / (D / 8);
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
     hipLaunchKernelGGL((reduce_kernel<D>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok,
-                       (const bf16 *)dout, meta, dq_part, dqk_part, dv_part, (bf16 *)dq, (bf16 *)dv);
+                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, dq_part, dkr_part, dv_part, (bf16 *)dq,
+                       (bf16 *)dv);
     return hipGetLastError();
 }
 

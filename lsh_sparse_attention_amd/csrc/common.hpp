@@ -270,7 +270,7 @@ __device__ __forceinline__ int xcd_block(int i, int n)
 bool mfma_path_ok(const Dims &, int dtype);
 size_t mfma_ktile_bytes(const Dims &);
 size_t mfma_qtile_bytes(const Dims &);
-// bf16 per-round partials dq, dqk (key side, already through the key
+// bf16 per-round partials dq (query side), dk rn (key side, before the key
 // normalisation) and dv, each [B][H][nh][L][d], in one buffer of this size
 size_t bwd_mfma_part_bytes(const Dims &);
 hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const int32_t *inv,

@@ -35,6 +35,9 @@ SMALL = [
     ("many-buckets", 1, 1, 4096, 64, 4096, 2, 128, "bf16", False),
     ("tiny-L", 1, 1, 8, 32, 4, 2, 2, "f32", False),
     ("single-token", 1, 1, 1, 32, 2, 1, 1, "f32", False),
+    ("bf16-m96", 1, 2, 1536, 64, 32, 3, 96, "bf16", False),
+    ("bf16-m256", 1, 1, 2048, 128, 16, 2, 256, "bf16", False),
+    ("bf16-runs", 1, 4, 8192, 64, 128, 2, 128, "bf16", False),
 ]
 
 
