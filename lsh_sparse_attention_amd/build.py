@@ -26,6 +26,11 @@ HIPCC_FLAGS = [
 ]
 
 
+# per-source extra flags: the hash keeps its matrix-core accumulators in
+# ordinary VGPRs (the argmax reads every accumulator element)
+EXTRA_FLAGS = {"hash.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -36,8 +41,8 @@ def _hipcc() -> str:
 
 def compile_commands(objdir: str) -> list[list[str]]:
     flags = [f for f in HIPCC_FLAGS if f != "-shared"]
-    return [[_hipcc(), *flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o",
-             os.path.join(objdir, os.path.basename(src) + ".o")] for src in sources()]
+    return [[_hipcc(), *flags, *EXTRA_FLAGS.get(os.path.basename(src), []), f"-I{INCLUDE}", f"-I{CSRC}", "-c", src,
+             "-o", os.path.join(objdir, os.path.basename(src) + ".o")] for src in sources()]
 
 
 def _run(cmd: list[str]) -> tuple[int, str]:

@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 bm = fmaxf(bm, x[4 * g + t]);
             }
         }
-        bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+        bm = max_xor32(bm);
         const bool raise = bm > mrun + kLazy;
         const float mnew = raise ? bm : mrun;
         const float mref = (mnew == -INFINITY) ? 0.f : mnew;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             x[e] = fast_exp2(x[e] - mref);
             ps += x[e];
         }
-        ps += __shfl_xor(ps, 32, kWave);
+        ps = sum_xor32(ps);
         if (__ballot(raise) != 0ull) {
             const float corr = raise ? fast_exp2(mrun - mref) : 1.f;
             lrun *= corr;
@@ -1066,6 +1066,280 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     dkv_store<D>(dkr_part, dv_part, (part0 + kpos_prev) * D, g, rn_prev, dka, dva);
 }
 
+// ---------------------------------------------------------------------------
+// query-owned kernels (forward, and dq of the backward), persistent form for
+// chunk lengths that divide 128.
+//
+// A query tile [s0, s0 + 128) then reaches keys in [s0 - 128, s0 + 128) (a
+// window lies in the query's chunk and the one before), i.e. key blocks
+// s0/32 - 4 .. s0/32 + 3, and the next tile needs this tile's last four
+// blocks plus four new ones.  Eight waves own 16 queries each
+// (v_mfma_f32_16x16x32_bf16).  Stages hold the key (= query) rows, value rows
+// and key tiles of a block, indexed by absolute block mod 8.  Per tile: the
+// four earlier blocks first; then their stages take the next tile's new
+// blocks (and the next tile's query rows are loaded into registers) while
+// the tile's own four blocks are worked on.
+
+template <int D, bool BWD>
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(
+    int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dvec,
+    const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
+    bf16 *__restrict__ out, float *__restrict__ lse_rounds)
+{
+    __shared__ __align__(16) uint16_t Ks[kStreamStages][kBlk * D];
+    __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
+    __shared__ __align__(16) uint8_t Kts[kStreamStages][kKTile];
+    __shared__ __align__(16) uint32_t recs[kRecRing];
+    __shared__ uint32_t qm[kKvThreads / kWave][kMaxEarlier][16];   // earlier-round records of the queries
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int g = lane / 16, c = lane % 16;
+    // 16-query group of this wave: waves w and w + 4 share a SIMD, and the
+    // late query groups (which see more of the tile's own keys) pair with
+    // early ones
+    const int qg = wave < 4 ? wave : 11 - wave;
+    const int nt = L / kRows, nblk = L / kBlk;
+    const int rps = (nt + T - 1) / T;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int seg = lb / rps, run = lb % rps;
+    const int r = seg % nh, bh = seg / nh;
+    const int t_begin = run * T, t_end = min(nt, t_begin + T);
+    const uint32_t *sr = srec + (size_t)seg * L;
+    const size_t tok0 = (size_t)bh * L;
+    const size_t part0 = (size_t)seg * L;
+    const uint8_t *ktb = ktile + (size_t)seg * nblk * kKTile;
+    const float scale_log2 = scale * kLog2e;
+
+    auto issue_block = [&](int a) __attribute__((always_inline)) {
+        const int st = a % kStreamStages;
+        dma_rows512<D>(q, v, Ks[st], Vs[st], recs + (a * kBlk) % kRecRing, 0, tok0, tid, wave);
+        if (wave == 0)
+            dma16(ktb + (size_t)a * kKTile + 16 * lane, Kts[st]);
+    };
+    auto issue_recs = [&](int row0, int wv) __attribute__((always_inline)) {
+        if (wave == wv && lane < kRows / 4)
+            dma16(sr + row0 + 4 * lane, recs + row0 % kRecRing);
+    };
+
+    // this lane's query of tile t (16 per wave) in registers
+    struct QRegs {
+        bf16x8_t qop[D / 32], gop[D / 32];
+        uint32_t qm[kMaxEarlier];
+        int qpos, qw;
+        float lse2, Di;
+    };
+    auto load_q = [&](int t, QRegs &R) __attribute__((always_inline)) {
+        const int sq = t * kRows + qg * 16 + c;
+        const uint32_t rec = recs[sq % kRecRing];
+        R.qpos = (int)rec_lo(rec);
+        R.qw = (int)rec_hi(rec);
+        const size_t tok = tok0 + R.qpos;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            R.qop[ks] = as_bf16x8(ld16(q + tok * D + 32 * ks + 8 * g));
+        if constexpr (BWD) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                R.gop[ks] = as_bf16x8(ld16(dout + tok * D + 32 * ks + 8 * g));
+            R.lse2 = lse[tok] * kLog2e;
+            R.Di = Dvec[tok];
+        }
+#pragma unroll
+        for (int rr = 0; rr < kMaxEarlier; ++rr)
+            if (rr < r)
+                R.qm[rr] = meta[tok * nh + rr];
+    };
+
+    // prologue: records [s0 - 128, s0 + 256), then the first tile's eight blocks and query rows
+    {
+        const int s0 = t_begin * kRows;
+        if (s0 >= kRows)
+            issue_recs(s0 - kRows, 5);
+        issue_recs(s0, 6);
+        if (s0 + kRows < L)
+            issue_recs(s0 + kRows, 7);
+        wait_vm<0>();
+        block_barrier();
+        for (int a = s0 / kBlk - 4; a < s0 / kBlk + 4; ++a)
+            if (a >= 0 && a < nblk)
+                issue_block(a);
+    }
+    QRegs cur;
+    load_q(t_begin, cur);
+
+    constexpr int NA = BWD ? D / 16 : D / 16;
+    f32x4_t acc[NA];
+    float mrun = -INFINITY, lrun = 0.f;
+    int qpos_prev = 0;
+    auto finish = [&](int qpos) __attribute__((always_inline)) {
+        const size_t row = (part0 + qpos) * D;
+        float sc = 1.f;
+        if constexpr (!BWD)
+            sc = lrun > 0.f ? 1.f / lrun : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[dt][0] * sc, acc[dt][1] * sc);
+            w.y = pack_bf16x2(acc[dt][2] * sc, acc[dt][3] * sc);
+            *reinterpret_cast<uint2 *>(out + row + 16 * dt + 4 * g) = w;
+        }
+        if constexpr (!BWD)
+            if (g == 0)
+                lse_rounds[part0 + qpos] = lrun > 0.f ? (mrun + __log2f(lrun)) * 0.69314718055994531f : -INFINITY;
+    };
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int s0 = t * kRows, a0 = s0 / kBlk;
+        // everything issued during the previous tile has landed
+        wait_vm<0>();
+        if (t > t_begin)
+            finish(qpos_prev);
+        if (g == 0) {
+#pragma unroll
+            for (int rr = 0; rr < kMaxEarlier; ++rr)
+                if (rr < r)
+                    qm[wave][rr][c] = cur.qm[rr];
+        }
+        block_barrier();
+#pragma unroll
+        for (int dt = 0; dt < NA; ++dt)
+            acc[dt] = f32x4_t{};
+        mrun = -INFINITY;
+        lrun = 0.f;
+
+        const int wq0 = s0 + qg * 16;
+        const int sq = wq0 + c;
+        const int qlo = sq - cur.qw;
+        const int wlo = __builtin_amdgcn_readlane(qlo, 0);   // window starts do not decrease
+
+        auto work = [&](int a) __attribute__((always_inline)) {
+            const int kb = a * kBlk, st = a % kStreamStages;
+            if (kb > wq0 + 14 || kb + kBlk - 1 < wlo)
+                return;
+            const uint16_t *K = Ks[st], *V = Vs[st];
+            const float *rnk = reinterpret_cast<const float *>(Kts[st]);
+            const uint16_t *skm = reinterpret_cast<const uint16_t *>(Kts[st] + 128);
+            // S^T = K Q^T (and dP^T = V dO^T): lane (query c, group g) gets keys 16 kk + 4 g + t
+            bf16x8_t ka[2][D / 32], va[2][D / 32];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    ka[kk][ks] = tile_row<D>(K, 16 * kk + c, 32 * ks + 8 * g);
+                    if constexpr (BWD)
+                        va[kk][ks] = tile_row<D>(V, 16 * kk + c, 32 * ks + 8 * g);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t sacc[2], pacc[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                sacc[kk] = f32x4_t{};
+                pacc[kk] = f32x4_t{};
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks) {
+                    sacc[kk] = mfma16(ka[kk][ks], cur.qop[ks], sacc[kk]);
+                    if constexpr (BWD)
+                        pacc[kk] = mfma16(va[kk][ks], cur.gop[ks], pacc[kk]);
+                }
+            }
+            bool ok[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ok[e] = (unsigned)(kb + 16 * (e / 4) + 4 * g + (e % 4) - qlo) < (unsigned)cur.qw;
+            if (r > 0) {
+                uint32_t hit[4] = {0u, 0u, 0u, 0u};
+                for (int rr = 0; rr < r; ++rr) {
+                    const uint32_t qmr = qm[wave][rr][c];
+                    const uint32_t si1p = bcast16(rec_lo(qmr) - 1u), wp = bcast16(rec_hi(qmr));
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const uint2 kp = *reinterpret_cast<const uint2 *>(skm + 32 * rr + 16 * kk + 4 * g);
+                        hit[2 * kk] |= win_hits2(si1p, wp, kp.x);
+                        hit[2 * kk + 1] |= win_hits2(si1p, wp, kp.y);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+            }
+            float x[8];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float4 rn4 = *reinterpret_cast<const float4 *>(rnk + 16 * kk + 4 * g);
+                const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int e = 4 * kk + tt;
+                    if constexpr (BWD) {
+                        const float pr = ok[e] ? fast_exp2(sacc[kk][tt] * rn[tt] * scale_log2 - cur.lse2) : 0.f;
+                        x[e] = pr * (pacc[kk][tt] - cur.Di) * (scale * rn[tt]);
+                    } else {
+                        x[e] = ok[e] ? sacc[kk][tt] * (rn[tt] * scale_log2) : -INFINITY;
+                    }
+                }
+            }
+            if constexpr (!BWD) {
+                float bm = x[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e)
+                    bm = fmaxf(bm, x[e]);
+                bm = max_xor32(max_xor16(bm));
+                const bool raise = bm > mrun + kLazy;
+                const float mnew = raise ? bm : mrun;
+                const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+                float ps = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x[e] = fast_exp2(x[e] - mref);
+                    ps += x[e];
+                }
+                ps = sum_xor32(sum_xor16(ps));
+                if (__ballot(raise) != 0ull) {
+                    const float corr = raise ? fast_exp2(mrun - mref) : 1.f;
+                    lrun *= corr;
+#pragma unroll
+                    for (int dt = 0; dt < NA; ++dt)
+                        acc[dt] *= corr;
+                }
+                lrun += ps;
+                mrun = mnew;
+            }
+            // O^T += V^T P^T, or dQ^T += K^T G^T: B slot s is value s of x
+            const bf16x8_t xb = pack8(x);
+            bf16x8_t tr[D / 16];
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                tr[dt] = tile_tr16x<D>(BWD ? K : V, 16 * dt, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                acc[dt] = mfma16(tr[dt], xb, acc[dt]);
+        };
+
+        for (int a = a0 - 4; a < a0; ++a)
+            if (a >= 0)
+                work(a);
+        // the earlier blocks are through: their stages take the next tile's new blocks
+        block_barrier();
+        QRegs nxt;
+        if (t + 1 < t_end) {
+            load_q(t + 1, nxt);
+            for (int a = a0 + 4; a < a0 + 8; ++a)
+                if (a < nblk)
+                    issue_block(a);
+            if (s0 + 2 * kRows < L)
+                issue_recs(s0 + 2 * kRows, 6);
+        }
+        for (int a = a0; a < a0 + 4; ++a)
+            work(a);
+        qpos_prev = cur.qpos;
+        if (t + 1 < t_end)
+            cur = nxt;
+    }
+    finish(qpos_prev);
+}
+
 // Sum of the per-round partials and the key-normalisation backward:
 //   a = sum_r dq_r,  b = sum_r dk_r rn  (rn = 1/|q|),  k = q rn,
 //   dQ = a + b - k (k . b),  dV = sum_r dv_r,
@@ -1146,9 +1420,18 @@ hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *m
                   const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     ProfScope prof(LSH_KERNEL_FWD, st);
-    hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
-                       max_window(P), P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile, (bf16 *)o_rounds,
-                       lse_rounds);
+    if (kRows % P.m == 0) {
+        const int nt = P.L / kRows, segs = P.BH() * P.nh;
+        const int T = stream_run_tiles(nt, segs);
+        hipLaunchKernelGGL((q_stream_kernel<D, false>), dim3(segs * ((nt + T - 1) / T)), dim3(kKvThreads), 0, st, P.L,
+                           P.nh, T, P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)nullptr,
+                           (const float *)nullptr, (const float *)nullptr, meta, srec, ktile, (bf16 *)o_rounds,
+                           lse_rounds);
+    } else {
+        hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
+                           max_window(P), P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile,
+                           (bf16 *)o_rounds, lse_rounds);
+    }
     return hipGetLastError();
 }
 
@@ -1162,8 +1445,17 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     const dim3 grid((P.L / kRows) * P.nh * P.BH());
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
-        hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, max_window(P), P.scale, (const bf16 *)q,
-                           (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile, dq_part);
+        if (kRows % P.m == 0) {
+            const int nt = P.L / kRows, segs = P.BH() * P.nh;
+            const int T = stream_run_tiles(nt, segs);
+            hipLaunchKernelGGL((q_stream_kernel<D, true>), dim3(segs * ((nt + T - 1) / T)), dim3(kKvThreads), 0, st,
+                               P.L, P.nh, T, P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv,
+                               meta, srec, ktile, dq_part, (float *)nullptr);
+        } else {
+            hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, max_window(P), P.scale,
+                               (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile,
+                               dq_part);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

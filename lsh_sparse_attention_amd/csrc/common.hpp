@@ -256,6 +256,29 @@ __device__ __forceinline__ uint32_t win_hits2(uint32_t si1p, uint32_t wp, uint32
     const u16x2_t z = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, wp), x);
     return __builtin_bit_cast(uint32_t, z);
 }
+// Exchange across lanes l and l ^ 16 (l ^ 32) with v_permlane16_swap_b32
+// (v_permlane32_swap_b32): swapping a value with itself leaves the row pair's
+// two values in the two results, in the same order on both lanes.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 __device__ __forceinline__ uint32_t bcast16(uint32_t x) { return (x & 0xffffu) * 0x10001u; }
 
 // Workgroup index remapped so that consecutive logical blocks run on the same

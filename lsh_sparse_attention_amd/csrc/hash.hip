@@ -102,8 +102,12 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
         const int row = min(row0 + 32 * ct + c, L - 1);
         const bf16 *qrow = q + ((size_t)bh * L + row) * D;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            qop[ct][ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h));
+        for (int ks = 0; ks < D / 16; ++ks) {
+            // -q: the products then give y' = -y exactly (a sign flip is exact
+            // in bf16 and round-to-nearest is symmetric)
+            const u32x4_t u = ld16(qrow + 16 * ks + 8 * h) ^ 0x80008000u;
+            qop[ct][ks] = as_bf16x8(u);
+        }
     }
     const uint16_t *Rbits = reinterpret_cast<const uint16_t *>(rot);
     // staging: item i = (row d = i / 8, columns 8 (i % 8) .. +7 of the block)
@@ -133,9 +137,14 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
         }
     };
 
-    // running max of +y (bp, ip) and running min of y (mn, in): -y > -mn <=> y < mn
-    float bp[2] = {-INFINITY, -INFINITY}, mn[2] = {INFINITY, INFINITY};
-    int ip[2] = {0, 0}, in[2] = {0, 0};
+    // Argmax over [y ; -y] with first-index ties, one tracker per lane and
+    // parity of the slot: the key rotl(bits(y'), 1) with y' = -y orders by |y|
+    // (bits of |y| on top) and, for equal |y|, puts y > 0 (sign bit of y'
+    // set) above y < 0, i.e. the +y half (lower indices) above the -y half;
+    // a strictly greater key replaces the tracked one, so the first column
+    // wins among equal keys.  Key 0 is y = 0 (never -0: the sums start at +0).
+    uint32_t bk[2][2] = {{0u, 0u}, {0u, 0u}};
+    int bi[2][2] = {{0, 0}, {0, 0}};
     fetch(0);
     for (int blk = 0; blk < nh * nblk; ++blk) {
         const int r = blk / nblk, jb = (blk % nblk) * kHashCols;
@@ -163,37 +172,47 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
                 const uint2 y = lds_read_tr16(&Rs[(dr + 4) * P + col]);
                 aop[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x.x, x.y, y.x, y.y});
             }
+            f32x16_t acc[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                acc[ct] = f32x16_t{};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    acc[ct] = mfma32(aop[ks], qop[ct][ks], acc[ct]);
+            }
+            // acc[4 g + t] = y'[column j0 + 8 g + 4 h + t] of row c.  Within the
+            // tile each parity tracker keeps (key, slot offset 8 g + t), the
+            // offsets being immediates; the tile result then merges into the
+            // round's tracker (strictly greater key: an earlier tile wins ties).
             const bool full = j0 + 32 <= half;
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                f32x16_t acc = f32x16_t{};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
-                    acc = mfma32(aop[ks], qop[ct][ks], acc);
-                // acc[4 g + t] = y[column j0 + 8 g + 4 h + t] of row c; the
-                // uniform part j0 + 8 g + t is selected, 4 h added at the end
+                uint32_t tk[2] = {0u, 0u};
+                int ts[2] = {0, 0};
                 if (full) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int ju = j0 + 8 * (e / 4) + (e % 4);
-                        const float yv = acc[e];
-                        const bool gp = yv > bp[ct], gn = yv < mn[ct];
-                        ip[ct] = gp ? ju : ip[ct];
-                        bp[ct] = gp ? yv : bp[ct];
-                        in[ct] = gn ? ju : in[ct];
-                        mn[ct] = gn ? yv : mn[ct];
+                        const uint32_t u = __float_as_uint(acc[ct][e]);
+                        const uint32_t key = __builtin_amdgcn_alignbit(u, u, 31);
+                        const int p = e % 2;
+                        ts[p] = key > tk[p] ? 8 * (e / 4) + (e % 4) : ts[p];
+                        tk[p] = max(tk[p], key);
                     }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int ju = j0 + 8 * (e / 4) + (e % 4);
-                        const float yv = (ju + 4 * h < half) ? acc[e] : NAN;   // NaN never wins
-                        const bool gp = yv > bp[ct], gn = yv < mn[ct];
-                        ip[ct] = gp ? ju : ip[ct];
-                        bp[ct] = gp ? yv : bp[ct];
-                        in[ct] = gn ? ju : in[ct];
-                        mn[ct] = gn ? yv : mn[ct];
+                        const uint32_t u = __float_as_uint(acc[ct][e]);
+                        const int off = 8 * (e / 4) + (e % 4);
+                        const uint32_t key = (j0 + off + 4 * h < half) ? __builtin_amdgcn_alignbit(u, u, 31) : 0u;
+                        const int p = e % 2;
+                        ts[p] = key > tk[p] ? off : ts[p];
+                        tk[p] = max(tk[p], key);
                     }
+                }
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    bi[ct][p] = tk[p] > bk[ct][p] ? j0 + ts[p] : bi[ct][p];
+                    bk[ct][p] = max(bk[ct][p], tk[p]);
                 }
             }
         }
@@ -201,29 +220,32 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
             // last block of round r
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                ip[ct] += 4 * h;
-                in[ct] += 4 * h;
-                // merge with the other half of the row (first index on ties)
-                const float obp = __shfl_xor(bp[ct], 32, kWave), omn = __shfl_xor(mn[ct], 32, kWave);
-                const int oip = __shfl_xor(ip[ct], 32, kWave), oin = __shfl_xor(in[ct], 32, kWave);
-                if (obp > bp[ct] || (obp == bp[ct] && oip < ip[ct])) {
-                    bp[ct] = obp;
-                    ip[ct] = oip;
+                // the two slot parities, then the other half of the row:
+                // larger key, else smaller column
+                uint32_t k0 = bk[ct][0], k1 = bk[ct][1];
+                int i0 = bi[ct][0] + 4 * h, i1 = bi[ct][1] + 4 * h;
+                if (k1 > k0 || (k1 == k0 && i1 < i0)) {
+                    k0 = k1;
+                    i0 = i1;
                 }
-                if (omn < mn[ct] || (omn == mn[ct] && oin < in[ct])) {
-                    mn[ct] = omn;
-                    in[ct] = oin;
+                const auto pk = __builtin_amdgcn_permlane32_swap(k0, k0, false, false);
+                const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i0, (uint32_t)i0, false, false);
+                const uint32_t ok = h ? pk[0] : pk[1];
+                const int oi = (int)(h ? pi[0] : pi[1]);
+                if (ok > k0 || (ok == k0 && oi < i0)) {
+                    k0 = ok;
+                    i0 = oi;
                 }
                 const int row = row0 + 32 * ct + c;
-                // first index of the maximum over [+y ; -y]: the +y half wins ties
+                // key 0: every projection is zero and bucket 0 (a +y entry) is the first maximum
                 if (h == 0 && row < L)
-                    buckets[((size_t)bh * nh + r) * L + row] = (bp[ct] >= -mn[ct]) ? ip[ct] : half + in[ct];
-                bp[ct] = -INFINITY;
-                mn[ct] = INFINITY;
-                ip[ct] = in[ct] = 0;
+                    buckets[((size_t)bh * nh + r) * L + row] = k0 == 0u ? 0 : ((k0 & 1u) ? i0 : half + i0);
+                bk[ct][0] = bk[ct][1] = 0u;
+                bi[ct][0] = bi[ct][1] = 0;
             }
         }
     }
+
 }
 
 template <int D>
