@@ -185,38 +185,51 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
 // ---------------------------------------------------------------------------
 // combine: one wave per token
 
-template <typename T, int D>
+template <typename T, int D, int NH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int L, int nh, int ntok, float scale,
                                                            const T *__restrict__ q, const T *__restrict__ v,
                                                            const T *__restrict__ o_rounds,
                                                            const float *__restrict__ lse_rounds,
                                                            T *__restrict__ out, float *__restrict__ lse)
 {
-    // D/8 lanes per token, each on 8 consecutive elements
+    // D/8 lanes per token, each on 8 consecutive elements; the nh <= NH round
+    // rows are all requested before any is used
     constexpr int CPT = D / 8, TPB = kThreads / CPT;
     const int grp = threadIdx.x / CPT, ch = threadIdx.x % CPT;
     const int tok = blockIdx.x * TPB + grp;
     const bool valid = tok < ntok;
     const int tk = valid ? tok : 0;
     const int bh = tk / L, t = tk % L;
+    float ls[NH], x[NH][8];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        if (r < nh) {
+            const size_t orow = ((size_t)bh * nh + r) * L + t;
+            ls[r] = lse_rounds[orow];
+            load8(o_rounds + orow * D + ch * 8, x[r]);
+        } else {
+            ls[r] = -INFINITY;
+        }
+    }
     float M = -INFINITY;
-    for (int r = 0; r < nh; ++r)
-        M = fmaxf(M, lse_rounds[((size_t)bh * nh + r) * L + t]);
+#pragma unroll
+    for (int r = 0; r < NH; ++r)
+        M = fmaxf(M, ls[r]);
     const bool alone = valid && M == -INFINITY;
     if (__ballot(alone) != 0ull) {
         // no member in any round: the token attends only to itself
-        float x[8];
+        float y[8];
         float ss = 0.f;
         if (alone) {
-            load8(q + (size_t)tk * D + ch * 8, x);
+            load8(q + (size_t)tk * D + ch * 8, y);
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                ss = fmaf(x[k], x[k], ss);
+                ss = fmaf(y[k], y[k], ss);
         }
         ss = group_sum(ss, CPT);
         if (alone) {
-            load8(v + (size_t)tk * D + ch * 8, x);
-            store8(out + (size_t)tk * D + ch * 8, x);
+            load8(v + (size_t)tk * D + ch * 8, y);
+            store8(out + (size_t)tk * D + ch * 8, y);
             if (ch == 0)
                 lse[tk] = scale * sqrtf(ss);
         }
@@ -224,20 +237,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int L, int nh, int nt
     if (!valid || alone)
         return;
     float den = 0.f;
-    for (int r = 0; r < nh; ++r)
-        den += expf(lse_rounds[((size_t)bh * nh + r) * L + t] - M);
+#pragma unroll
+    for (int r = 0; r < NH; ++r)
+        den += expf(ls[r] - M);          // exp(-inf) = 0 for empty rounds and r >= nh
     const float total = M + logf(den);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < nh; ++r) {
-        const size_t orow = ((size_t)bh * nh + r) * L + t;
-        const float wgt = expf(lse_rounds[orow] - total);
-        if (wgt == 0.f)
-            continue;
-        float x[8];
-        load8(o_rounds + orow * D + ch * 8, x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            acc[k] = fmaf(wgt, x[k], acc[k]);
+    for (int r = 0; r < NH; ++r) {
+        const float wgt = expf(ls[r] - total);
+        if (r < nh) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                acc[k] = fmaf(wgt, x[r][k], acc[k]);
+        }
     }
     store8(out + (size_t)tk * D + ch * 8, acc);
     if (ch == 0)
@@ -497,8 +509,18 @@ hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o
     constexpr int TPB = kThreads / (D / 8);
     dim3 grid((ntok + TPB - 1) / TPB);
     ProfScope prof(LSH_KERNEL_COMBINE, st);
-    hipLaunchKernelGGL((combine_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, ntok, P.scale,
-                       (const T *)q, (const T *)v, (const T *)o_rounds, lse_rounds, (T *)out, lse);
+#define LSH_COMBINE(NH)                                                                                           \
+    hipLaunchKernelGGL((combine_kernel<T, D, NH>), grid, dim3(kThreads), 0, st, P.L, P.nh, ntok, P.scale,        \
+                       (const T *)q, (const T *)v, (const T *)o_rounds, lse_rounds, (T *)out, lse)
+    if (P.nh <= 2)
+        LSH_COMBINE(2);
+    else if (P.nh <= 4)
+        LSH_COMBINE(4);
+    else if (P.nh <= 8)
+        LSH_COMBINE(8);
+    else
+        LSH_COMBINE(16);
+#undef LSH_COMBINE
     return hipGetLastError();
 }
 

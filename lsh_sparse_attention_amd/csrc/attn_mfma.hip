@@ -1345,7 +1345,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 //   dQ = a + b - k (k . b),  dV = sum_r dv_r,
 // plus dO for tokens that attend only to themselves (o = v).  D/8 lanes per
 // token, 8 elements each.
-template <int D>
+template <int D, int NH>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int ntok, const bf16 *__restrict__ q,
                                                           const float *__restrict__ rnorm,
                                                           const bf16 *__restrict__ dout,
@@ -1363,22 +1363,35 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
     const int bh = tok / L, t = tok % L;
     float aq[8] = {}, ak[8] = {}, av[8] = {};
     bool alone = true;
-    for (int r = 0; r < nh; ++r) {
-        alone = alone && rec_hi(meta[(size_t)tok * nh + r]) == 0u;
-        const size_t off = (((size_t)bh * nh + r) * L + t) * D + ch * 8;
-        float x[8], y[8], z[8];
-        load8(dq_part + off, x);
-        load8(dkr_part + off, y);
-        load8(dv_part + off, z);
+    // every round's rows requested before any is summed (nh <= NH)
+    u32x4_t xq[NH], xk[NH], xv[NH];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            aq[k] += x[k];
-            ak[k] += y[k];
-            av[k] += z[k];
+    for (int r = 0; r < NH; ++r)
+        if (r < nh) {
+            const size_t off = (((size_t)bh * nh + r) * L + t) * D + ch * 8;
+            xq[r] = ld16(dq_part + off);
+            xk[r] = ld16(dkr_part + off);
+            xv[r] = ld16(dv_part + off);
+            alone = alone && rec_hi(meta[(size_t)tok * nh + r]) == 0u;
         }
-    }
     float qv[8];
     load8(q + (size_t)tok * D + ch * 8, qv);
+#pragma unroll
+    for (int r = 0; r < NH; ++r)
+        if (r < nh) {
+            const uint32_t wq[4] = {xq[r].x, xq[r].y, xq[r].z, xq[r].w};
+            const uint32_t wk[4] = {xk[r].x, xk[r].y, xk[r].z, xk[r].w};
+            const uint32_t wv[4] = {xv[r].x, xv[r].y, xv[r].z, xv[r].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                aq[2 * k] += __uint_as_float(wq[k] << 16);
+                aq[2 * k + 1] += __uint_as_float(wq[k] & 0xffff0000u);
+                ak[2 * k] += __uint_as_float(wk[k] << 16);
+                ak[2 * k + 1] += __uint_as_float(wk[k] & 0xffff0000u);
+                av[2 * k] += __uint_as_float(wv[k] << 16);
+                av[2 * k + 1] += __uint_as_float(wv[k] & 0xffff0000u);
+            }
+        }
     float qb = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
@@ -1479,9 +1492,19 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     const int ntok = P.BH() * P.L;
     constexpr int TPB = kThreads / (D / 8);
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
-    hipLaunchKernelGGL((reduce_kernel<D>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok,
-                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, dq_part, dkr_part, dv_part, (bf16 *)dq,
-                       (bf16 *)dv);
+#define LSH_REDUCE(NH)                                                                                            \
+    hipLaunchKernelGGL((reduce_kernel<D, NH>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok, \
+                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, dq_part, dkr_part, dv_part, (bf16 *)dq,     \
+                       (bf16 *)dv)
+    if (P.nh <= 2)
+        LSH_REDUCE(2);
+    else if (P.nh <= 4)
+        LSH_REDUCE(4);
+    else if (P.nh <= 8)
+        LSH_REDUCE(8);
+    else
+        LSH_REDUCE(16);
+#undef LSH_REDUCE
     return hipGetLastError();
 }
 
