@@ -43,9 +43,10 @@ constexpr int kQStages = 4;     // ring depth of the query-owned kernels (two wo
 constexpr int kKvStages = 8;    // blocks resident at once in the key-owned kernel (one workgroup per CU)
 constexpr int kRecCache = 1024;           // sorted records of a workgroup's streamed range
 constexpr int kMaxEarlier = 13;           // earlier rounds a tile holds (n_hashes <= 14)
-constexpr int kKTile = 1024;              // key tile: rn[32] f32, sk[13][32] u16
+constexpr int kKTile = 1024;              // key tile: rn * scale * log2(e) [32] f32, sk[13][32] u16
 constexpr int kQTile = 2048;              // query tile: lse2[32], D[32] f32, w[32] u16, (si1, w)[13][32] u16
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLazy = 8.0f;             // lazy running-max threshold (log2 units)
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -180,7 +181,7 @@ __device__ __forceinline__ void clear_hits(bool (&ok)[16], const uint32_t (&hit)
 
 // One wave per tile of 32 sorted rows: lanes 0..31 fill the key tile, lanes
 // 32..63 the query tile; every field is written as one contiguous run.
-__global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int ntiles,
+__global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int ntiles, float scale_log2,
                                                              const uint32_t *__restrict__ srec,
                                                              const uint32_t *__restrict__ meta,
                                                              const float *__restrict__ rnorm,
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
     const int nr = r < kMaxEarlier ? r : kMaxEarlier;
     if (lane < kBlk) {
         uint8_t *kt = ktile + (size_t)tile * kKTile;
-        reinterpret_cast<float *>(kt)[k] = rnorm[tok];
+        reinterpret_cast<float *>(kt)[k] = rnorm[tok] * scale_log2;
         for (int rr = 0; rr < nr; ++rr)
             reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] = (uint16_t)rec_lo(m[rr]);
     } else if (qtile) {
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const float4 rn4 = *reinterpret_cast<const float4 *>(rnk + 8 * g + 4 * h);
-            const float rn[4] = {rn4.x * scale_log2, rn4.y * scale_log2, rn4.z * scale_log2, rn4.w * scale_log2};
+            const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};   // already times scale log2(e)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 x[4 * g + t] = ok[4 * g + t] ? sacc[4 * g + t] * rn[t] : -INFINITY;
@@ -533,8 +534,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int e = 4 * g + t;
-                const float pr = ok[e] ? fast_exp2(sacc[e] * rn[t] * scale_log2 - lse2) : 0.f;
-                gs[e] = pr * (pacc[e] - Di) * (scale * rn[t]);
+                const float pr = ok[e] ? fast_exp2(fmaf(sacc[e], rn[t], -lse2)) : 0.f;
+                gs[e] = pr * (pacc[e] - Di) * (rn[t] * kLn2);
             }
         }
         // dQ^T += K^T Gs^T
@@ -644,8 +645,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int kpos = (int)rec_lo(qrecs[sk - k0]);
     const uint8_t *kt = Kt[wave / 2];             // this wave's 16 keys are entries 16 (wave % 2) + c
     const int ke = 16 * (wave % 2) + c;
-    const float rn = reinterpret_cast<const float *>(kt)[ke];
-    const float krn2 = rn * scale * kLog2e;
+    const float krn2 = reinterpret_cast<const float *>(kt)[ke];   // rn * scale * log2(e)
+    const float rn = krn2 / (scale * kLog2e);
     // query blocks [k0 + 32 b, +32) whose first query's window reaches the owned keys
     // (window starts do not decrease along the sorted order)
     const int k_last = k0 + kRows - 1;
@@ -944,6 +945,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const size_t part0 = (size_t)seg * L;
     const uint8_t *qtb = qtile + (size_t)seg * nblk * kQTile;
     const uint8_t *ktb = ktile + (size_t)seg * nblk * kKTile;
+    const float inv_sl2 = 1.f / (scale * kLog2e);
 
     // absolute query block a: its rows of q and dO, and its query tile
     auto issue_block = [&](int a) __attribute__((always_inline)) {
@@ -1008,8 +1010,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int kpos = (int)rec_lo(recs[sk % kRecRing]);
         const uint8_t *kt = Kt[j % 3][kg / 2];                // entries 16 (kg % 2) + c
         const int ke = 16 * (kg % 2) + c;
-        const float rn = reinterpret_cast<const float *>(kt)[ke];
-        const float krn2 = rn * scale * kLog2e;
+        const float krn2 = reinterpret_cast<const float *>(kt)[ke];   // rn * scale * log2(e)
+        const float rn = krn2 * inv_sl2;
         bf16x8_t kop[D / 32];
         {
             const uint16_t *Kq = Qs[(a0 + kg / 2) % kStreamStages];
@@ -1267,15 +1269,15 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const float4 rn4 = *reinterpret_cast<const float4 *>(rnk + 16 * kk + 4 * g);
-                const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};
+                const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};   // rn * scale * log2(e)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const int e = 4 * kk + tt;
                     if constexpr (BWD) {
-                        const float pr = ok[e] ? fast_exp2(sacc[kk][tt] * rn[tt] * scale_log2 - cur.lse2) : 0.f;
-                        x[e] = pr * (pacc[kk][tt] - cur.Di) * (scale * rn[tt]);
+                        const float pr = ok[e] ? fast_exp2(fmaf(sacc[kk][tt], rn[tt], -cur.lse2)) : 0.f;
+                        x[e] = pr * (pacc[kk][tt] - cur.Di) * (rn[tt] * kLn2);
                     } else {
-                        x[e] = ok[e] ? sacc[kk][tt] * (rn[tt] * scale_log2) : -INFINITY;
+                        x[e] = ok[e] ? sacc[kk][tt] * rn[tt] : -INFINITY;
                     }
                 }
             }
@@ -1515,7 +1517,7 @@ hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, c
     const int per_block = kThreads / kWave;
     ProfScope prof(LSH_KERNEL_TILES, st);
     hipLaunchKernelGGL(tile_prep_kernel, dim3((ntiles + per_block - 1) / per_block), dim3(kThreads), 0, st, P.L, P.nh,
-                       ntiles, srec, meta, rnorm, lse, Dv, ktile, qtile);
+                       ntiles, P.scale * kLog2e, srec, meta, rnorm, lse, Dv, ktile, qtile);
     return hipGetLastError();
 }
 
