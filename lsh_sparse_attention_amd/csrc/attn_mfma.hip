@@ -609,6 +609,24 @@ __device__ __forceinline__ void dma_rows512(const bf16 *__restrict__ a, const bf
     }
 }
 
+// One wave loads a whole block: rows [0, 32) of tensors a and b (positions
+// from rec) into the swizzled tiles A and B, D/16 instructions per tensor.
+template <int D>
+__device__ __forceinline__ void dma_block_wave(const bf16 *__restrict__ a, const bf16 *__restrict__ b, uint16_t *A,
+                                               uint16_t *B, const uint32_t *rec, size_t tok0, int lane)
+{
+    constexpr int CPR = D / 8, N = kBlk * CPR / kWave;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int qc = i * kWave + lane;
+        const int row = qc / CPR, p = qc % CPR;
+        const int lc = p ^ (row & (CPR - 1));
+        const size_t off = (tok0 + rec_lo(rec[row])) * D + lc * 8;
+        dma16(a + off, A + i * kWave * 8);
+        dma16(b + off, B + i * kWave * 8);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(
     int L, int nh, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
@@ -1094,6 +1112,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     __shared__ __align__(16) uint8_t Kts[kStreamStages][kKTile];
     __shared__ __align__(16) uint32_t recs[kRecRing];
     __shared__ uint32_t qm[kKvThreads / kWave][kMaxEarlier][16];   // earlier-round records of the queries
+    __shared__ uint32_t rel[kStreamStages];   // waves through a stage's block, 8 per tile
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int g = lane / 16, c = lane % 16;
@@ -1154,6 +1173,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     };
 
     // prologue: records [s0 - 128, s0 + 256), then the first tile's eight blocks and query rows
+    if (tid < kStreamStages)
+        rel[tid] = 0u;
     {
         const int s0 = t_begin * kRows;
         if (s0 >= kRows)
@@ -1162,7 +1183,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         if (s0 + kRows < L)
             issue_recs(s0 + kRows, 7);
         wait_vm<0>();
-        block_barrier();
+        lds_barrier();   // also publishes the zeroed release counters
         for (int a = s0 / kBlk - 4; a < s0 / kBlk + 4; ++a)
             if (a >= 0 && a < nblk)
                 issue_block(a);
@@ -1191,12 +1212,15 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 lse_rounds[part0 + qpos] = lrun > 0.f ? (mrun + __log2f(lrun)) * 0.69314718055994531f : -INFINITY;
     };
 
+    QRegs nxt;
     for (int t = t_begin; t < t_end; ++t) {
         const int s0 = t * kRows, a0 = s0 / kBlk;
         // everything issued during the previous tile has landed
         wait_vm<0>();
-        if (t > t_begin)
+        if (t > t_begin) {
             finish(qpos_prev);
+            cur = nxt;
+        }
         if (g == 0) {
 #pragma unroll
             for (int rr = 0; rr < kMaxEarlier; ++rr)
@@ -1319,25 +1343,31 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 acc[dt] = mfma16(tr[dt], xb, acc[dt]);
         };
 
-        for (int a = a0 - 4; a < a0; ++a)
+        // The earlier blocks: once every wave is through block a, its stage
+        // takes block a + 8 (the next tile's own rows), loaded by the wave
+        // that released it last, so the next tile's loads start as early as
+        // the stages allow and no wave waits for another here.
+        for (int a = a0 - 4; a < a0; ++a) {
             if (a >= 0)
                 work(a);
-        // the earlier blocks are through: their stages take the next tile's new blocks
-        block_barrier();
-        QRegs nxt;
+            uint32_t old = 0u;
+            if (lane == 0)
+                old = atomicAdd(&rel[(a + 8) % kStreamStages], 1u);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old % 8u == 7u && t + 1 < t_end && a + 8 < nblk) {
+                const int st = (a + 8) % kStreamStages;
+                dma_block_wave<D>(q, v, Ks[st], Vs[st], recs + ((a + 8) * kBlk) % kRecRing, tok0, lane);
+                dma16(ktb + (size_t)(a + 8) * kKTile + 16 * lane, Kts[st]);
+            }
+        }
         if (t + 1 < t_end) {
             load_q(t + 1, nxt);
-            for (int a = a0 + 4; a < a0 + 8; ++a)
-                if (a < nblk)
-                    issue_block(a);
             if (s0 + 2 * kRows < L)
                 issue_recs(s0 + 2 * kRows, 6);
         }
         for (int a = a0; a < a0 + 4; ++a)
             work(a);
         qpos_prev = cur.qpos;
-        if (t + 1 < t_end)
-            cur = nxt;
     }
     finish(qpos_prev);
 }
