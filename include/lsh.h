@@ -52,7 +52,9 @@ typedef enum { LSH_WS_SORT = 0, LSH_WS_FWD = 1, LSH_WS_BWD = 2 } lsh_ws_kind_t;
 /*
  * Problem description, passed by pointer to every call.
  *   batch, heads, seq_len, head_dim: B, H, L, d.  Supported: d in {32, 64, 128};
- *       1 <= L <= 65536.
+ *       B >= 0, H >= 0, 0 <= L <= 65536.  A problem with B, H or L equal to 0
+ *       is empty: every call on it returns LSH_OK at once, without reading
+ *       its pointers or launching anything.
  *   n_hashes: nh >= 1 hash rounds (<= 16).
  *   n_buckets: nb, even, 2 <= nb <= 4096; nb = 2 * columns of the rotation.
  *   chunk_len: m, 1 <= m, L % m == 0 (m == L gives one chunk).
@@ -78,7 +80,7 @@ int lsh_version(void);
 
 /* Bytes of device workspace that lsh_sort (LSH_WS_SORT), lsh_attn_fwd
  * (LSH_WS_FWD) or lsh_attn_bwd (LSH_WS_BWD) needs for `prob`; 0 if the
- * problem is invalid.  Alignment of the workspace pointer: 256 bytes. */
+ * problem is invalid or empty.  Alignment of the workspace pointer: 256 bytes. */
 size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind);
 
 /*

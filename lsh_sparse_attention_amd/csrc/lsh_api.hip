@@ -43,7 +43,7 @@ int validate(const lsh_problem_t *p)
 {
     if (!p)
         return LSH_ERR_INVALID;
-    if (p->batch < 1 || p->heads < 1 || p->seq_len < 1 || p->head_dim < 1 || p->n_hashes < 1 ||
+    if (p->batch < 0 || p->heads < 0 || p->seq_len < 0 || p->head_dim < 1 || p->n_hashes < 1 ||
         p->n_buckets < 2 || (p->n_buckets & 1) || p->chunk_len < 1 || p->seq_len % p->chunk_len ||
         !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16))
         return LSH_ERR_INVALID;
@@ -59,6 +59,10 @@ int validate(const lsh_problem_t *p)
         return LSH_ERR_UNSUPPORTED;
     return LSH_OK;
 }
+
+// B, H or L of zero: nothing to compute; every call returns LSH_OK without
+// reading its pointers or touching the device.
+bool empty(const lsh_problem_t *p) { return p->batch == 0 || p->heads == 0 || p->seq_len == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
@@ -148,7 +152,7 @@ int lsh_profile_kernel(int kernel, void *start_event, void *stop_event)
 
 size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
 {
-    if (validate(prob) != LSH_OK)
+    if (validate(prob) != LSH_OK || empty(prob))
         return 0;
     const Dims P = dims_of(prob);
     switch (kind) {
@@ -162,7 +166,7 @@ size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
 int lsh_hash(const lsh_problem_t *prob, const void *q, const void *rot, int32_t *buckets, void *stream)
 {
     int st = validate(prob);
-    if (st != LSH_OK)
+    if (st != LSH_OK || empty(prob))
         return st;
     if (!q || !rot || !buckets || !aligned16(q) || !aligned16(rot) || !aligned16(buckets))
         return LSH_ERR_INVALID;
@@ -173,7 +177,7 @@ int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, i
              void *ws, size_t ws_bytes, void *stream)
 {
     int st = validate(prob);
-    if (st != LSH_OK)
+    if (st != LSH_OK || empty(prob))
         return st;
     const Dims P = dims_of(prob);
     if (!buckets || !perm || !inv || !win_lo || !ws || ws_bytes < sort_ws_bytes(P) || ((uintptr_t)ws & 255u))
@@ -185,7 +189,7 @@ int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const 
                  const int32_t *win_lo, void *o_rounds, float *lse_rounds, void *ws, size_t ws_bytes, void *stream)
 {
     int st = validate(prob);
-    if (st != LSH_OK)
+    if (st != LSH_OK || empty(prob))
         return st;
     const Dims P = dims_of(prob);
     if (!q || !v || !perm || !inv || !win_lo || !o_rounds || !lse_rounds || !ws || ((uintptr_t)ws & 255u) ||
@@ -211,7 +215,7 @@ int lsh_combine(const lsh_problem_t *prob, const void *q, const void *v, const v
                 const float *lse_rounds, void *out, float *lse, void *stream)
 {
     int st = validate(prob);
-    if (st != LSH_OK)
+    if (st != LSH_OK || empty(prob))
         return st;
     if (!q || !v || !o_rounds || !lse_rounds || !out || !lse || !aligned16(q) || !aligned16(v) ||
         !aligned16(o_rounds) || !aligned16(out))
@@ -225,7 +229,7 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
                  void *ws, size_t ws_bytes, void *stream)
 {
     int st = validate(prob);
-    if (st != LSH_OK)
+    if (st != LSH_OK || empty(prob))
         return st;
     const Dims P = dims_of(prob);
     if (!q || !v || !out || !dout || !lse || !perm || !inv || !win_lo || !dq || !dv || !ws ||

@@ -42,7 +42,8 @@ def _prob(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(n_buckets=15), 1), (dict(n_buckets=0), 1), (dict(chunk_len=48), 1), (dict(seq_len=0), 1),
+    (dict(n_buckets=15), 1), (dict(n_buckets=0), 1), (dict(chunk_len=48), 1), (dict(seq_len=-256), 1),
+    (dict(batch=-1), 1), (dict(chunk_len=0), 1),
     (dict(head_dim=48), 2), (dict(seq_len=65536 * 2, chunk_len=64), 2), (dict(n_hashes=17), 2),
     (dict(n_buckets=8192), 2),
 ])
@@ -52,6 +53,24 @@ def test_invalid_problems_rejected_before_launch(kw, status):
     dummy = ctypes.c_void_p(256)
     assert L.lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == status
     assert L.lsh_workspace_bytes(ctypes.byref(p), 0) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(seq_len=0), dict(batch=0), dict(heads=0)])
+def test_empty_problems_are_no_ops(kw):
+    # null pointers and a null workspace are fine: nothing is read or launched
+    p = _prob(**kw)
+    L = _lib.lib()
+    for k in (0, 1, 2):
+        assert L.lsh_workspace_bytes(ctypes.byref(p), k) == 0
+    n = None
+    assert L.lsh_hash(ctypes.byref(p), n, n, n, n) == 0
+    assert L.lsh_sort(ctypes.byref(p), n, n, n, n, n, ctypes.c_size_t(0), n) == 0
+    assert L.lsh_attn_fwd(ctypes.byref(p), n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
+    assert L.lsh_combine(ctypes.byref(p), n, n, n, n, n, n, n) == 0
+    assert L.lsh_attn_bwd(ctypes.byref(p), n, n, n, n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
+    # an empty problem is still validated: a bad head size is reported
+    bad = _prob(head_dim=48, **kw)
+    assert L.lsh_hash(ctypes.byref(bad), n, n, n, n) == 2
 
 
 def test_non_causal_is_unsupported():

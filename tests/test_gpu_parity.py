@@ -38,6 +38,8 @@ SMALL = [
     ("bf16-m96", 1, 2, 1536, 64, 32, 3, 96, "bf16", False),
     ("bf16-m256", 1, 1, 2048, 128, 16, 2, 256, "bf16", False),
     ("bf16-runs", 1, 4, 8192, 64, 128, 2, 128, "bf16", False),
+    ("bf16-m1", 1, 2, 512, 64, 8, 2, 1, "bf16", False),
+    ("bf16-nh16", 1, 1, 512, 64, 16, 16, 32, "bf16", False),
 ]
 
 
@@ -117,3 +119,16 @@ def test_deterministic():
     b = gu.run_gpu(x)
     for k in ("buckets", "perm", "inv", "win_lo", "out", "lse", "dq", "dv"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_empty_problem_is_a_no_op():
+    import lsh_sparse_attention_amd as lsh
+    gu.say("[gpu] empty problem L=0")
+    p = lsh.problem(1, 2, 0, 64, 2, 16, 32, dtype="bf16")
+    att = lsh.LshAttention(p)
+    q = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    rot = torch.randn((2, 64, 8), device="cuda").to(torch.bfloat16)
+    out, lse = att.forward(q, q, rot)
+    dq, dv = att.backward(q, q, q)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 2, 0, 64) and lse.shape == (1, 2, 0) and dq.numel() == 0 and dv.numel() == 0
