@@ -47,7 +47,7 @@ typedef enum {
 typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype_t;
 
 /* Which call a workspace is for (lsh_workspace_bytes). */
-typedef enum { LSH_WS_SORT = 0, LSH_WS_FWD = 1, LSH_WS_BWD = 2 } lsh_ws_kind_t;
+typedef enum { LSH_WS_SORT = 0, LSH_WS_FWD = 1, LSH_WS_BWD = 2, LSH_WS_TRAIN = 3 } lsh_ws_kind_t;
 
 /*
  * Problem description, passed by pointer to every call.
@@ -79,8 +79,10 @@ const char *lsh_status_string(int status);
 int lsh_version(void);
 
 /* Bytes of device workspace that lsh_sort (LSH_WS_SORT), lsh_attn_fwd
- * (LSH_WS_FWD) or lsh_attn_bwd (LSH_WS_BWD) needs for `prob`; 0 if the
- * problem is invalid or empty.  Alignment of the workspace pointer: 256 bytes. */
+ * (LSH_WS_FWD) or lsh_attn_bwd (LSH_WS_BWD) needs for `prob`, or that one
+ * workspace shared by lsh_attn_fwd and a later lsh_attn_bwd_saved needs
+ * (LSH_WS_TRAIN); 0 if the problem is invalid or empty.  Alignment of every
+ * workspace pointer: 256 bytes. */
 size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind);
 
 /*
@@ -130,7 +132,10 @@ int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, i
  *              the round's unmasked members (0 if there are none).
  *   lse_rounds [B][H][nh][L] fp32 out: log of the round's softmax
  *              denominator (-inf if there are no unmasked members).
- *   ws         workspace of lsh_workspace_bytes(prob, LSH_WS_FWD) bytes.
+ *   ws         workspace of lsh_workspace_bytes(prob, LSH_WS_FWD) bytes, or
+ *              of LSH_WS_TRAIN bytes to keep what the forward derives from
+ *              q, perm, inv and win_lo (packed sorted records, inverse norms,
+ *              per-block key data) for lsh_attn_bwd_saved.
  */
 int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const int32_t *perm,
                  const int32_t *inv, const int32_t *win_lo, void *o_rounds, float *lse_rounds,
@@ -170,6 +175,23 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
                  void *stream);
 
 /*
+ * lsh_attn_bwd_saved -- lsh_attn_bwd for a training step that keeps the
+ * forward's workspace: the gradient is the same (bit for bit), but the
+ * records that the forward derived from q, perm, inv and win_lo are read
+ * from ws instead of being derived again.
+ *   ws         workspace of at least lsh_workspace_bytes(prob, LSH_WS_TRAIN)
+ *              bytes that was passed to lsh_attn_fwd for the same problem,
+ *              q, perm, inv and win_lo, and that nothing has written to
+ *              since (the caller's contract; it is not checked, and results
+ *              are undefined if it does not hold).  Its first LSH_WS_FWD
+ *              bytes are read, the rest is overwritten.
+ *   other arguments as for lsh_attn_bwd.
+ */
+int lsh_attn_bwd_saved(const lsh_problem_t *prob, const void *q, const void *v, const void *out,
+                       const void *dout, const float *lse, void *dq, void *dv, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/*
  * Instrumentation (not needed to compute anything).
  *
  * Kernels of the library, for lsh_profile_kernel and lsh_kernel_name.
@@ -180,7 +202,8 @@ typedef enum {
     LSH_KERNEL_SORT_SCAN = 2,   /* lsh_sort: offsets of (tile, bucket) runs         */
     LSH_KERNEL_SORT_SCATTER = 3,/* lsh_sort: stable ranks, perm / inv / win_lo      */
     LSH_KERNEL_PREP = 4,        /* lsh_attn_fwd / lsh_attn_bwd: packed records,
-                                   inverse norms (and dO . O in the backward)      */
+                                   inverse norms (and dO . O in the backward;
+                                   only that in lsh_attn_bwd_saved)                */
     LSH_KERNEL_FWD = 5,         /* lsh_attn_fwd: per-round chunk attention          */
     LSH_KERNEL_COMBINE = 6,     /* lsh_combine                                      */
     LSH_KERNEL_BWD_DQ = 7,      /* lsh_attn_bwd: query-side gradient per round      */

@@ -6,7 +6,8 @@ stream.  No step of the computation runs in Python or torch; torch provides
 device memory and streams only.  If liblsh.so is missing, the calls raise.
 
 Pipeline (per (batch, head, round)): ``lsh_hash`` -> ``lsh_sort`` ->
-``lsh_attn_fwd`` -> ``lsh_combine``; backward: ``lsh_attn_bwd``.
+``lsh_attn_fwd`` -> ``lsh_combine``; backward: ``lsh_attn_bwd``, or
+``lsh_attn_bwd_saved`` on the workspace the forward filled.
 """
 from __future__ import annotations
 
@@ -15,10 +16,11 @@ import math
 
 import torch
 
-from ._lib import (LSH_BF16, LSH_F32, LSH_WS_BWD, LSH_WS_FWD, LSH_WS_SORT, LshError, Problem, check, lib)
+from ._lib import (LSH_BF16, LSH_F32, LSH_WS_BWD, LSH_WS_FWD, LSH_WS_SORT, LSH_WS_TRAIN, LshError, Problem, check,
+                   lib)
 
 __all__ = ["Problem", "LshError", "problem", "workspace_bytes", "lsh_hash", "lsh_sort", "lsh_attn_fwd",
-           "lsh_combine", "lsh_attn_bwd", "LshAttention"]
+           "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "LshAttention"]
 
 _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
 
@@ -137,11 +139,25 @@ def lsh_attn_bwd(prob, q, v, out, dout, lse, perm, inv, win_lo, dq, dv, ws, stre
         _ptr(win_lo, "win_lo", torch.int32), _ptr(dq, "dq", dt), _ptr(dv, "dv", dt), wp, wn, _stream(stream)))
 
 
+def lsh_attn_bwd_saved(prob, q, v, out, dout, lse, dq, dv, ws, stream=None):
+    """lsh_attn_bwd on the records that lsh_attn_fwd left in ``ws`` (an LSH_WS_TRAIN workspace)."""
+    dt = torch_dtype(prob)
+    n, nd = _tok(prob), _tok(prob) * prob.head_dim
+    for t, nm, k in ((q, "q", nd), (v, "v", nd), (out, "out", nd), (dout, "dout", nd), (lse, "lse", n),
+                     (dq, "dq", nd), (dv, "dv", nd)):
+        _numel_check(t, k, nm)
+    wp, wn = _ws(ws, prob, LSH_WS_TRAIN)
+    check("lsh_attn_bwd_saved", lib().lsh_attn_bwd_saved(
+        ctypes.byref(prob), _ptr(q, "q", dt), _ptr(v, "v", dt), _ptr(out, "out", dt), _ptr(dout, "dout", dt),
+        _ptr(lse, "lse", torch.float32), _ptr(dq, "dq", dt), _ptr(dv, "dv", dt), wp, wn, _stream(stream)))
+
+
 class LshAttention:
     """Device buffers for one problem shape and the five calls in order.
 
     ``forward(q, v, rot)`` runs hash, sort, per-round attention and combine;
-    ``backward(q, v, dout)`` runs the backward of the last forward.  Buffers
+    ``backward(q, v, dout)`` runs the backward of the last forward (same q
+    and v), on the records the forward left in the shared workspace.  Buffers
     are allocated once, here; the calls themselves allocate nothing.
     """
 
@@ -159,9 +175,10 @@ class LshAttention:
         self.out = torch.empty((B, H, L, d), dtype=dt, **kw)
         self.lse = torch.empty((B, H, L), dtype=torch.float32, **kw)
         self.ws_sort = torch.empty(max(1, workspace_bytes(prob, LSH_WS_SORT)), dtype=torch.uint8, **kw)
-        self.ws_fwd = torch.empty(max(1, workspace_bytes(prob, LSH_WS_FWD)), dtype=torch.uint8, **kw)
+        # with a backward, one workspace serves both (the backward reads the forward's records)
+        kind = LSH_WS_TRAIN if backward else LSH_WS_FWD
+        self.ws_fwd = torch.empty(max(1, workspace_bytes(prob, kind)), dtype=torch.uint8, **kw)
         if backward:
-            self.ws_bwd = torch.empty(max(1, workspace_bytes(prob, LSH_WS_BWD)), dtype=torch.uint8, **kw)
             self.dq = torch.empty((B, H, L, d), dtype=dt, **kw)
             self.dv = torch.empty((B, H, L, d), dtype=dt, **kw)
 
@@ -175,6 +192,5 @@ class LshAttention:
 
     def backward(self, q, v, dout, stream=None):
         p = self.prob
-        lsh_attn_bwd(p, q, v, self.out, dout, self.lse, self.perm, self.inv, self.win_lo, self.dq, self.dv,
-                     self.ws_bwd, stream)
+        lsh_attn_bwd_saved(p, q, v, self.out, dout, self.lse, self.dq, self.dv, self.ws_fwd, stream)
         return self.dq, self.dv

@@ -42,23 +42,25 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *
     const bool valid = t < L;
     const size_t tok = (size_t)bh * L + (valid ? t : 0);
     float x[8], y[8];
-    float ss = 0.f;
-    if (valid) {
-        load8(q + tok * D + ch * 8, x);
+    if (meta) {
+        float ss = 0.f;
+        if (valid) {
+            load8(q + tok * D + ch * 8, x);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            ss = fmaf(x[k], x[k], ss);
-    }
-    ss = group_sum(ss, CPT);
-    if (valid && ch == 0)
-        rnorm[tok] = 1.0f / sqrtf(ss);
-    if (valid) {
-        for (int r = ch; r < nh; r += CPT) {
-            const size_t idx = ((size_t)bh * nh + r) * L + t;
-            const uint32_t s = (uint32_t)inv[idx];
-            const uint32_t w = s - (uint32_t)win_lo[idx];
-            meta[tok * nh + r] = s | (w << 16);
-            srec[((size_t)bh * nh + r) * L + s] = (uint32_t)t | (w << 16);
+            for (int k = 0; k < 8; ++k)
+                ss = fmaf(x[k], x[k], ss);
+        }
+        ss = group_sum(ss, CPT);
+        if (valid && ch == 0)
+            rnorm[tok] = 1.0f / sqrtf(ss);
+        if (valid) {
+            for (int r = ch; r < nh; r += CPT) {
+                const size_t idx = ((size_t)bh * nh + r) * L + t;
+                const uint32_t s = (uint32_t)inv[idx];
+                const uint32_t w = s - (uint32_t)win_lo[idx];
+                meta[tok * nh + r] = s | (w << 16);
+                srec[((size_t)bh * nh + r) * L + s] = (uint32_t)t | (w << 16);
+            }
         }
     }
     if (Dvec) {

@@ -179,8 +179,9 @@ __device__ __forceinline__ void clear_hits(bool (&ok)[16], const uint32_t (&hit)
 // ---------------------------------------------------------------------------
 // metadata tiles, per 32 sorted rows of each (b, h, round)
 
-// One wave per tile of 32 sorted rows: lanes 0..31 fill the key tile, lanes
-// 32..63 the query tile; every field is written as one contiguous run.
+// One wave per tile of 32 sorted rows: lanes 0..31 fill the key tile (unless
+// ktile is null), lanes 32..63 the query tile (unless qtile is null); every
+// field is written as one contiguous run.
 __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int ntiles, float scale_log2,
                                                              const uint32_t *__restrict__ srec,
                                                              const uint32_t *__restrict__ meta,
@@ -201,6 +202,8 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
     const uint32_t *m = meta + tok * nh;
     const int nr = r < kMaxEarlier ? r : kMaxEarlier;
     if (lane < kBlk) {
+        if (!ktile)
+            return;
         uint8_t *kt = ktile + (size_t)tile * kKTile;
         reinterpret_cast<float *>(kt)[k] = rnorm[tok] * scale_log2;
         for (int rr = 0; rr < nr; ++rr)
@@ -1581,12 +1584,12 @@ hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, con
 
 hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
                                 const float *Dv, const int32_t *inv, const int32_t *win_lo, const uint32_t *meta,
-                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, uint8_t *qtile, void *part,
-                                void *dq, void *dv, hipStream_t st)
+                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, bool make_ktile,
+                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
 {
     (void)inv;
     (void)win_lo;
-    hipError_t e = tiles_go(P, srec, meta, rnorm, lse, Dv, ktile, qtile, st);
+    hipError_t e = tiles_go(P, srec, meta, rnorm, lse, Dv, make_ktile ? ktile : nullptr, qtile, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)

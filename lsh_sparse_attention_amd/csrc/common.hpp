@@ -95,6 +95,8 @@ hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, 
 hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv,
                        int32_t *win_lo, void *ws, hipStream_t);
 size_t sort_ws_bytes(const Dims &);
+// Packed records, inverse norms and (with out, dout) D = dO . O; with meta
+// null only D is written (the records are already in place).
 hipError_t launch_prep(const Dims &, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
                        const int32_t *win_lo, uint32_t *meta, uint32_t *srec, float *rnorm,
                        const void *out, const void *dout, float *D, hipStream_t);
@@ -301,8 +303,8 @@ hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, cons
                                 const float *rnorm, uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t);
 hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
                                 const float *D, const int32_t *inv, const int32_t *win_lo, const uint32_t *meta,
-                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, uint8_t *qtile,
-                                void *part, void *dq, void *dv, hipStream_t);
+                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, bool make_ktile,
+                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t);
 hipError_t launch_bwd_reduce(const Dims &, int dtype, const void *q, const void *dout, const uint32_t *meta,
                              const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,
                              void *dq, void *dv, hipStream_t);

@@ -103,17 +103,49 @@ BwdWs bwd_layout(const Dims &P, void *base)
     w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
+    // up to here the same offsets as the forward's workspace, so that a
+    // backward can take over the forward's records
+    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
     w.D = (float *)(b + o); o += align_up(tok * 4, 256);
     w.dq_part = (float *)(b + o); o += align_up(part, 256);
     w.dk_part = (float *)(b + o); o += align_up(part, 256);
     w.dv_part = (float *)(b + o); o += align_up(part, 256);
-    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
     w.qtile = (uint8_t *)(b + o); o += align_up(mfma_qtile_bytes(P), 256);
     w.bytes = o;
     return w;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The backward behind both entry points.  With perm null the packed
+// records, norms and key tiles are taken as lsh_attn_fwd left them in ws
+// (same offsets); otherwise they are derived from perm, inv, win_lo first.
+int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void *out, const void *dout,
+             const float *lse, const int32_t *perm, const int32_t *inv, const int32_t *win_lo, void *dq, void *dv,
+             void *ws, size_t ws_bytes, void *stream)
+{
+    const Dims P = dims_of(prob);
+    if (!q || !v || !out || !dout || !lse || !dq || !dv || !ws || ((uintptr_t)ws & 255u) || !aligned16(q) ||
+        !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dv))
+        return LSH_ERR_INVALID;
+    const BwdWs w = bwd_layout(P, ws);
+    if (ws_bytes < w.bytes)
+        return LSH_ERR_INVALID;
+    const bool derive = perm != nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, derive ? w.meta : nullptr, w.srec, w.rnorm,
+                               out, dout, w.D, s);
+    if (e == hipSuccess) {
+        if (mfma_path_ok(P, prob->dtype)) {
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, inv, win_lo, w.meta, w.srec, w.rnorm, w.ktile, derive,
+                                     w.qtile, w.dq_part, dq, dv, s);
+        } else {
+            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part,
+                                w.dk_part, w.dv_part, dq, dv, s);
+        }
+    }
+    return hip_status(e);
+}
 
 }  // namespace
 
@@ -130,7 +162,7 @@ const char *lsh_status_string(int status)
     }
 }
 
-int lsh_version(void) { return 100; }
+int lsh_version(void) { return 200; }
 
 const char *lsh_kernel_name(int kernel)
 {
@@ -158,7 +190,8 @@ size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
     switch (kind) {
     case LSH_WS_SORT: return sort_ws_bytes(P);
     case LSH_WS_FWD: return fwd_layout(P, nullptr).bytes;
-    case LSH_WS_BWD: return bwd_layout(P, nullptr).bytes;
+    case LSH_WS_BWD:
+    case LSH_WS_TRAIN: return bwd_layout(P, nullptr).bytes;
     default: return 0;
     }
 }
@@ -231,26 +264,18 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     int st = validate(prob);
     if (st != LSH_OK || empty(prob))
         return st;
-    const Dims P = dims_of(prob);
-    if (!q || !v || !out || !dout || !lse || !perm || !inv || !win_lo || !dq || !dv || !ws ||
-        ((uintptr_t)ws & 255u) || !aligned16(q) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
-        !aligned16(dq) || !aligned16(dv))
+    if (!perm || !inv || !win_lo)
         return LSH_ERR_INVALID;
-    const BwdWs w = bwd_layout(P, ws);
-    if (ws_bytes < w.bytes)
-        return LSH_ERR_INVALID;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, out, dout, w.D, s);
-    if (e == hipSuccess) {
-        if (mfma_path_ok(P, prob->dtype)) {
-            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, inv, win_lo, w.meta, w.srec, w.rnorm, w.ktile, w.qtile,
-                                     w.dq_part, dq, dv, s);
-        } else {
-            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part,
-                                w.dk_part, w.dv_part, dq, dv, s);
-        }
-    }
-    return hip_status(e);
+    return attn_bwd(prob, q, v, out, dout, lse, perm, inv, win_lo, dq, dv, ws, ws_bytes, stream);
+}
+
+int lsh_attn_bwd_saved(const lsh_problem_t *prob, const void *q, const void *v, const void *out, const void *dout,
+                       const float *lse, void *dq, void *dv, void *ws, size_t ws_bytes, void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK || empty(prob))
+        return st;
+    return attn_bwd(prob, q, v, out, dout, lse, nullptr, nullptr, nullptr, dq, dv, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

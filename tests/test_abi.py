@@ -60,7 +60,7 @@ def test_empty_problems_are_no_ops(kw):
     # null pointers and a null workspace are fine: nothing is read or launched
     p = _prob(**kw)
     L = _lib.lib()
-    for k in (0, 1, 2):
+    for k in (0, 1, 2, 3):
         assert L.lsh_workspace_bytes(ctypes.byref(p), k) == 0
     n = None
     assert L.lsh_hash(ctypes.byref(p), n, n, n, n) == 0
@@ -68,6 +68,7 @@ def test_empty_problems_are_no_ops(kw):
     assert L.lsh_attn_fwd(ctypes.byref(p), n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
     assert L.lsh_combine(ctypes.byref(p), n, n, n, n, n, n, n) == 0
     assert L.lsh_attn_bwd(ctypes.byref(p), n, n, n, n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
+    assert L.lsh_attn_bwd_saved(ctypes.byref(p), n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
     # an empty problem is still validated: a bad head size is reported
     bad = _prob(head_dim=48, **kw)
     assert L.lsh_hash(ctypes.byref(bad), n, n, n, n) == 2
@@ -99,10 +100,31 @@ def test_null_and_misaligned_pointers_rejected():
     assert L.lsh_attn_fwd(None, ok, ok, ok, ok, ok, ok, ok, ok, ctypes.c_size_t(1 << 30), None) == 1
 
 
+def test_saved_backward_workspace_and_arguments():
+    # the shared workspace holds the forward's records at the forward's offsets and the backward's scratch
+    p = _prob()
+    L = _lib.lib()
+    fwd = lsh.workspace_bytes(p, _lib.LSH_WS_FWD)
+    train = lsh.workspace_bytes(p, _lib.LSH_WS_TRAIN)
+    assert train == lsh.workspace_bytes(p, _lib.LSH_WS_BWD) and train > fwd > 0
+    assert L.lsh_workspace_bytes(ctypes.byref(p), 4) == 0
+    ok = ctypes.c_void_p(1 << 20)
+    args = [ok] * 7
+    assert L.lsh_attn_bwd_saved(ctypes.byref(p), *args, ok, ctypes.c_size_t(train - 1), None) == 1
+    assert L.lsh_attn_bwd_saved(ctypes.byref(p), *args, None, ctypes.c_size_t(train), None) == 1
+    assert L.lsh_attn_bwd_saved(ctypes.byref(p), *args, ctypes.c_void_p((1 << 20) + 128), ctypes.c_size_t(train),
+                                None) == 1
+    assert L.lsh_attn_bwd_saved(ctypes.byref(p), None, *args[1:], ok, ctypes.c_size_t(train), None) == 1
+    assert L.lsh_attn_bwd_saved(None, *args, ok, ctypes.c_size_t(train), None) == 1
+    # the standalone backward still wants the sort's outputs
+    assert L.lsh_attn_bwd(ctypes.byref(p), ok, ok, ok, ok, ok, None, ok, ok, ok, ok, ok, ctypes.c_size_t(train),
+                          None) == 1
+
+
 def test_workspace_sizes_grow_with_problem():
     small = _prob()
     big = _prob(batch=4)
-    for k in (0, 1, 2):
+    for k in (0, 1, 2, 3):
         assert 0 < lsh.workspace_bytes(small, k) < lsh.workspace_bytes(big, k)
         assert lsh.workspace_bytes(small, k) % 256 == 0
 

@@ -121,6 +121,32 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("idx", [1, 0, 2, 17, 19])
+def test_standalone_backward_matches_saved(idx):
+    # lsh_attn_bwd (records derived again from perm, inv, win_lo) against the
+    # saved-records backward that LshAttention runs: same kernels, same bits
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    cfg = _small_cfg(SMALL[idx])
+    gu.say(f"[gpu] standalone vs saved backward {cfg}")
+    x = gen.generate(cfg)
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype)
+    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
+    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
+    mod = lsh.LshAttention(prob)
+    mod.forward(q, v, rot)
+    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
+    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
+    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
+    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq.view(torch.int16) if dq.dtype == torch.bfloat16 else dq,
+                       dq_s.view(torch.int16) if dq_s.dtype == torch.bfloat16 else dq_s)
+    assert torch.equal(dv.view(torch.int16) if dv.dtype == torch.bfloat16 else dv,
+                       dv_s.view(torch.int16) if dv_s.dtype == torch.bfloat16 else dv_s)
+
+
 def test_empty_problem_is_a_no_op():
     import lsh_sparse_attention_amd as lsh
     gu.say("[gpu] empty problem L=0")
