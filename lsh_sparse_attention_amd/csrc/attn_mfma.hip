@@ -45,6 +45,12 @@ constexpr int kRecCache = 1024;           // sorted records of a workgroup's str
 constexpr int kMaxEarlier = 13;           // earlier rounds a tile holds (n_hashes <= 14)
 constexpr int kKTile = 1024;              // key tile: rn * scale * log2(e) [32] f32, sk[13][32] u16
 constexpr int kQTile = 2048;              // query tile: lse2[32], D[32] f32, w[32] u16, (si1, w)[13][32] u16
+// In global memory a tile stores only the fields of the nh - 1 earlier rounds
+// it can have, rounded up to 256 bytes; in LDS it keeps the full layout
+// above, and copies move only that prefix (16 bytes per lane).
+__host__ __device__ constexpr int ktile_stride(int nh) { return (128 + 64 * (nh - 1) + 255) & ~255; }
+__host__ __device__ constexpr int qtile_stride(int nh) { return (320 + 128 * (nh - 1) + 255) & ~255; }
+static_assert(ktile_stride(kMaxEarlier + 1) <= kKTile && qtile_stride(kMaxEarlier + 1) <= kQTile, "tile sizes");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLazy = 8.0f;             // lazy running-max threshold (log2 units)
@@ -204,12 +210,12 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
     if (lane < kBlk) {
         if (!ktile)
             return;
-        uint8_t *kt = ktile + (size_t)tile * kKTile;
+        uint8_t *kt = ktile + (size_t)tile * ktile_stride(nh);
         reinterpret_cast<float *>(kt)[k] = rnorm[tok] * scale_log2;
         for (int rr = 0; rr < nr; ++rr)
             reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] = (uint16_t)rec_lo(m[rr]);
     } else if (qtile) {
-        uint8_t *qt = qtile + (size_t)tile * kQTile;
+        uint8_t *qt = qtile + (size_t)tile * qtile_stride(nh);
         reinterpret_cast<float *>(qt)[k] = lse[tok] * kLog2e;
         reinterpret_cast<float *>(qt + 128)[k] = Dvec[tok];
         reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
@@ -279,13 +285,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kb_first = (s0 - (int)rec_hi(krec[s0 - c0])) & ~(kBlk - 1);
     const int nblocks = (s0 + kRows - kb_first) / kBlk;
     const uint32_t *kr = krec + (kb_first - c0);
-    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
+    const int kts = ktile_stride(nh);
+    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kts;
 
     auto issue = [&](int b) __attribute__((always_inline)) {
         const int kb = kb_first + b * kBlk, st = b % kQStages;
         dma_rows<D>(q, v, Ks[st], Vs[st], kr, b * kBlk, tok0, tid, wave);
-        if (wave == 0)
-            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
+        if (wave == 0 && 16 * lane < kts)
+            dma16(ktb + (size_t)(kb / kBlk) * kts + 16 * lane, Ts[st]);
     };
     constexpr int AHEAD = kQStages - 1;
     for (int b = 0; b < AHEAD && b < nblocks; ++b)
@@ -453,13 +460,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kb_first = (s0 - (int)rec_hi(krec[s0 - c0])) & ~(kBlk - 1);
     const int nblocks = (s0 + kRows - kb_first) / kBlk;
     const uint32_t *kr = krec + (kb_first - c0);
-    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kKTile;
+    const int kts = ktile_stride(nh);
+    const uint8_t *ktb = ktile + ((size_t)bh * nh + r) * (L / kBlk) * kts;
 
     auto issue = [&](int b) __attribute__((always_inline)) {
         const int kb = kb_first + b * kBlk, st = b % kQStages;
         dma_rows<D>(q, v, Ks[st], Vs[st], kr, b * kBlk, tok0, tid, wave);
-        if (wave == 0)
-            dma16(ktb + (size_t)(kb / kBlk) * kKTile + 16 * lane, Ts[st]);
+        if (wave == 0 && 16 * lane < kts)
+            dma16(ktb + (size_t)(kb / kBlk) * kts + 16 * lane, Ts[st]);
     };
     constexpr int AHEAD = kQStages - 1;
     for (int b = 0; b < AHEAD && b < nblocks; ++b)
@@ -648,13 +656,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int r = W.r, bh = W.bh, k0 = W.s0;
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
-    const uint8_t *qtb = qtile + ((size_t)bh * nh + r) * (L / kBlk) * kQTile;
+    const int kts = ktile_stride(nh), qts = qtile_stride(nh);
+    const uint8_t *qtb = qtile + ((size_t)bh * nh + r) * (L / kBlk) * qts;
 
     // Prologue, two dependent memory round trips: (1) the sorted records of
     // the streamed range and the key tiles of the owned keys; (2) the query
     // blocks (straight into LDS) together with this lane's key and value rows.
-    if (wave < kRows / kBlk)
-        dma16(ktile + (((size_t)bh * nh + r) * (L / kBlk) + k0 / kBlk + wave) * kKTile + 16 * lane, Kt[wave]);
+    if (wave < kRows / kBlk && 16 * lane < kts)
+        dma16(ktile + (((size_t)bh * nh + r) * (L / kBlk) + k0 / kBlk + wave) * kts + 16 * lane, Kt[wave]);
     const int cache_n = min(L - k0, kRecCache);
     for (int i = tid; i < cache_n; i += kKvThreads)
         qrecs[i] = sr[k0 + i];
@@ -677,8 +686,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     auto issue = [&](int b, int st) __attribute__((always_inline)) {
         const int qb = k0 + b * kBlk;
         dma_rows512<D>(q, dout, Qs[st], Gs[st], qrecs, b * kBlk, tok0, tid, wave);
-        if (wave < 2)
-            dma16(qtb + (size_t)(qb / kBlk) * kQTile + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
+        if (wave < 2 && 1024 * wave + 16 * lane < qts)
+            dma16(qtb + (size_t)(qb / kBlk) * qts + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
     };
     for (int i = 0; i < kKvStages && i < nblocks; ++i)
         issue(i, i);
@@ -964,21 +973,22 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint32_t *sr = srec + (size_t)seg * L;
     const size_t tok0 = (size_t)bh * L;
     const size_t part0 = (size_t)seg * L;
-    const uint8_t *qtb = qtile + (size_t)seg * nblk * kQTile;
-    const uint8_t *ktb = ktile + (size_t)seg * nblk * kKTile;
+    const int kts = ktile_stride(nh), qts = qtile_stride(nh);
+    const uint8_t *qtb = qtile + (size_t)seg * nblk * qts;
+    const uint8_t *ktb = ktile + (size_t)seg * nblk * kts;
     const float inv_sl2 = 1.f / (scale * kLog2e);
 
     // absolute query block a: its rows of q and dO, and its query tile
     auto issue_block = [&](int a) __attribute__((always_inline)) {
         const int st = a % kStreamStages;
         dma_rows512<D>(q, dout, Qs[st], Gs[st], recs + (a * kBlk) % kRecRing, 0, tok0, tid, wave);
-        if (wave < 2)
-            dma16(qtb + (size_t)a * kQTile + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
+        if (wave < 2 && 1024 * wave + 16 * lane < qts)
+            dma16(qtb + (size_t)a * qts + 1024 * wave + 16 * lane, Ts[st] + 1024 * wave);
     };
     // key tiles of tile t into buffer buf (waves 2..5, one 32-row tile each)
     auto issue_ktiles = [&](int t, int buf) __attribute__((always_inline)) {
-        if (wave >= 2 && wave < 6)
-            dma16(ktb + ((size_t)t * (kRows / kBlk) + (wave - 2)) * kKTile + 16 * lane, Kt[buf][wave - 2]);
+        if (wave >= 2 && wave < 6 && 16 * lane < kts)
+            dma16(ktb + ((size_t)t * (kRows / kBlk) + (wave - 2)) * kts + 16 * lane, Kt[buf][wave - 2]);
     };
     // records of rows [row0, row0 + 128) (row0 a multiple of 128), by wave wv
     auto issue_recs = [&](int row0, int wv) __attribute__((always_inline)) {
@@ -1132,14 +1142,15 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const uint32_t *sr = srec + (size_t)seg * L;
     const size_t tok0 = (size_t)bh * L;
     const size_t part0 = (size_t)seg * L;
-    const uint8_t *ktb = ktile + (size_t)seg * nblk * kKTile;
+    const int kts = ktile_stride(nh);
+    const uint8_t *ktb = ktile + (size_t)seg * nblk * kts;
     const float scale_log2 = scale * kLog2e;
 
     auto issue_block = [&](int a) __attribute__((always_inline)) {
         const int st = a % kStreamStages;
         dma_rows512<D>(q, v, Ks[st], Vs[st], recs + (a * kBlk) % kRecRing, 0, tok0, tid, wave);
-        if (wave == 0)
-            dma16(ktb + (size_t)a * kKTile + 16 * lane, Kts[st]);
+        if (wave == 0 && 16 * lane < kts)
+            dma16(ktb + (size_t)a * kts + 16 * lane, Kts[st]);
     };
     auto issue_recs = [&](int row0, int wv) __attribute__((always_inline)) {
         if (wave == wv && lane < kRows / 4)
@@ -1360,7 +1371,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             if (old % 8u == 7u && t + 1 < t_end && a + 8 < nblk) {
                 const int st = (a + 8) % kStreamStages;
                 dma_block_wave<D>(q, v, Ks[st], Vs[st], recs + ((a + 8) * kBlk) % kRecRing, tok0, lane);
-                dma16(ktb + (size_t)(a + 8) * kKTile + 16 * lane, Kts[st]);
+                if (16 * lane < kts)
+                    dma16(ktb + (size_t)(a + 8) * kts + 16 * lane, Kts[st]);
             }
         }
         if (t + 1 < t_end) {
@@ -1564,8 +1576,8 @@ bool mfma_path_ok(const Dims &P, int dtype)
            kRows + 2 * P.m + kBlk <= kRecCache;
 }
 
-size_t mfma_ktile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * kKTile; }
-size_t mfma_qtile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * kQTile; }
+size_t mfma_ktile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * ktile_stride(P.nh); }
+size_t mfma_qtile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * qtile_stride(P.nh); }
 size_t bwd_mfma_part_bytes(const Dims &P) { return 3 * (size_t)P.BH() * P.nh * P.L * P.d * sizeof(uint16_t); }
 
 hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, const int32_t *inv, const int32_t *win_lo,
