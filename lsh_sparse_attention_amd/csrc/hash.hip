@@ -84,6 +84,90 @@ __global__ __launch_bounds__(kHashThreads) void hash_generic(int L, int nh, int 
 constexpr int kHashRows = 256;
 constexpr int kHashCols = 64;              // rotation columns per staged block
 
+// Argmax over [y ; -y] with first-index ties, one tracker per lane and
+// parity of the slot: the key rotl(bits(y'), 1) with y' = -y orders by |y|
+// (bits of |y| on top) and, for equal |y|, puts y > 0 (sign bit of y'
+// set) above y < 0, i.e. the +y half (lower indices) above the -y half;
+// a strictly greater key replaces the tracked one, so the first column
+// wins among equal keys.  Key 0 is y = 0 (never -0: the sums start at +0).
+//
+// acc[ct][4 g + t] = y'[column j0 + 8 g + 4 h + t] of row 32 ct + c.  Within
+// the tile each parity tracker keeps (key, slot offset 8 g + t), the offsets
+// being immediates; the tile result then merges into the round's tracker
+// (strictly greater key: an earlier tile wins ties).  FULL: all 32 columns
+// exist; otherwise columns at or past `half` are skipped.
+template <bool FULL>
+__device__ __forceinline__ void tile_argmax(const f32x16_t (&acc)[2], int j0, int h, int half, uint32_t (&bk)[2][2],
+                                            int (&bi)[2][2])
+{
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        uint32_t tk[2] = {0u, 0u};
+        int ts[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t u = __float_as_uint(acc[ct][e]);
+            const int off = 8 * (e / 4) + (e % 4);
+            uint32_t key = __builtin_amdgcn_alignbit(u, u, 31);
+            if constexpr (!FULL)
+                key = (j0 + off + 4 * h < half) ? key : 0u;
+            const int p = e % 2;
+            ts[p] = key > tk[p] ? off : ts[p];
+            tk[p] = max(tk[p], key);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            bi[ct][p] = tk[p] > bk[ct][p] ? j0 + ts[p] : bi[ct][p];
+            bk[ct][p] = max(bk[ct][p], tk[p]);
+        }
+    }
+}
+
+// End of a round: merge the two slot parities, then the other half of the
+// row (larger key, else smaller column), store the bucket and reset.
+__device__ __forceinline__ void round_store(uint32_t (&bk)[2][2], int (&bi)[2][2], int h, int c, int row0, int L,
+                                            int half, int32_t *__restrict__ out)
+{
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        uint32_t k0 = bk[ct][0], k1 = bk[ct][1];
+        int i0 = bi[ct][0] + 4 * h, i1 = bi[ct][1] + 4 * h;
+        if (k1 > k0 || (k1 == k0 && i1 < i0)) {
+            k0 = k1;
+            i0 = i1;
+        }
+        const auto pk = __builtin_amdgcn_permlane32_swap(k0, k0, false, false);
+        const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i0, (uint32_t)i0, false, false);
+        const uint32_t ok = h ? pk[0] : pk[1];
+        const int oi = (int)(h ? pi[0] : pi[1]);
+        if (ok > k0 || (ok == k0 && oi < i0)) {
+            k0 = ok;
+            i0 = oi;
+        }
+        const int row = row0 + 32 * ct + c;
+        // key 0: every projection is zero and bucket 0 (a +y entry) is the first maximum
+        if (h == 0 && row < L)
+            out[row] = k0 == 0u ? 0 : ((k0 & 1u) ? i0 : half + i0);
+        bk[ct][0] = bk[ct][1] = 0u;
+        bi[ct][0] = bi[ct][1] = 0;
+    }
+}
+
+// A operand of tile jt of a staged block: lane (column 32 jt + c, half h)
+// gets d = 16 ks + 8 h + 0..7, read transposed from the row-major block.
+template <int D, int P>
+__device__ __forceinline__ void read_rot(const uint16_t *Rs, int jt, int grp, int m, bf16x8_t (&aop)[D / 16])
+{
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const int dr = 16 * ks + 8 * (grp / 2) + m / 4;
+        const int col = 32 * jt + 16 * (grp % 2) + 4 * (m % 4);
+        const uint2 x = lds_read_tr16(&Rs[dr * P + col]);
+        const uint2 y = lds_read_tr16(&Rs[(dr + 4) * P + col]);
+        aop[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x.x, x.y, y.x, y.y});
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, int half, const bf16 *__restrict__ q,
                                                                  const bf16 *__restrict__ rot,
@@ -137,12 +221,6 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
         }
     };
 
-    // Argmax over [y ; -y] with first-index ties, one tracker per lane and
-    // parity of the slot: the key rotl(bits(y'), 1) with y' = -y orders by |y|
-    // (bits of |y| on top) and, for equal |y|, puts y > 0 (sign bit of y'
-    // set) above y < 0, i.e. the +y half (lower indices) above the -y half;
-    // a strictly greater key replaces the tracked one, so the first column
-    // wins among equal keys.  Key 0 is y = 0 (never -0: the sums start at +0).
     uint32_t bk[2][2] = {{0u, 0u}, {0u, 0u}};
     int bi[2][2] = {{0, 0}, {0, 0}};
     fetch(0);
@@ -162,16 +240,8 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
             const int j0 = jb + 32 * jt;
             if (j0 >= half)
                 break;
-            // A operand: lane (column j0 + c, half h) gets d = 16 ks + 8 h + 0..7
             bf16x8_t aop[D / 16];
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const int dr = 16 * ks + 8 * (grp / 2) + m / 4;
-                const int col = 32 * jt + 16 * (grp % 2) + 4 * (m % 4);
-                const uint2 x = lds_read_tr16(&Rs[dr * P + col]);
-                const uint2 y = lds_read_tr16(&Rs[(dr + 4) * P + col]);
-                aop[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{x.x, x.y, y.x, y.y});
-            }
+            read_rot<D, P>(Rs, jt, grp, m, aop);
             f32x16_t acc[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
@@ -180,72 +250,126 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
                 for (int ks = 0; ks < D / 16; ++ks)
                     acc[ct] = mfma32(aop[ks], qop[ct][ks], acc[ct]);
             }
-            // acc[4 g + t] = y'[column j0 + 8 g + 4 h + t] of row c.  Within the
-            // tile each parity tracker keeps (key, slot offset 8 g + t), the
-            // offsets being immediates; the tile result then merges into the
-            // round's tracker (strictly greater key: an earlier tile wins ties).
-            const bool full = j0 + 32 <= half;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                uint32_t tk[2] = {0u, 0u};
-                int ts[2] = {0, 0};
-                if (full) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const uint32_t u = __float_as_uint(acc[ct][e]);
-                        const uint32_t key = __builtin_amdgcn_alignbit(u, u, 31);
-                        const int p = e % 2;
-                        ts[p] = key > tk[p] ? 8 * (e / 4) + (e % 4) : ts[p];
-                        tk[p] = max(tk[p], key);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const uint32_t u = __float_as_uint(acc[ct][e]);
-                        const int off = 8 * (e / 4) + (e % 4);
-                        const uint32_t key = (j0 + off + 4 * h < half) ? __builtin_amdgcn_alignbit(u, u, 31) : 0u;
-                        const int p = e % 2;
-                        ts[p] = key > tk[p] ? off : ts[p];
-                        tk[p] = max(tk[p], key);
-                    }
-                }
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    bi[ct][p] = tk[p] > bk[ct][p] ? j0 + ts[p] : bi[ct][p];
-                    bk[ct][p] = max(bk[ct][p], tk[p]);
-                }
-            }
+            if (j0 + 32 <= half)
+                tile_argmax<true>(acc, j0, h, half, bk, bi);
+            else
+                tile_argmax<false>(acc, j0, h, half, bk, bi);
         }
-        if (jb + kHashCols >= half) {
-            // last block of round r
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                // the two slot parities, then the other half of the row:
-                // larger key, else smaller column
-                uint32_t k0 = bk[ct][0], k1 = bk[ct][1];
-                int i0 = bi[ct][0] + 4 * h, i1 = bi[ct][1] + 4 * h;
-                if (k1 > k0 || (k1 == k0 && i1 < i0)) {
-                    k0 = k1;
-                    i0 = i1;
-                }
-                const auto pk = __builtin_amdgcn_permlane32_swap(k0, k0, false, false);
-                const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i0, (uint32_t)i0, false, false);
-                const uint32_t ok = h ? pk[0] : pk[1];
-                const int oi = (int)(h ? pi[0] : pi[1]);
-                if (ok > k0 || (ok == k0 && oi < i0)) {
-                    k0 = ok;
-                    i0 = oi;
-                }
-                const int row = row0 + 32 * ct + c;
-                // key 0: every projection is zero and bucket 0 (a +y entry) is the first maximum
-                if (h == 0 && row < L)
-                    buckets[((size_t)bh * nh + r) * L + row] = k0 == 0u ? 0 : ((k0 & 1u) ? i0 : half + i0);
-                bk[ct][0] = bk[ct][1] = 0u;
-                bi[ct][0] = bi[ct][1] = 0;
-            }
-        }
+        if (jb + kHashCols >= half)   // last block of round r
+            round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + r) * L);
     }
 
+}
+
+// The same computation when every staged block holds 64 full columns
+// (half % 64 == 0), software-pipelined within the wave: the matrix-core
+// products of a tile are issued interleaved with the argmax of the tile
+// before it (its accumulators are a second register set), so the vector ALU
+// work runs while the matrix core is busy instead of after it.  The argmax
+// of a block's last tile runs under the next block's first tile; a round is
+// stored once its last tile's argmax is done.  The staged blocks alternate
+// between two LDS buffers, so one barrier per block suffices: block b + 1
+// is written while block b is read.
+template <int D>
+__global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int nh, int half,
+                                                                      const bf16 *__restrict__ q,
+                                                                      const bf16 *__restrict__ rot,
+                                                                      int32_t *__restrict__ buckets)
+{
+    constexpr int COLS = kHashCols, P = COLS + 8;
+    constexpr int NT = COLS / 32;   // tiles per block (even: they alternate between two accumulator sets)
+    __shared__ __align__(16) uint16_t Rs[2][D * P];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int h = lane / 32, c = lane % 32, grp = lane / 16, m = lane % 16;
+    const int bh = blockIdx.y;
+    const int row0 = blockIdx.x * kHashRows + wave * 64;
+
+    bf16x8_t qop[2][D / 16];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const int row = min(row0 + 32 * ct + c, L - 1);
+        const bf16 *qrow = q + ((size_t)bh * L + row) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            qop[ct][ks] = as_bf16x8(ld16(qrow + 16 * ks + 8 * h) ^ 0x80008000u);   // -q, as above
+    }
+    const uint16_t *Rbits = reinterpret_cast<const uint16_t *>(rot);
+    constexpr int CPR = COLS / 8;                          // 16-byte chunks per staged row
+    constexpr int kItems = D * CPR / kHashThreads;
+    const int nblk = half / COLS, total = nh * nblk;
+    u32x4_t pre[kItems];
+    auto fetch = [&](int blk) __attribute__((always_inline)) {
+        const uint16_t *R = Rbits + (size_t)(blk / nblk) * D * half + (blk % nblk) * COLS;
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = tid + it * kHashThreads;
+            pre[it] = ld16(R + (size_t)(i / CPR) * half + 8 * (i % CPR));
+        }
+    };
+    auto stage = [&](uint16_t *buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+            const int i = tid + it * kHashThreads;
+            st16(&buf[(i / CPR) * P + 8 * (i % CPR)], pre[it]);
+        }
+    };
+    // one product, then a share of the other tile's argmax, sixteen times
+    auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2 * (D / 16); ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+    };
+    auto products = [&](const uint16_t *buf, int jt, f32x16_t (&acc)[2]) __attribute__((always_inline)) {
+        bf16x8_t aop[D / 16];
+        read_rot<D, P>(buf, jt, grp, m, aop);
+        acc[0] = acc[1] = f32x16_t{};
+        // the two accumulator chains alternate
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                acc[ct] = mfma32(aop[ks], qop[ct][ks], acc[ct]);
+    };
+
+    uint32_t bk[2][2] = {{0u, 0u}, {0u, 0u}};
+    int bi[2][2] = {{0, 0}, {0, 0}};
+    // accumulators of the previous block's last tile; zero keys change nothing
+    f32x16_t acc0[2], acc1[2] = {f32x16_t{}, f32x16_t{}};
+    int prev_j = 0, prev_r = 0;   // first column and round of that tile
+    bool prev_last = false;       // it ended its round
+    fetch(0);
+    stage(Rs[0]);
+    if (total > 1)
+        fetch(1);
+    for (int blk = 0; blk < total; ++blk) {
+        const int r = blk / nblk, jb = (blk % nblk) * COLS;
+        const uint16_t *buf = Rs[blk % 2];
+        // block blk is staged, and every wave is done with the other buffer
+        __syncthreads();
+        if (blk + 1 < total) {
+            stage(Rs[(blk + 1) % 2]);
+            if (blk + 2 < total)
+                fetch(blk + 2);
+        }
+#pragma unroll
+        for (int jt = 0; jt < NT; jt += 2) {
+            products(buf, jt, acc0);
+            tile_argmax<true>(acc1, jt == 0 ? prev_j : jb + 32 * (jt - 1), h, half, bk, bi);
+            interleave();
+            if (jt == 0 && prev_last)
+                round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
+            products(buf, jt + 1, acc1);
+            tile_argmax<true>(acc0, jb + 32 * jt, h, half, bk, bi);
+            interleave();
+        }
+        prev_j = jb + COLS - 32;
+        prev_r = r;
+        prev_last = jb + COLS == half;
+    }
+    tile_argmax<true>(acc1, prev_j, h, half, bk, bi);
+    round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
 }
 
 template <int D>
@@ -253,8 +377,12 @@ hipError_t go_mfma(const Dims &P, const void *q, const void *rot, int32_t *bucke
 {
     dim3 grid((P.L + kHashRows - 1) / kHashRows, P.BH());
     ProfScope prof(LSH_KERNEL_HASH, st);
-    hipLaunchKernelGGL((hash_mfma_kernel<D>), grid, dim3(kHashThreads), 0, st, P.L, P.nh, P.nb / 2,
-                       (const bf16 *)q, (const bf16 *)rot, buckets);
+    if ((P.nb / 2) % kHashCols == 0)
+        hipLaunchKernelGGL((hash_mfma_pipe_kernel<D>), grid, dim3(kHashThreads), 0, st, P.L, P.nh, P.nb / 2,
+                           (const bf16 *)q, (const bf16 *)rot, buckets);
+    else
+        hipLaunchKernelGGL((hash_mfma_kernel<D>), grid, dim3(kHashThreads), 0, st, P.L, P.nh, P.nb / 2,
+                           (const bf16 *)q, (const bf16 *)rot, buckets);
     return hipGetLastError();
 }
 

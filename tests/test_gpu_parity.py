@@ -40,6 +40,9 @@ SMALL = [
     ("bf16-runs", 1, 4, 8192, 64, 128, 2, 128, "bf16", False),
     ("bf16-m1", 1, 2, 512, 64, 8, 2, 1, "bf16", False),
     ("bf16-nh16", 1, 1, 512, 64, 16, 16, 32, "bf16", False),
+    ("bf16-hash-d128", 1, 2, 1024, 128, 256, 3, 64, "bf16", False),
+    ("bf16-hash-d32", 1, 1, 1024, 32, 128, 2, 32, "bf16", False),
+    ("bf16-hash-ragged", 1, 1, 1000, 64, 128, 2, 8, "bf16", False),
 ]
 
 
