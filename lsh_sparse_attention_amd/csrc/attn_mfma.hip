@@ -1113,7 +1113,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // blocks (and the next tile's query rows are loaded into registers) while
 // the tile's own four blocks are worked on.
 
-template <int D, bool BWD>
+template <int D, bool BWD, int NR>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(
     int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dvec,
@@ -1124,8 +1124,11 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint8_t Kts[kStreamStages][kKTile];
     __shared__ __align__(16) uint32_t recs[kRecRing];
-    __shared__ uint32_t qm[kKvThreads / kWave][kMaxEarlier][16];   // earlier-round records of the queries
     __shared__ uint32_t rel[kStreamStages];   // waves through a stage's block, 8 per tile
+    // with more than seven earlier rounds the queries' records of those
+    // rounds wait in LDS during a tile rather than in registers
+    constexpr bool kKeepWin = NR <= 7;
+    __shared__ uint32_t qmL[kKeepWin ? 1 : kKvThreads / kWave][kKeepWin ? 1 : NR][16];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int g = lane / 16, c = lane % 16;
@@ -1160,7 +1163,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // this lane's query of tile t (16 per wave) in registers
     struct QRegs {
         bf16x8_t qop[D / 32], gop[D / 32];
-        uint32_t qm[kMaxEarlier];
+        uint32_t qm[NR];   // the query's records in the earlier rounds (NR >= r)
         int qpos, qw;
         float lse2, Di;
     };
@@ -1181,7 +1184,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             R.Di = Dvec[tok];
         }
 #pragma unroll
-        for (int rr = 0; rr < kMaxEarlier; ++rr)
+        for (int rr = 0; rr < NR; ++rr)
             if (rr < r)
                 R.qm[rr] = meta[tok * nh + rr];
     };
@@ -1235,11 +1238,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             finish(qpos_prev);
             cur = nxt;
         }
-        if (g == 0) {
+        if constexpr (!kKeepWin) {
+            if (g == 0) {
 #pragma unroll
-            for (int rr = 0; rr < kMaxEarlier; ++rr)
-                if (rr < r)
-                    qm[wave][rr][c] = cur.qm[rr];
+                for (int rr = 0; rr < NR; ++rr)
+                    if (rr < r)
+                        qmL[wave][rr][c] = cur.qm[rr];
+            }
         }
         block_barrier();
 #pragma unroll
@@ -1253,6 +1258,18 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int qlo = sq - cur.qw;
         const int wlo = __builtin_amdgcn_readlane(qlo, 0);   // window starts do not decrease
 
+        // earlier-round window tests: (start - 1, length) of the query's set
+        // in round rr, both halves of a packed pair (kept for up to seven
+        // rounds, formed per block from LDS beyond that)
+        uint32_t si1p[kKeepWin ? NR : 1], wp[kKeepWin ? NR : 1];
+        if constexpr (kKeepWin) {
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr) {
+                si1p[rr] = bcast16(rec_lo(cur.qm[rr]) - 1u);
+                wp[rr] = bcast16(rec_hi(cur.qm[rr]));
+            }
+        }
+
         auto work = [&](int a) __attribute__((always_inline)) {
             const int kb = a * kBlk, st = a % kStreamStages;
             if (kb > wq0 + 14 || kb + kBlk - 1 < wlo)
@@ -1260,6 +1277,12 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const uint16_t *K = Ks[st], *V = Vs[st];
             const float *rnk = reinterpret_cast<const float *>(Kts[st]);
             const uint16_t *skm = reinterpret_cast<const uint16_t *>(Kts[st] + 128);
+            // The LDS reads of the block are issued here, before any of the
+            // arithmetic, so the block waits for LDS once (register space
+            // permitting: the dq kernel reads K^T after the softmax, and with
+            // more than seven earlier rounds their key indices are read in the
+            // mask loop).
+            constexpr bool kEarlyTr = !BWD, kEarlySk = NR <= (BWD ? 3 : 7);
             // S^T = K Q^T (and dP^T = V dO^T): lane (query c, group g) gets keys 16 kk + 4 g + t
             bf16x8_t ka[2][D / 32], va[2][D / 32];
 #pragma unroll
@@ -1270,6 +1293,37 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                     if constexpr (BWD)
                         va[kk][ks] = tile_row<D>(V, 16 * kk + c, 32 * ks + 8 * g);
                 }
+            float4 rn4[2];   // rn * scale * log2(e) of the lane's keys
+            auto read_rn = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    rn4[kk] = *reinterpret_cast<const float4 *>(rnk + 16 * kk + 4 * g);
+            };
+            if constexpr (kEarlySk)
+                read_rn();
+            // the keys' sorted indices in the earlier rounds
+            auto read_sk = [&](int rr, int kk) __attribute__((always_inline)) {
+                return *reinterpret_cast<const uint2 *>(skm + 32 * rr + 16 * kk + 4 * g);
+            };
+            uint2 kp[kEarlySk ? NR : 1][2];
+            if constexpr (kEarlySk) {
+#pragma unroll
+                for (int rr = 0; rr < NR; ++rr)
+                    if (rr < r) {
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+                            kp[rr][kk] = read_sk(rr, kk);
+                    }
+            }
+            // the operand of the second product: V^T (forward) or K^T (dq)
+            bf16x8_t tr[D / 16];
+            auto read_tr = [&]() __attribute__((always_inline)) {
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+                    tr[dt] = tile_tr16x<D>(BWD ? K : V, 16 * dt, lane);
+            };
+            if constexpr (kEarlyTr)
+                read_tr();
             __builtin_amdgcn_sched_barrier(0);
             f32x4_t sacc[2], pacc[2];
 #pragma unroll
@@ -1289,25 +1343,29 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 ok[e] = (unsigned)(kb + 16 * (e / 4) + 4 * g + (e % 4) - qlo) < (unsigned)cur.qw;
             if (r > 0) {
                 uint32_t hit[4] = {0u, 0u, 0u, 0u};
-                for (int rr = 0; rr < r; ++rr) {
-                    const uint32_t qmr = qm[wave][rr][c];
-                    const uint32_t si1p = bcast16(rec_lo(qmr) - 1u), wp = bcast16(rec_hi(qmr));
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const uint2 kp = *reinterpret_cast<const uint2 *>(skm + 32 * rr + 16 * kk + 4 * g);
-                        hit[2 * kk] |= win_hits2(si1p, wp, kp.x);
-                        hit[2 * kk + 1] |= win_hits2(si1p, wp, kp.y);
+                for (int rr = 0; rr < NR; ++rr)
+                    if (rr < r) {
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk) {
+                            const uint2 k2 = kEarlySk ? kp[kEarlySk ? rr : 0][kk] : read_sk(rr, kk);
+                            const uint32_t qmr = kKeepWin ? 0u : qmL[kKeepWin ? 0 : wave][kKeepWin ? 0 : rr][c];
+                            const uint32_t s1 = kKeepWin ? si1p[kKeepWin ? rr : 0] : bcast16(rec_lo(qmr) - 1u);
+                            const uint32_t w1 = kKeepWin ? wp[kKeepWin ? rr : 0] : bcast16(rec_hi(qmr));
+                            hit[2 * kk] |= win_hits2(s1, w1, k2.x);
+                            hit[2 * kk + 1] |= win_hits2(s1, w1, k2.y);
+                        }
                     }
-                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
             }
+            if constexpr (!kEarlySk)
+                read_rn();
             float x[8];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const float4 rn4 = *reinterpret_cast<const float4 *>(rnk + 16 * kk + 4 * g);
-                const float rn[4] = {rn4.x, rn4.y, rn4.z, rn4.w};   // rn * scale * log2(e)
+                const float rn[4] = {rn4[kk].x, rn4[kk].y, rn4[kk].z, rn4[kk].w};
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const int e = 4 * kk + tt;
@@ -1347,11 +1405,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
             // O^T += V^T P^T, or dQ^T += K^T G^T: B slot s is value s of x
             const bf16x8_t xb = pack8(x);
-            bf16x8_t tr[D / 16];
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-                tr[dt] = tile_tr16x<D>(BWD ? K : V, 16 * dt, lane);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!kEarlyTr) {
+                read_tr();
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
                 acc[dt] = mfma16(tr[dt], xb, acc[dt]);
@@ -1475,18 +1532,38 @@ int stream_run_tiles(int nt, int segs)
 // than 2 m; rounded up to whole blocks.
 int max_window(const Dims &P) { return (2 * P.m + kBlk - 1) / kBlk * kBlk; }
 
+// The query-side stream kernel for the bound NR on the earlier rounds
+// (n_hashes - 1 rounded up to 1, 3, 7 or 13).
+template <int D, bool BWD>
+void q_stream_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
+                 const uint32_t *meta, const uint32_t *srec, const uint8_t *ktile, void *out, float *lse_rounds,
+                 hipStream_t st)
+{
+    const int nt = P.L / kRows, segs = P.BH() * P.nh;
+    const int T = stream_run_tiles(nt, segs);
+    const dim3 grid(segs * ((nt + T - 1) / T));
+#define LSH_QSTREAM(NR)                                                                                           \
+    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,       \
+                       (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile, (bf16 *)out, \
+                       lse_rounds)
+    if (P.nh <= 2)
+        LSH_QSTREAM(1);
+    else if (P.nh <= 4)
+        LSH_QSTREAM(3);
+    else if (P.nh <= 8)
+        LSH_QSTREAM(7);
+    else
+        LSH_QSTREAM(13);
+#undef LSH_QSTREAM
+}
+
 template <int D>
 hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
                   const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     ProfScope prof(LSH_KERNEL_FWD, st);
     if (kRows % P.m == 0) {
-        const int nt = P.L / kRows, segs = P.BH() * P.nh;
-        const int T = stream_run_tiles(nt, segs);
-        hipLaunchKernelGGL((q_stream_kernel<D, false>), dim3(segs * ((nt + T - 1) / T)), dim3(kKvThreads), 0, st, P.L,
-                           P.nh, T, P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)nullptr,
-                           (const float *)nullptr, (const float *)nullptr, meta, srec, ktile, (bf16 *)o_rounds,
-                           lse_rounds);
+        q_stream_go<D, false>(P, q, v, nullptr, nullptr, nullptr, meta, srec, ktile, o_rounds, lse_rounds, st);
     } else {
         hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
                            max_window(P), P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile,
@@ -1506,11 +1583,7 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         if (kRows % P.m == 0) {
-            const int nt = P.L / kRows, segs = P.BH() * P.nh;
-            const int T = stream_run_tiles(nt, segs);
-            hipLaunchKernelGGL((q_stream_kernel<D, true>), dim3(segs * ((nt + T - 1) / T)), dim3(kKvThreads), 0, st,
-                               P.L, P.nh, T, P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv,
-                               meta, srec, ktile, dq_part, (float *)nullptr);
+            q_stream_go<D, true>(P, q, v, dout, lse, Dv, meta, srec, ktile, dq_part, nullptr, st);
         } else {
             hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, max_window(P), P.scale,
                                (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile,

@@ -43,6 +43,9 @@ SMALL = [
     ("bf16-hash-d128", 1, 2, 1024, 128, 256, 3, 64, "bf16", False),
     ("bf16-hash-d32", 1, 1, 1024, 32, 128, 2, 32, "bf16", False),
     ("bf16-hash-ragged", 1, 1, 1000, 64, 128, 2, 8, "bf16", False),
+    ("bf16-nh12-d128", 1, 1, 1024, 128, 32, 12, 64, "bf16", False),
+    ("bf16-nh10-d64", 1, 2, 512, 64, 16, 10, 32, "bf16", False),
+    ("bf16-nh6", 1, 1, 1024, 128, 64, 6, 128, "bf16", False),
 ]
 
 
