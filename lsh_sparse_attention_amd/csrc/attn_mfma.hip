@@ -845,11 +845,21 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 constexpr int kStreamStages = 8;
 constexpr int kRecRing = 512;                 // records of sorted rows x at x mod 512
 
-template <int D>
+// Whether the key's sorted indices in the NR earlier rounds stay in
+// registers for a tile (else they are read from the key tile per block).
+template <int D, int NR>
+constexpr bool kv_sk_in_regs() { return D < 128 || NR <= 3; }
+
+// One query block against this wave's 16 keys.  The queries' windows, lse
+// and D are read with the operand rows, before any arithmetic.  skp[rr]:
+// this lane's key's sorted index in round rr (NR >= r), both halves of a
+// pair, or (see kv_sk_in_regs) entry ke of the key tile kt.
+template <int D, int NR>
 __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt, const uint8_t *T, const uint8_t *kt,
                                           int ke, int r, int qb, int sk, int g, int c, int lane, float krn2,
-                                          float scale, const bf16x8_t (&kop)[D / 32], const bf16x8_t (&vop)[D / 32],
-                                          f32x4_t (&dka)[D / 16], f32x4_t (&dva)[D / 16])
+                                          float scale, const uint32_t (&skp)[NR], const bf16x8_t (&kop)[D / 32],
+                                          const bf16x8_t (&vop)[D / 32], f32x4_t (&dka)[D / 16],
+                                          f32x4_t (&dva)[D / 16])
 {
     const float *qlse2 = reinterpret_cast<const float *>(T);
     const float *qD = reinterpret_cast<const float *>(T + 128);
@@ -862,6 +872,14 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
             qa[u][ks] = tile_row<D>(Qt, 16 * u + c, 32 * ks + 8 * g);
             ga[u][ks] = tile_row<D>(Gt, 16 * u + c, 32 * ks + 8 * g);
         }
+    uint2 w4[2];
+    float4 l4[2], d4[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        w4[u] = *reinterpret_cast<const uint2 *>(qwv + 16 * u + 4 * g);
+        l4[u] = *reinterpret_cast<const float4 *>(qlse2 + 16 * u + 4 * g);
+        d4[u] = *reinterpret_cast<const float4 *>(qD + 16 * u + 4 * g);
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x4_t sacc[2], pacc[2];
 #pragma unroll
@@ -876,8 +894,8 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
     bool ok[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const uint2 w4 = *reinterpret_cast<const uint2 *>(qwv + 16 * u + 4 * g);
-        const int wv[4] = {(int)(w4.x & 0xffffu), (int)(w4.x >> 16), (int)(w4.y & 0xffffu), (int)(w4.y >> 16)};
+        const int wv[4] = {(int)(w4[u].x & 0xffffu), (int)(w4[u].x >> 16), (int)(w4[u].y & 0xffffu),
+                           (int)(w4[u].y >> 16)};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int sq = qb + 16 * u + 4 * g + t;   // key in [sq - w, sq)
@@ -886,17 +904,22 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
     }
     if (r > 0) {
         uint32_t hit[4] = {0u, 0u, 0u, 0u};
-        for (int rr = 0; rr < r; ++rr) {
-            const uint32_t skp = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
-            const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
-                const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
-                hit[2 * u] |= win_hits2(a.x, ww.x, skp);
-                hit[2 * u + 1] |= win_hits2(a.y, ww.y, skp);
+        for (int rr = 0; rr < NR; ++rr)
+            if (rr < r) {
+                const uint32_t kp = kv_sk_in_regs<D, NR>()
+                                        ? skp[rr]
+                                        : bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
+                // the queries' (start - 1, length) pairs in round rr
+                const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
+                    const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                    hit[2 * u] |= win_hits2(a.x, ww.x, kp);
+                    hit[2 * u + 1] |= win_hits2(a.y, ww.y, kp);
+                }
             }
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
@@ -904,9 +927,7 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
     float pr[8], gr[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const float4 l4 = *reinterpret_cast<const float4 *>(qlse2 + 16 * u + 4 * g);
-        const float4 d4 = *reinterpret_cast<const float4 *>(qD + 16 * u + 4 * g);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lv[4] = {l4[u].x, l4[u].y, l4[u].z, l4[u].w}, dv[4] = {d4[u].x, d4[u].y, d4[u].z, d4[u].w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int e = 4 * u + t;
@@ -947,7 +968,7 @@ __device__ __forceinline__ void dkv_store(bf16 *dkr_part, bf16 *dv_part, size_t 
     }
 }
 
-template <int D>
+template <int D, int NR>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_stream_kernel(
     int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
@@ -1043,6 +1064,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int ke = 16 * (kg % 2) + c;
         const float krn2 = reinterpret_cast<const float *>(kt)[ke];   // rn * scale * log2(e)
         const float rn = krn2 * inv_sl2;
+        uint32_t skp[NR];   // the key's sorted index in the earlier rounds
+        if constexpr (kv_sk_in_regs<D, NR>()) {
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr)
+                if (rr < r)
+                    skp[rr] = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
+        }
         bf16x8_t kop[D / 32];
         {
             const uint16_t *Kq = Qs[(a0 + kg / 2) % kStreamStages];
@@ -1061,7 +1089,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const int blk_lo = qb - (int)rec_hi(recs[qb % kRecRing]);
             if (qb + kBlk - 1 <= wk0 || blk_lo > wk0 + 15)
                 return;
-            dkv_block<D>(Qs[st], Gs[st], Ts[st], kt, ke, r, qb, sk, g, c, lane, krn2, scale, kop, vop, dka, dva);
+            dkv_block<D, NR>(Qs[st], Gs[st], Ts[st], kt, ke, r, qb, sk, g, c, lane, krn2, scale, skp, kop, vop, dka,
+                             dva);
         };
         for (int b = 0; b < 4 && b < nb; ++b)
             work(b);
@@ -1599,9 +1628,18 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
             const int nt = P.L / kRows, segs = P.BH() * P.nh;
             const int T = stream_run_tiles(nt, segs);
             const int runs = segs * ((nt + T - 1) / T);
-            hipLaunchKernelGGL((dkv_stream_kernel<D>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,
-                               (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part,
-                               dv_part);
+#define LSH_DKV(NR)                                                                                       \
+    hipLaunchKernelGGL((dkv_stream_kernel<D, NR>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,   \
+                       (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part, dv_part)
+            if (P.nh <= 2)
+                LSH_DKV(1);
+            else if (P.nh <= 4)
+                LSH_DKV(3);
+            else if (P.nh <= 8)
+                LSH_DKV(7);
+            else
+                LSH_DKV(13);
+#undef LSH_DKV
         } else {
             hipLaunchKernelGGL((dkv_kernel<D>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
                                (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part, dv_part);
