@@ -50,6 +50,9 @@ KERNEL_SOURCE = {
 def algorithmic_work(name: str, cfg, backward_prep: bool = True) -> tuple[float, float]:
     """(flops, bytes) that one launch of kernel `name` must do for `cfg`.
 
+    prep and tiles run twice per training step; backward_prep selects the
+    backward's launch (the one a step's timing of those kernels ends on).
+
     Bytes count every input a kernel needs read once and every output written
     once (row gathers by position count their rows once per round; a
     per-round result is written once).  Flops count the method's dense chunk
@@ -72,10 +75,17 @@ def algorithmic_work(name: str, cfg, backward_prep: bool = True) -> tuple[float,
         return 0.0, 4 * S * ntiles * nb * 4 + S * nb * 4
     if name == "sort_scatter":
         return 0.0, Tr * 4 + S * ntiles * nb * 4 + Tr * 12
-    if name == "prep":   # backward prep: q for norms, out and dout for D; records in/out
-        return 0.0, T * d * s * (3 if backward_prep else 1) + Tr * 16 + T * 8
-    if name == "tiles":  # backward tiles: key and query tiles per 32 sorted rows
-        return 0.0, Tr * (4 + meta + 12) + Tr * (32 + 64)
+    qtile_row = ((320 + 128 * (nh - 1) + 255) & ~255) // 32   # stored query-tile bytes per sorted row
+    ktile_row = ((128 + 64 * (nh - 1) + 255) & ~255) // 32    # stored key-tile bytes per sorted row
+    if name == "prep":
+        if backward_prep:   # backward on the forward's records: out and dout in, D out
+            return 0.0, 2 * T * d * s + T * 4
+        # forward: q for the norms, inv and win_lo in; packed records (both orders) and norms out
+        return 0.0, T * d * s + Tr * 8 + Tr * 8 + T * 4
+    if name == "tiles":
+        if backward_prep:   # query tiles: sorted record, the row's meta, lse and D gathered; tile written
+            return 0.0, Tr * (4 + meta + 8) + Tr * qtile_row
+        return 0.0, Tr * (4 + meta + 4) + Tr * ktile_row
     if name == "attn_fwd":   # q, v rows; o row and lse written
         return 2.0 * 2 * d * pairs, Tr * (3 * d * s + 4 + 4 + 32)
     if name == "combine":
