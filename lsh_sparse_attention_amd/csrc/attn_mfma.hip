@@ -1189,9 +1189,11 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             dma16(sr + row0 + 4 * lane, recs + row0 % kRecRing);
     };
 
-    // this lane's query of tile t (16 per wave) in registers
+    // this lane's query of tile t (16 per wave) in registers; its q row is
+    // not among them: the tile's own key blocks hold the query rows (shared
+    // QK), so the operand is read from LDS once the tile's blocks are in
     struct QRegs {
-        bf16x8_t qop[D / 32], gop[D / 32];
+        bf16x8_t gop[D / 32];
         uint32_t qm[NR];   // the query's records in the earlier rounds (NR >= r)
         int qpos, qw;
         float lse2, Di;
@@ -1202,9 +1204,6 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         R.qpos = (int)rec_lo(rec);
         R.qw = (int)rec_hi(rec);
         const size_t tok = tok0 + R.qpos;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            R.qop[ks] = as_bf16x8(ld16(q + tok * D + 32 * ks + 8 * g));
         if constexpr (BWD) {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
@@ -1276,6 +1275,11 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
         }
         block_barrier();
+        // query operand: rows 16 (qg % 2) + c of own block a0 + qg / 2
+        bf16x8_t qop[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            qop[ks] = tile_row<D>(Ks[(a0 + qg / 2) % kStreamStages], 16 * (qg % 2) + c, 32 * ks + 8 * g);
 #pragma unroll
         for (int dt = 0; dt < NA; ++dt)
             acc[dt] = f32x4_t{};
@@ -1361,7 +1365,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 pacc[kk] = f32x4_t{};
 #pragma unroll
                 for (int ks = 0; ks < D / 32; ++ks) {
-                    sacc[kk] = mfma16(ka[kk][ks], cur.qop[ks], sacc[kk]);
+                    sacc[kk] = mfma16(ka[kk][ks], qop[ks], sacc[kk]);
                     if constexpr (BWD)
                         pacc[kk] = mfma16(va[kk][ks], cur.gop[ks], pacc[kk]);
                 }
