@@ -160,15 +160,20 @@ __device__ __forceinline__ void dma_rows(const bf16 *__restrict__ a, const bf16 
 // rec[kb + row] is the sorted record of streamed row kb + row (kb relative to the cache start)
 {
     constexpr int CPR = D / 8, KPT = D / 64;
+    // every record first: the copies are asm statements that LDS reads cannot move past
+    size_t off[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         const int qc = i * kThreads + tid;            // linear 16-byte chunk of the tile
         const int row = qc / CPR, p = qc % CPR;
         const int lc = p ^ (row & (CPR - 1));         // logical chunk stored at physical p
-        const size_t off = (tok0 + rec_lo(rec[kb + row])) * D + lc * 8;
+        off[i] = (tok0 + rec_lo(rec[kb + row])) * D + lc * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
         const int base = (i * kThreads + wave * kWave) * 8;   // elements
-        dma16(a + off, A + base);
-        dma16(b + off, B + base);
+        dma16(a + off[i], A + base);
+        dma16(b + off[i], B + base);
     }
 }
 
@@ -605,18 +610,22 @@ __device__ __forceinline__ void dma_rows512(const bf16 *__restrict__ a, const bf
                                             uint16_t *B, const uint32_t *rec, int qb, size_t tok0, int tid, int wave)
 {
     constexpr int CPR = D / 8, PER = 8 * D / kKvThreads, TCH = 4 * D;
+    size_t off[PER];   // records first (see dma_rows)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int cc = (i * kKvThreads + tid) % TCH;
+        const int row = cc / CPR, p = cc % CPR;
+        const int lc = p ^ (row & (CPR - 1));
+        off[i] = (tok0 + rec_lo(rec[qb + row])) * D + lc * 8;
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int qc = i * kKvThreads + tid;
-        const int which = qc / TCH, cc = qc % TCH;
-        const int row = cc / CPR, p = cc % CPR;
-        const int lc = p ^ (row & (CPR - 1));
-        const size_t off = (tok0 + rec_lo(rec[qb + row])) * D + lc * 8;
         const int base = ((i * kKvThreads + wave * kWave) % TCH) * 8;
-        if (which == 0)
-            dma16(a + off, A + base);
+        if (qc / TCH == 0)
+            dma16(a + off[i], A + base);
         else
-            dma16(b + off, B + base);
+            dma16(b + off[i], B + base);
     }
 }
 
@@ -627,14 +636,18 @@ __device__ __forceinline__ void dma_block_wave(const bf16 *__restrict__ a, const
                                                uint16_t *B, const uint32_t *rec, size_t tok0, int lane)
 {
     constexpr int CPR = D / 8, N = kBlk * CPR / kWave;
+    size_t off[N];   // records first (see dma_rows)
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const int qc = i * kWave + lane;
         const int row = qc / CPR, p = qc % CPR;
         const int lc = p ^ (row & (CPR - 1));
-        const size_t off = (tok0 + rec_lo(rec[row])) * D + lc * 8;
-        dma16(a + off, A + i * kWave * 8);
-        dma16(b + off, B + i * kWave * 8);
+        off[i] = (tok0 + rec_lo(rec[row])) * D + lc * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        dma16(a + off[i], A + i * kWave * 8);
+        dma16(b + off[i], B + i * kWave * 8);
     }
 }
 
