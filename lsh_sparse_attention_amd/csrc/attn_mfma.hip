@@ -629,6 +629,26 @@ __device__ __forceinline__ void dma_rows512(const bf16 *__restrict__ a, const bf
     }
 }
 
+// One wave loads one tensor of a block: rows [0, 32) of a (positions from
+// rec) into the swizzled tile A, D/16 instructions.
+template <int D>
+__device__ __forceinline__ void dma_tensor_wave(const bf16 *__restrict__ a, uint16_t *A, const uint32_t *rec,
+                                                size_t tok0, int lane)
+{
+    constexpr int CPR = D / 8, N = kBlk * CPR / kWave;
+    size_t off[N];   // records first (see dma_rows)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int qc = i * kWave + lane;
+        const int row = qc / CPR, p = qc % CPR;
+        const int lc = p ^ (row & (CPR - 1));
+        off[i] = (tok0 + rec_lo(rec[row])) * D + lc * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        dma16(a + off[i], A + i * kWave * 8);
+}
+
 // One wave loads a whole block: rows [0, 32) of tensors a and b (positions
 // from rec) into the swizzled tiles A and B, D/16 instructions per tensor.
 template <int D>
@@ -1166,7 +1186,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint8_t Kts[kStreamStages][kKTile];
     __shared__ __align__(16) uint32_t recs[kRecRing];
-    __shared__ uint32_t rel[kStreamStages];   // waves through a stage's block, 8 per tile
+    __shared__ uint32_t through;   // waves through the earlier blocks of their tile, 8 per tile
     // with more than seven earlier rounds the queries' records of those
     // rounds wait in LDS during a tile rather than in registers
     constexpr bool kKeepWin = NR <= 7;
@@ -1232,7 +1252,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // prologue: records [s0 - 128, s0 + 256), then the first tile's eight blocks and query rows
     if (tid < kStreamStages)
-        rel[tid] = 0u;
+        through = 0u;
     {
         const int s0 = t_begin * kRows;
         if (s0 >= kRows)
@@ -1460,31 +1480,53 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 acc[dt] = mfma16(tr[dt], xb, acc[dt]);
         };
 
-        // The earlier blocks: once every wave is through block a, its stage
-        // takes block a + 8 (the next tile's own rows), loaded by the wave
-        // that released it last, so the next tile's loads start as early as
-        // the stages allow and no wave waits for another here.
-        for (int a = a0 - 4; a < a0; ++a) {
+        // The earlier blocks first.  Once every wave is through them, their
+        // stages take the next tile's four new blocks (its own rows), each
+        // wave loading one tensor of one block: the wave that completes the
+        // count at once, the others at their next check (after each of their
+        // own blocks, and at the latest before the tile's end), so the loads
+        // start early and no wave carries all of them.
+        for (int a = a0 - 4; a < a0; ++a)
             if (a >= 0)
                 work(a);
+        const uint32_t goal = 8u * (uint32_t)(t - t_begin + 1);
+        bool pending = t + 1 < t_end;
+        auto issue_share = [&]() __attribute__((always_inline)) {
+            const int a = a0 + 4 + wave / 2, st = a % kStreamStages;
+            if (a < nblk) {
+                dma_tensor_wave<D>(wave % 2 ? v : q, wave % 2 ? Vs[st] : Ks[st], recs + (a * kBlk) % kRecRing, tok0,
+                                   lane);
+                if (wave % 2 == 0 && 16 * lane < kts)
+                    dma16(ktb + (size_t)a * kts + 16 * lane, Kts[st]);
+            }
+            pending = false;
+        };
+        auto check = [&]() __attribute__((always_inline)) {
+            if (pending && *(volatile LDS_AS uint32_t *)(LDS_AS uint32_t *)&through >= goal)
+                issue_share();
+        };
+        {
             uint32_t old = 0u;
             if (lane == 0)
-                old = atomicAdd(&rel[(a + 8) % kStreamStages], 1u);
+                old = atomicAdd(&through, 1u);
             old = __builtin_amdgcn_readfirstlane(old);
-            if (old % 8u == 7u && t + 1 < t_end && a + 8 < nblk) {
-                const int st = (a + 8) % kStreamStages;
-                dma_block_wave<D>(q, v, Ks[st], Vs[st], recs + ((a + 8) * kBlk) % kRecRing, tok0, lane);
-                if (16 * lane < kts)
-                    dma16(ktb + (size_t)(a + 8) * kts + 16 * lane, Kts[st]);
-            }
+            if (pending && old + 1u == goal)
+                issue_share();
         }
         if (t + 1 < t_end) {
             load_q(t + 1, nxt);
             if (s0 + 2 * kRows < L)
                 issue_recs(s0 + 2 * kRows, 6);
         }
-        for (int a = a0; a < a0 + 4; ++a)
+        for (int a = a0; a < a0 + 4; ++a) {
             work(a);
+            check();
+        }
+        // every wave reaches the count above without waiting, so this ends
+        while (pending) {
+            __builtin_amdgcn_s_sleep(1);
+            check();
+        }
         qpos_prev = cur.qpos;
     }
     finish(qpos_prev);
