@@ -51,6 +51,14 @@ constexpr int kQTile = 2048;              // query tile: lse2[32], D[32] f32, w[
 __host__ __device__ constexpr int ktile_stride(int nh) { return (128 + 64 * (nh - 1) + 255) & ~255; }
 __host__ __device__ constexpr int qtile_stride(int nh) { return (320 + 128 * (nh - 1) + 255) & ~255; }
 static_assert(ktile_stride(kMaxEarlier + 1) <= kKTile && qtile_stride(kMaxEarlier + 1) <= kQTile, "tile sizes");
+// Per-round bf16 gradient partials, token-major: for token tok (= bh L + pos)
+// and round r, the dq, dk rn and dv rows follow one another, so the reduce
+// streams one contiguous run of 3 nh rows per token.  Element offset of the
+// (tok, r) dq row; dk rn and dv are D and 2 D further on.
+__host__ __device__ constexpr size_t part_row(size_t tok, int nh, int r, int D)
+{
+    return ((tok * (size_t)nh + (size_t)r) * 3) * (size_t)D;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLazy = 8.0f;             // lazy running-max threshold (log2 units)
@@ -564,7 +572,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     }
 
-    bf16 *out = dq_part + (((size_t)bh * nh + r) * L + qpos) * D;
+    bf16 *out = dq_part + part_row(bh * L + qpos, nh, r, D);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -846,7 +854,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // dk of this round times the key's inverse norm; the projection through
     // the normalisation k = q rn is linear, so it is applied once to the sum
     // over rounds (reduce_kernel).  Lane (key c, group g) holds d = 16 dt + 4 g + t.
-    const size_t row = (((size_t)bh * nh + r) * L + kpos) * D;
+    const size_t row = part_row(bh * L + kpos, nh, r, D);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
         const int d0 = 16 * dt + 4 * g;
@@ -1026,7 +1034,6 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int t_begin = run * T, t_end = min(nt, t_begin + T);
     const uint32_t *sr = srec + (size_t)seg * L;
     const size_t tok0 = (size_t)bh * L;
-    const size_t part0 = (size_t)seg * L;
     const int kts = ktile_stride(nh), qts = qtile_stride(nh);
     const uint8_t *qtb = qtile + (size_t)seg * nblk * qts;
     const uint8_t *ktb = ktile + (size_t)seg * nblk * kts;
@@ -1086,7 +1093,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int t = t_begin; t < t_end; ++t) {
         const int k0 = t * kRows, a0 = k0 / kBlk, j = t - t_begin;
         if (t > t_begin)
-            dkv_store<D>(dkr_part, dv_part, (part0 + kpos_prev) * D, g, rn_prev, dka, dva);
+            dkv_store<D>(dkr_part, dv_part, part_row(tok0 + kpos_prev, nh, r, D), g, rn_prev, dka, dva);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
             dka[dt] = dva[dt] = f32x4_t{};
@@ -1158,7 +1165,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 vop[ks] = vnext[ks];
         }
     }
-    dkv_store<D>(dkr_part, dv_part, (part0 + kpos_prev) * D, g, rn_prev, dka, dva);
+    dkv_store<D>(dkr_part, dv_part, part_row(tok0 + kpos_prev, nh, r, D), g, rn_prev, dka, dva);
 }
 
 // ---------------------------------------------------------------------------
@@ -1274,7 +1281,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     float mrun = -INFINITY, lrun = 0.f;
     int qpos_prev = 0;
     auto finish = [&](int qpos) __attribute__((always_inline)) {
-        const size_t row = (part0 + qpos) * D;
+        // forward: o_rounds [b][h][r][L][D]; dq: the partial's row (see part_row)
+        const size_t row = BWD ? part_row(tok0 + qpos, nh, r, D) : (part0 + qpos) * D;
         float sc = 1.f;
         if constexpr (!BWD)
             sc = lrun > 0.f ? 1.f / lrun : 0.f;
@@ -1560,7 +1568,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
 #pragma unroll
     for (int r = 0; r < NH; ++r)
         if (r < nh) {
-            const size_t off = (((size_t)bh * nh + r) * L + t) * D + ch * 8;
+            const size_t off = part_row(tok, nh, r, D) + ch * 8;   // the round's three rows are adjacent
             xq[r] = ld16(dq_part + off);
             xk[r] = ld16(dkr_part + off);
             xv[r] = ld16(dv_part + off);
@@ -1665,8 +1673,8 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
                   const uint32_t *meta, const uint32_t *srec, const float *rnorm, const uint8_t *ktile,
                   const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
 {
-    const size_t n = (size_t)P.BH() * P.nh * P.L * D;
-    bf16 *dq_part = (bf16 *)part, *dkr_part = dq_part + n, *dv_part = dkr_part + n;
+    // rows of one (token, round) are dq, dk rn, dv in turn (part_row)
+    bf16 *dq_part = (bf16 *)part, *dkr_part = dq_part + D, *dv_part = dq_part + 2 * D;
     const dim3 grid((P.L / kRows) * P.nh * P.BH());
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);

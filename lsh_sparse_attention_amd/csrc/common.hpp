@@ -296,7 +296,7 @@ bool mfma_path_ok(const Dims &, int dtype);
 size_t mfma_ktile_bytes(const Dims &);
 size_t mfma_qtile_bytes(const Dims &);
 // bf16 per-round partials dq (query side), dk rn (key side, before the key
-// normalisation) and dv, each [B][H][nh][L][d], in one buffer of this size
+// normalisation) and dv, [B*H*L][nh][3][d] (token-major), in one buffer of this size
 size_t bwd_mfma_part_bytes(const Dims &);
 hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const int32_t *inv,
                                 const int32_t *win_lo, const uint32_t *meta, const uint32_t *srec,
