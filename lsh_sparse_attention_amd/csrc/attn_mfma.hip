@@ -991,22 +991,37 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
     }
 }
 
+// Stores one row of 16x16-MFMA accumulators times sc in bf16: lane (row c,
+// group g) holds d = 16 dt + 4 g + t.  Lanes g and g ^ 1 trade half of a pair
+// of d-groups (v_permlane16_swap: the odd row of the first operand with the
+// even row of the second), so each lane writes 8 consecutive d with one
+// 16-byte store and a row gets 64 contiguous bytes per instruction: g even
+// keeps group 2 dp and takes its partner's half of it, g odd takes the
+// partner's half of group 2 dp + 1.
+template <int D>
+__device__ __forceinline__ void store_row16(bf16 *row, int g, float sc, const f32x4_t (&acc)[D / 16])
+{
+    const bool odd = g & 1;
+#pragma unroll
+    for (int dp = 0; dp < D / 32; ++dp) {
+        const uint32_t u0 = pack_bf16x2(acc[2 * dp][0] * sc, acc[2 * dp][1] * sc);
+        const uint32_t u1 = pack_bf16x2(acc[2 * dp][2] * sc, acc[2 * dp][3] * sc);
+        const uint32_t u2 = pack_bf16x2(acc[2 * dp + 1][0] * sc, acc[2 * dp + 1][1] * sc);
+        const uint32_t u3 = pack_bf16x2(acc[2 * dp + 1][2] * sc, acc[2 * dp + 1][3] * sc);
+        const auto p = __builtin_amdgcn_permlane16_swap(u0, u2, false, false);
+        const auto q = __builtin_amdgcn_permlane16_swap(u1, u3, false, false);
+        const u32x4_t w = odd ? u32x4_t{p[0], q[0], u2, u3} : u32x4_t{u0, u1, p[1], q[1]};
+        st16(row + 32 * dp + 16 * (g & 1) + 8 * (g >> 1), w);
+    }
+}
+
 // stores dk rn and dv of one key (lane: key c, d = 16 dt + 4 g + t)
 template <int D>
 __device__ __forceinline__ void dkv_store(bf16 *dkr_part, bf16 *dv_part, size_t row, int g, float rn,
                                           const f32x4_t (&dka)[D / 16], const f32x4_t (&dva)[D / 16])
 {
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        const int d0 = 16 * dt + 4 * g;
-        uint2 w;
-        w.x = pack_bf16x2(dka[dt][0] * rn, dka[dt][1] * rn);
-        w.y = pack_bf16x2(dka[dt][2] * rn, dka[dt][3] * rn);
-        *reinterpret_cast<uint2 *>(dkr_part + row + d0) = w;
-        w.x = pack_bf16x2(dva[dt][0], dva[dt][1]);
-        w.y = pack_bf16x2(dva[dt][2], dva[dt][3]);
-        *reinterpret_cast<uint2 *>(dv_part + row + d0) = w;
-    }
+    store_row16<D>(dkr_part + row, g, rn, dka);
+    store_row16<D>(dv_part + row, g, 1.f, dva);
 }
 
 template <int D, int NR>
@@ -1286,13 +1301,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         float sc = 1.f;
         if constexpr (!BWD)
             sc = lrun > 0.f ? 1.f / lrun : 0.f;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            uint2 w;
-            w.x = pack_bf16x2(acc[dt][0] * sc, acc[dt][1] * sc);
-            w.y = pack_bf16x2(acc[dt][2] * sc, acc[dt][3] * sc);
-            *reinterpret_cast<uint2 *>(out + row + 16 * dt + 4 * g) = w;
-        }
+        store_row16<D>(out + row, g, sc, acc);
         if constexpr (!BWD)
             if (g == 0)
                 lse_rounds[part0 + qpos] = lrun > 0.f ? (mrun + __log2f(lrun)) * 0.69314718055994531f : -INFINITY;
