@@ -123,6 +123,34 @@ __device__ __forceinline__ void tile_argmax(const f32x16_t (&acc)[2], int j0, in
     }
 }
 
+// The same update for a full tile with fewer vector instructions: the
+// tile's largest key by three-input maxima, then the first slot holding it
+// (a compare and a select per score, last slot first).  Only tracker 0 of
+// each column tile is used.
+__device__ __forceinline__ void tile_argmax_full(const f32x16_t (&acc)[2], int j0, uint32_t (&bk)[2][2],
+                                                 int (&bi)[2][2])
+{
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        uint32_t k[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t u = __float_as_uint(acc[ct][e]);
+            k[e] = __builtin_amdgcn_alignbit(u, u, 31);
+        }
+        const uint32_t m0 = max(max(k[0], k[1]), k[2]), m1 = max(max(k[3], k[4]), k[5]);
+        const uint32_t m2 = max(max(k[6], k[7]), k[8]), m3 = max(max(k[9], k[10]), k[11]);
+        const uint32_t m4 = max(max(k[12], k[13]), k[14]);
+        const uint32_t tm = max(max(max(m0, m1), m2), max(max(m3, m4), k[15]));
+        int ts = 0;
+#pragma unroll
+        for (int e = 15; e >= 0; --e)
+            ts = k[e] == tm ? 8 * (e / 4) + (e % 4) : ts;
+        bi[ct][0] = tm > bk[ct][0] ? j0 + ts : bi[ct][0];
+        bk[ct][0] = max(bk[ct][0], tm);
+    }
+}
+
 // End of a round: merge the two slot parities, then the other half of the
 // row (larger key, else smaller column), store the bucket and reset.
 __device__ __forceinline__ void round_store(uint32_t (&bk)[2][2], int (&bi)[2][2], int h, int c, int row0, int L,
@@ -356,19 +384,19 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int
 #pragma unroll
         for (int jt = 0; jt < NT; jt += 2) {
             products(buf, jt, acc0);
-            tile_argmax<true>(acc1, jt == 0 ? prev_j : jb + 32 * (jt - 1), h, half, bk, bi);
+            tile_argmax_full(acc1, jt == 0 ? prev_j : jb + 32 * (jt - 1), bk, bi);
             interleave();
             if (jt == 0 && prev_last)
                 round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
             products(buf, jt + 1, acc1);
-            tile_argmax<true>(acc0, jb + 32 * jt, h, half, bk, bi);
+            tile_argmax_full(acc0, jb + 32 * jt, bk, bi);
             interleave();
         }
         prev_j = jb + COLS - 32;
         prev_r = r;
         prev_last = jb + COLS == half;
     }
-    tile_argmax<true>(acc1, prev_j, h, half, bk, bi);
+    tile_argmax_full(acc1, prev_j, bk, bi);
     round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
 }
 
