@@ -657,28 +657,6 @@ __device__ __forceinline__ void dma_tensor_wave(const bf16 *__restrict__ a, uint
         dma16(a + off[i], A + i * kWave * 8);
 }
 
-// One wave loads a whole block: rows [0, 32) of tensors a and b (positions
-// from rec) into the swizzled tiles A and B, D/16 instructions per tensor.
-template <int D>
-__device__ __forceinline__ void dma_block_wave(const bf16 *__restrict__ a, const bf16 *__restrict__ b, uint16_t *A,
-                                               uint16_t *B, const uint32_t *rec, size_t tok0, int lane)
-{
-    constexpr int CPR = D / 8, N = kBlk * CPR / kWave;
-    size_t off[N];   // records first (see dma_rows)
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int qc = i * kWave + lane;
-        const int row = qc / CPR, p = qc % CPR;
-        const int lc = p ^ (row & (CPR - 1));
-        off[i] = (tok0 + rec_lo(rec[row])) * D + lc * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        dma16(a + off[i], A + i * kWave * 8);
-        dma16(b + off[i], B + i * kWave * 8);
-    }
-}
-
 template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(
     int L, int nh, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v, const bf16 *__restrict__ dout,
