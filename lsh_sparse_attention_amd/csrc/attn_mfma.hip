@@ -923,22 +923,44 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
     }
     if (r > 0) {
         uint32_t hit[4] = {0u, 0u, 0u, 0u};
+        if constexpr (kv_sk_in_regs<D, NR>()) {
+            // the queries' (start - 1, length) pairs of every round rr < NR,
+            // read without a branch so that they go out together (pairs of
+            // rounds rr >= r lie within the LDS tile and are not used)
+            uint2 qa1[NR][2], qww[NR][2];
 #pragma unroll
-        for (int rr = 0; rr < NR; ++rr)
-            if (rr < r) {
-                const uint32_t kp = kv_sk_in_regs<D, NR>()
-                                        ? skp[rr]
-                                        : bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
-                // the queries' (start - 1, length) pairs in round rr
-                const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
+            for (int rr = 0; rr < NR; ++rr)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
-                    const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
-                    hit[2 * u] |= win_hits2(a.x, ww.x, kp);
-                    hit[2 * u + 1] |= win_hits2(a.y, ww.y, kp);
+                    const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
+                    qa1[rr][u] = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
+                    qww[rr][u] = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
                 }
-            }
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr)
+                if (rr < r) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        hit[2 * u] |= win_hits2(qa1[rr][u].x, qww[rr][u].x, skp[rr]);
+                        hit[2 * u + 1] |= win_hits2(qa1[rr][u].y, qww[rr][u].y, skp[rr]);
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < NR; ++rr)
+                if (rr < r) {
+                    const uint32_t kp = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
+                    // the queries' (start - 1, length) pairs in round rr
+                    const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
+                        const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                        hit[2 * u] |= win_hits2(a.x, ww.x, kp);
+                        hit[2 * u + 1] |= win_hits2(a.y, ww.y, kp);
+                    }
+                }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
@@ -1099,10 +1121,11 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const float rn = krn2 * inv_sl2;
         uint32_t skp[NR];   // the key's sorted index in the earlier rounds
         if constexpr (kv_sk_in_regs<D, NR>()) {
+            // read for every rr < NR without a branch, so the reads go out
+            // together (entries rr >= r are within the LDS tile and unused)
 #pragma unroll
             for (int rr = 0; rr < NR; ++rr)
-                if (rr < r)
-                    skp[rr] = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
+                skp[rr] = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
         }
         bf16x8_t kop[D / 32];
         {
