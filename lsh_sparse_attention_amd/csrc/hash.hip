@@ -304,7 +304,10 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int
                                                                       const bf16 *__restrict__ rot,
                                                                       int32_t *__restrict__ buckets)
 {
-    constexpr int COLS = kHashCols, P = COLS + 8;
+    // pitch 96 elements (48 banks): the four rows of a transposed read start
+    // at banks 0, 48, 32, 16, so lane groups 0 and 1 (16 columns apart) read
+    // disjoint banks in the same cycle
+    constexpr int COLS = kHashCols, P = 96;
     constexpr int NT = COLS / 32;   // tiles per block (even: they alternate between two accumulator sets)
     __shared__ __align__(16) uint16_t Rs[2][D * P];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
