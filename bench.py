@@ -124,6 +124,31 @@ class Hip:
         self.h.hipEventDestroy(ev)
 
 
+def rehash_variant(prob, mod, q, v, rot, do, steps, cfg) -> dict:
+    """The reversible-layer step: forward, then a backward that recomputes hashing and sorting
+    (lsh_attn_bwd_rehash) instead of reading the forward's saved records."""
+    import torch
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib as L_
+    ws = torch.empty(lsh.workspace_bytes(prob, L_.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
+    dq, dv = torch.empty_like(mod.dq), torch.empty_like(mod.dv)
+
+    def step():
+        mod.forward(q, v, rot)
+        lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq, dv, ws)
+
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del ws
+    return {"ms_per_step": ms, "value": cfg.batch * cfg.seq_len / (ms * 1e-3), "unit": "tokens/s",
+            "kept_between_passes": "out, lse (no buckets, sorted order or records)"}
+
+
 def source_sha(kernel: str) -> str:
     """Digest of the sources a kernel is compiled from (its file and the shared header)."""
     h = hashlib.sha256()
@@ -276,6 +301,7 @@ def main() -> int:
                    "causal": True, "clustered_inputs": cfg.clustered},
         "roofline": roof,
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "variants": {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)},
     }
     del mod
     torch.cuda.empty_cache()

@@ -47,7 +47,13 @@ typedef enum {
 typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype_t;
 
 /* Which call a workspace is for (lsh_workspace_bytes). */
-typedef enum { LSH_WS_SORT = 0, LSH_WS_FWD = 1, LSH_WS_BWD = 2, LSH_WS_TRAIN = 3 } lsh_ws_kind_t;
+typedef enum {
+    LSH_WS_SORT = 0,
+    LSH_WS_FWD = 1,
+    LSH_WS_BWD = 2,
+    LSH_WS_TRAIN = 3,
+    LSH_WS_REHASH = 4
+} lsh_ws_kind_t;
 
 /*
  * Problem description, passed by pointer to every call.
@@ -79,9 +85,10 @@ const char *lsh_status_string(int status);
 int lsh_version(void);
 
 /* Bytes of device workspace that lsh_sort (LSH_WS_SORT), lsh_attn_fwd
- * (LSH_WS_FWD) or lsh_attn_bwd (LSH_WS_BWD) needs for `prob`, or that one
- * workspace shared by lsh_attn_fwd and a later lsh_attn_bwd_saved needs
- * (LSH_WS_TRAIN); 0 if the problem is invalid or empty.  Alignment of every
+ * (LSH_WS_FWD), lsh_attn_bwd (LSH_WS_BWD) or lsh_attn_bwd_rehash
+ * (LSH_WS_REHASH) needs for `prob`, or that one workspace shared by
+ * lsh_attn_fwd and a later lsh_attn_bwd_saved needs (LSH_WS_TRAIN); 0 if the
+ * problem is invalid or empty.  Alignment of every
  * workspace pointer: 256 bytes. */
 size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind);
 
@@ -173,6 +180,23 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
                  const void *dout, const float *lse, const int32_t *perm, const int32_t *inv,
                  const int32_t *win_lo, void *dq, void *dv, void *ws, size_t ws_bytes,
                  void *stream);
+
+/*
+ * lsh_attn_bwd_rehash -- lsh_attn_bwd for the reversible-layer setting
+ * ("Reformer" §3: activations are recovered in the backward pass instead of
+ * being stored): the buckets, the sorted order and the window starts are
+ * recomputed from q and rot (lsh_hash and lsh_sort inside the call), so the
+ * caller keeps none of them between the forward and the backward.  Hashing
+ * and sorting are deterministic, so the gradient is the same, bit for bit,
+ * as lsh_attn_bwd's with the forward's perm, inv and win_lo.
+ *   q, v, out, dout, lse, dq, dv  as for lsh_attn_bwd.
+ *   rot        [nh][d][nb/2] dtype: the rotations the forward hashed with.
+ *   ws         workspace of lsh_workspace_bytes(prob, LSH_WS_REHASH) bytes
+ *              (scratch only; nothing in it is needed after the call).
+ */
+int lsh_attn_bwd_rehash(const lsh_problem_t *prob, const void *q, const void *v, const void *rot,
+                        const void *out, const void *dout, const float *lse, void *dq, void *dv,
+                        void *ws, size_t ws_bytes, void *stream);
 
 /*
  * lsh_attn_bwd_saved -- lsh_attn_bwd for a training step that keeps the

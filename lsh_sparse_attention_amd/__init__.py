@@ -7,7 +7,9 @@ device memory and streams only.  If liblsh.so is missing, the calls raise.
 
 Pipeline (per (batch, head, round)): ``lsh_hash`` -> ``lsh_sort`` ->
 ``lsh_attn_fwd`` -> ``lsh_combine``; backward: ``lsh_attn_bwd``, or
-``lsh_attn_bwd_saved`` on the workspace the forward filled.
+``lsh_attn_bwd_saved`` on the workspace the forward filled, or
+``lsh_attn_bwd_rehash``, which recomputes the hashing and sorting (nothing kept
+from the forward but its output and lse).
 """
 from __future__ import annotations
 
@@ -16,11 +18,11 @@ import math
 
 import torch
 
-from ._lib import (LSH_BF16, LSH_F32, LSH_WS_BWD, LSH_WS_FWD, LSH_WS_SORT, LSH_WS_TRAIN, LshError, Problem, check,
-                   lib)
+from ._lib import (LSH_BF16, LSH_F32, LSH_WS_BWD, LSH_WS_FWD, LSH_WS_REHASH, LSH_WS_SORT, LSH_WS_TRAIN, LshError,
+                   Problem, check, lib)
 
 __all__ = ["Problem", "LshError", "problem", "workspace_bytes", "lsh_hash", "lsh_sort", "lsh_attn_fwd",
-           "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "LshAttention"]
+           "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash", "LshAttention"]
 
 _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
 
@@ -150,6 +152,20 @@ def lsh_attn_bwd_saved(prob, q, v, out, dout, lse, dq, dv, ws, stream=None):
     check("lsh_attn_bwd_saved", lib().lsh_attn_bwd_saved(
         ctypes.byref(prob), _ptr(q, "q", dt), _ptr(v, "v", dt), _ptr(out, "out", dt), _ptr(dout, "dout", dt),
         _ptr(lse, "lse", torch.float32), _ptr(dq, "dq", dt), _ptr(dv, "dv", dt), wp, wn, _stream(stream)))
+
+
+def lsh_attn_bwd_rehash(prob, q, v, rot, out, dout, lse, dq, dv, ws, stream=None):
+    """lsh_attn_bwd with buckets, sorted order and windows recomputed from q and rot (an LSH_WS_REHASH workspace)."""
+    dt = torch_dtype(prob)
+    n, nd = _tok(prob), _tok(prob) * prob.head_dim
+    for t, nm, k in ((q, "q", nd), (v, "v", nd), (rot, "rot", prob.n_hashes * prob.head_dim * (prob.n_buckets // 2)),
+                     (out, "out", nd), (dout, "dout", nd), (lse, "lse", n), (dq, "dq", nd), (dv, "dv", nd)):
+        _numel_check(t, k, nm)
+    wp, wn = _ws(ws, prob, LSH_WS_REHASH)
+    check("lsh_attn_bwd_rehash", lib().lsh_attn_bwd_rehash(
+        ctypes.byref(prob), _ptr(q, "q", dt), _ptr(v, "v", dt), _ptr(rot, "rot", dt), _ptr(out, "out", dt),
+        _ptr(dout, "dout", dt), _ptr(lse, "lse", torch.float32), _ptr(dq, "dq", dt), _ptr(dv, "dv", dt), wp, wn,
+        _stream(stream)))
 
 
 class LshAttention:

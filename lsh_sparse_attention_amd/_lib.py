@@ -12,15 +12,15 @@ LIB_PATH = os.path.join(HERE, "liblsh.so")
 
 # Exported symbols, in header order.
 SYMBOLS = ("lsh_status_string", "lsh_version", "lsh_workspace_bytes", "lsh_hash", "lsh_sort",
-           "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_kernel_name",
-           "lsh_profile_kernel")
+           "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash",
+           "lsh_kernel_name", "lsh_profile_kernel")
 
 KERNELS = ("hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq",
            "bwd_dkv", "bwd_reduce", "tiles")
 
 LSH_OK, LSH_ERR_INVALID, LSH_ERR_UNSUPPORTED, LSH_ERR_HIP = 0, 1, 2, 3
 LSH_F32, LSH_BF16 = 0, 1
-LSH_WS_SORT, LSH_WS_FWD, LSH_WS_BWD, LSH_WS_TRAIN = 0, 1, 2, 3
+LSH_WS_SORT, LSH_WS_FWD, LSH_WS_BWD, LSH_WS_TRAIN, LSH_WS_REHASH = 0, 1, 2, 3, 4
 
 
 class Problem(ctypes.Structure):
@@ -58,10 +58,11 @@ def lib() -> ctypes.CDLL:
         L.lsh_combine.argtypes = [pp, vp, vp, vp, fp, vp, fp, vp]
         L.lsh_attn_bwd.argtypes = [pp, vp, vp, vp, vp, fp, i32p, i32p, i32p, vp, vp, vp, sz, vp]
         L.lsh_attn_bwd_saved.argtypes = [pp, vp, vp, vp, vp, fp, vp, vp, vp, sz, vp]
+        L.lsh_attn_bwd_rehash.argtypes = [pp, vp, vp, vp, vp, vp, fp, vp, vp, vp, sz, vp]
         L.lsh_kernel_name.argtypes, L.lsh_kernel_name.restype = [ctypes.c_int], ctypes.c_char_p
         L.lsh_profile_kernel.argtypes = [ctypes.c_int, vp, vp]
         for name in ("lsh_hash", "lsh_sort", "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved",
-                     "lsh_profile_kernel"):
+                     "lsh_attn_bwd_rehash", "lsh_profile_kernel"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

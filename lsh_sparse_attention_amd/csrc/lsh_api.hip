@@ -115,9 +115,48 @@ BwdWs bwd_layout(const Dims &P, void *base)
     return w;
 }
 
+// lsh_attn_bwd_rehash's workspace: the backward's own, then the buckets,
+// sorted order and window starts it recomputes, then the sort's scratch.
+struct RehashWs {
+    void *bwd;
+    size_t bwd_bytes;
+    int32_t *buckets, *perm, *inv, *win_lo;
+    void *sort;
+    size_t sort_bytes;
+    size_t bytes;
+};
+
+RehashWs rehash_layout(const Dims &P, void *base)
+{
+    const size_t rnd = (size_t)P.BH() * P.nh * P.L;
+    const uintptr_t b = (uintptr_t)base;
+    RehashWs w{};
+    size_t o = 0;
+    w.bwd = (void *)(b + o);
+    w.bwd_bytes = bwd_layout(P, nullptr).bytes;
+    o += align_up(w.bwd_bytes, 256);
+    w.buckets = (int32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.perm = (int32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.inv = (int32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.win_lo = (int32_t *)(b + o); o += align_up(rnd * 4, 256);
+    w.sort = (void *)(b + o);
+    w.sort_bytes = sort_ws_bytes(P);
+    o += align_up(w.sort_bytes, 256);
+    w.bytes = o;
+    return w;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The backward behind both entry points.  With perm null the packed
+// Tensor arguments of a backward: present, and 16-byte aligned where rows are read in 16-byte pieces.
+bool bwd_args_ok(const void *q, const void *v, const void *out, const void *dout, const float *lse, const void *dq,
+                 const void *dv)
+{
+    return q && v && out && dout && lse && dq && dv && aligned16(q) && aligned16(v) && aligned16(out) &&
+           aligned16(dout) && aligned16(dq) && aligned16(dv);
+}
+
+// The backward behind the three entry points.  With perm null the packed
 // records, norms and key tiles are taken as lsh_attn_fwd left them in ws
 // (same offsets); otherwise they are derived from perm, inv, win_lo first.
 int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void *out, const void *dout,
@@ -125,8 +164,7 @@ int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void
              void *ws, size_t ws_bytes, void *stream)
 {
     const Dims P = dims_of(prob);
-    if (!q || !v || !out || !dout || !lse || !dq || !dv || !ws || ((uintptr_t)ws & 255u) || !aligned16(q) ||
-        !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) || !aligned16(dv))
+    if (!bwd_args_ok(q, v, out, dout, lse, dq, dv) || !ws || ((uintptr_t)ws & 255u))
         return LSH_ERR_INVALID;
     const BwdWs w = bwd_layout(P, ws);
     if (ws_bytes < w.bytes)
@@ -192,6 +230,7 @@ size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
     case LSH_WS_FWD: return fwd_layout(P, nullptr).bytes;
     case LSH_WS_BWD:
     case LSH_WS_TRAIN: return bwd_layout(P, nullptr).bytes;
+    case LSH_WS_REHASH: return rehash_layout(P, nullptr).bytes;
     default: return 0;
     }
 }
@@ -267,6 +306,29 @@ int lsh_attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     if (!perm || !inv || !win_lo)
         return LSH_ERR_INVALID;
     return attn_bwd(prob, q, v, out, dout, lse, perm, inv, win_lo, dq, dv, ws, ws_bytes, stream);
+}
+
+int lsh_attn_bwd_rehash(const lsh_problem_t *prob, const void *q, const void *v, const void *rot, const void *out,
+                        const void *dout, const float *lse, void *dq, void *dv, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    int st = validate(prob);
+    if (st != LSH_OK || empty(prob))
+        return st;
+    const Dims P = dims_of(prob);
+    // every argument is checked before the hash and sort are launched
+    if (!rot || !aligned16(rot) || !bwd_args_ok(q, v, out, dout, lse, dq, dv) || !ws || ((uintptr_t)ws & 255u))
+        return LSH_ERR_INVALID;
+    const RehashWs w = rehash_layout(P, ws);
+    if (ws_bytes < w.bytes)
+        return LSH_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_hash(P, prob->dtype, q, rot, w.buckets, s);
+    if (e == hipSuccess)
+        e = launch_sort(P, w.buckets, w.perm, w.inv, w.win_lo, w.sort, s);
+    if (e != hipSuccess)
+        return hip_status(e);
+    return attn_bwd(prob, q, v, out, dout, lse, w.perm, w.inv, w.win_lo, dq, dv, w.bwd, w.bwd_bytes, stream);
 }
 
 int lsh_attn_bwd_saved(const lsh_problem_t *prob, const void *q, const void *v, const void *out, const void *dout,

@@ -60,7 +60,7 @@ def test_empty_problems_are_no_ops(kw):
     # null pointers and a null workspace are fine: nothing is read or launched
     p = _prob(**kw)
     L = _lib.lib()
-    for k in (0, 1, 2, 3):
+    for k in (0, 1, 2, 3, 4):
         assert L.lsh_workspace_bytes(ctypes.byref(p), k) == 0
     n = None
     assert L.lsh_hash(ctypes.byref(p), n, n, n, n) == 0
@@ -69,6 +69,7 @@ def test_empty_problems_are_no_ops(kw):
     assert L.lsh_combine(ctypes.byref(p), n, n, n, n, n, n, n) == 0
     assert L.lsh_attn_bwd(ctypes.byref(p), n, n, n, n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
     assert L.lsh_attn_bwd_saved(ctypes.byref(p), n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), n, n, n, n, n, n, n, n, n, ctypes.c_size_t(0), n) == 0
     # an empty problem is still validated: a bad head size is reported
     bad = _prob(head_dim=48, **kw)
     assert L.lsh_hash(ctypes.byref(bad), n, n, n, n) == 2
@@ -107,7 +108,7 @@ def test_saved_backward_workspace_and_arguments():
     fwd = lsh.workspace_bytes(p, _lib.LSH_WS_FWD)
     train = lsh.workspace_bytes(p, _lib.LSH_WS_TRAIN)
     assert train == lsh.workspace_bytes(p, _lib.LSH_WS_BWD) and train > fwd > 0
-    assert L.lsh_workspace_bytes(ctypes.byref(p), 4) == 0
+    assert L.lsh_workspace_bytes(ctypes.byref(p), 5) == 0
     ok = ctypes.c_void_p(1 << 20)
     args = [ok] * 7
     assert L.lsh_attn_bwd_saved(ctypes.byref(p), *args, ok, ctypes.c_size_t(train - 1), None) == 1
@@ -121,10 +122,31 @@ def test_saved_backward_workspace_and_arguments():
                           None) == 1
 
 
+def test_rehash_backward_workspace_and_arguments():
+    # the rehash workspace holds the backward's, the recomputed sort outputs and the sort's scratch
+    p = _prob()
+    L = _lib.lib()
+    rehash = lsh.workspace_bytes(p, _lib.LSH_WS_REHASH)
+    rnd = p.batch * p.heads * p.n_hashes * p.seq_len
+    assert rehash >= lsh.workspace_bytes(p, _lib.LSH_WS_BWD) + 4 * rnd * 4 + lsh.workspace_bytes(p, _lib.LSH_WS_SORT)
+    ok = ctypes.c_void_p(1 << 20)
+    args = [ok] * 8   # q, v, rot, out, dout, lse, dq, dv
+    sz = ctypes.c_size_t(rehash)
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), *args, ok, ctypes.c_size_t(rehash - 1), None) == 1
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), *args, None, sz, None) == 1
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), *args, ctypes.c_void_p((1 << 20) + 64), sz, None) == 1
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), ok, ok, None, *args[3:], ok, sz, None) == 1          # rot
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), ok, ok, ctypes.c_void_p((1 << 20) + 2), *args[3:], ok, sz,
+                                 None) == 1
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(p), *args[:6], None, ok, ok, sz, None) == 1                # dq
+    bad = _prob(head_dim=48)
+    assert L.lsh_attn_bwd_rehash(ctypes.byref(bad), *args, ok, sz, None) == 2
+
+
 def test_workspace_sizes_grow_with_problem():
     small = _prob()
     big = _prob(batch=4)
-    for k in (0, 1, 2, 3):
+    for k in (0, 1, 2, 3, 4):
         assert 0 < lsh.workspace_bytes(small, k) < lsh.workspace_bytes(big, k)
         assert lsh.workspace_bytes(small, k) % 256 == 0
 

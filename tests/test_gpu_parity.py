@@ -153,6 +153,33 @@ def test_standalone_backward_matches_saved(idx):
                        dv_s.view(torch.int16) if dv_s.dtype == torch.bfloat16 else dv_s)
 
 
+@pytest.mark.parametrize("idx", [1, 0, 2, 17, 19])
+def test_rehash_backward_matches_stored_order(idx):
+    # lsh_attn_bwd_rehash recomputes buckets, order and windows from q and
+    # rot; hashing and sorting are deterministic, so the gradient equals
+    # lsh_attn_bwd's on the forward's stored order bit for bit
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    cfg = _small_cfg(SMALL[idx])
+    gu.say(f"[gpu] rehash vs stored-order backward {cfg}")
+    x = gen.generate(cfg)
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype)
+    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
+    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
+    mod = lsh.LshAttention(prob, backward=False)
+    mod.forward(q, v, rot)
+    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
+    dq, dv = torch.empty_like(q), torch.empty_like(v)
+    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
+    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
+    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
+    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    assert torch.equal(bits(dq), bits(dq2)) and torch.equal(bits(dv), bits(dv2))
+
+
 def test_empty_problem_is_a_no_op():
     import lsh_sparse_attention_amd as lsh
     gu.say("[gpu] empty problem L=0")
