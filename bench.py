@@ -188,6 +188,60 @@ def cpu_baseline(x, heads: int):
     }
 
 
+def sweep(kind: str, steps: int, warmup: int) -> int:
+    """Two sweeps on the text workload's shape (d = 128, 8 heads, m = 128), one JSON line each point.
+
+    length: total tokens fixed (B L = 65536), L from 1024 to 65536 with B = 65536 / L and
+    n_buckets = L / 64 (the text workload's rows per bucket), 4 rounds; forward + backward step.
+    The pages report that LSH attention's speed stays flat as L grows at a fixed total.
+    rounds: the text workload with n_hashes = 1, 2, 4, 8; forward (hash, sort, attention,
+    combine) and forward + backward, since more rounds can be used at evaluation."""
+    import torch
+    import numpy as np
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import inputs as gen
+
+    def dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    base = gen.CONFIGS["text"]
+    if kind == "length":
+        points = [base.with_(name=f"len{L}", batch=65536 // L, seq_len=L, n_buckets=L // 64)
+                  for L in (1024, 2048, 4096, 8192, 16384, 32768, 65536)]
+    else:
+        points = [base.with_(name=f"nh{nh}", n_hashes=nh) for nh in (1, 2, 4, 8)]
+    for cfg in points:
+        x = gen.generate(cfg, with_grad=True)
+        q, v, rot, do = (dev(x[k], cfg.dtype) for k in ("q", "v", "rot", "dout"))
+        prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                           cfg.chunk_len, cfg.scale, cfg.dtype)
+        mod = lsh.LshAttention(prob)
+        fwd_ms = timed(lambda: mod.forward(q, v, rot))
+        step_ms = timed(lambda: (mod.forward(q, v, rot), mod.backward(q, v, do)))
+        tokens = cfg.batch * cfg.seq_len
+        print(json.dumps({"sweep": kind, "batch": cfg.batch, "heads": cfg.heads, "seq_len": cfg.seq_len,
+                          "head_dim": cfg.head_dim, "n_buckets": cfg.n_buckets, "n_hashes": cfg.n_hashes,
+                          "chunk_len": cfg.chunk_len, "fwd_ms": round(fwd_ms, 4), "step_ms": round(step_ms, 4),
+                          "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3),
+                          "step_tokens_per_s": tokens / (step_ms * 1e-3)}), flush=True)
+        del mod, q, v, rot, do
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +249,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="text")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads of batch 0 the oracle times (0: skip)")
+    ap.add_argument("--sweep", choices=("length", "rounds"),
+                    help="instead of the bench line: a length sweep at fixed total tokens, or a rounds sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 1 GiB (reference point for HBM byte counters)")
     args = ap.parse_args()
@@ -204,6 +260,8 @@ def main() -> int:
               "the path is per-(batch, head) independent and is not sharded here.", file=sys.stderr)
         return 2
 
+    if args.sweep:
+        return sweep(args.sweep, args.steps, args.warmup)
     import torch
     if args.copy_calibration:
         n = 1 << 28                                   # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
