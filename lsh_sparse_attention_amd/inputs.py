@@ -52,6 +52,7 @@ class Config:
     seed: int
     n_clusters: int = 256
     cluster_sigma: float = 0.1
+    causal: bool = True
 
     @property
     def scale(self) -> float:

@@ -29,8 +29,9 @@ def sort(bk):
     return perm, inv
 
 
-def round_masks(bk, m):
-    """[nh, L, L] bool: j in A_i^r (self included)."""
+def round_masks(bk, m, causal=True):
+    """[nh, L, L] bool: j in A_i^r (self included).  Without ``causal`` the
+    condition j <= i is dropped (same bucket, own chunk or the one before)."""
     nh, L = bk.shape
     _, inv = sort(bk)
     i = np.arange(L)[:, None]
@@ -40,12 +41,13 @@ def round_masks(bk, m):
         c = inv[r] // m
         same = bk[r][:, None] == bk[r][None, :]
         dc = c[:, None] - c[None, :]
-        out.append(same & (j <= i) & ((dc == 0) | (dc == 1)))
+        order = (j <= i) if causal else np.ones((L, L), dtype=bool)
+        out.append(same & order & ((dc == 0) | (dc == 1)))
     return np.asarray(out)
 
 
-def union_mask(bk, m):
-    return round_masks(bk, m).any(axis=0)
+def union_mask(bk, m, causal=True):
+    return round_masks(bk, m, causal).any(axis=0)
 
 
 def attention(q, v, mask, scale):

@@ -338,6 +338,170 @@ def test_backward_constant_values_give_no_query_gradient():
     np.testing.assert_allclose(res["dq"], 0.0, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- non-causal sets
+# Encoder self-attention: the condition "not after the query" is dropped and
+# nothing else changes (same bucket, own chunk or the one before, no
+# look-ahead, no wrap-around, self only when nothing else is there).
+
+def _sdpa(q, v, mask, scale):
+    qt = torch.from_numpy(q)[None, None]
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    return torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, torch.from_numpy(v)[None, None], attn_mask=torch.from_numpy(mask), scale=scale)[0, 0].numpy()
+
+
+def test_noncausal_union_golden():
+    g = _golden()["attention_noncausal"]
+    bk = np.array(g["buckets"], np.int32)
+    L, m = g["L"], g["chunk_len"]
+    for key, nh in (("round0_only", 1), ("both_rounds", 2)):
+        perm, inv, _ = ora.sort(bk[:nh], m)
+        mask = ora.union_mask(bk[:nh], perm, inv, m, causal=False)
+        for i, members in enumerate(g[key]["sets"]):
+            got = sorted(set(np.nonzero(mask[i])[0].tolist()) - {i})
+            assert got == members, (key, i)
+
+
+def test_noncausal_forward_golden_one_hot():
+    g = _golden()["attention_noncausal"]
+    bk = np.array(g["buckets"], np.int32)
+    L, m = g["L"], g["chunk_len"]
+    q = np.random.default_rng(0).standard_normal((L, L))
+    for key, nh in (("round0_only", 1), ("both_rounds", 2)):
+        perm, inv, _ = ora.sort(bk[:nh], m)
+        out, lse = ora.forward(q, np.eye(L), bk[:nh], perm, inv, m, g["scale"], causal=False)
+        np.testing.assert_allclose(out, _weights_to_rows(g[key]["out_rows_as_weights"], L), atol=1e-15)
+        sizes = np.array([len(x) for x in g[key]["sets"]])
+        np.testing.assert_allclose(lse, np.where(sizes > 0, np.log(np.maximum(sizes, 1)), 0.0), atol=1e-15)
+
+
+@pytest.mark.parametrize("seed,L,nb,nh,m", [(51, 64, 4, 1, 8), (52, 128, 8, 3, 16), (53, 96, 2, 2, 32),
+                                            (54, 256, 32, 4, 16), (55, 64, 16, 2, 64), (56, 200, 4, 2, 8),
+                                            (57, 64, 2, 2, 1)])
+def test_noncausal_union_matches_bruteforce(seed, L, nb, nh, m):
+    rng = np.random.default_rng(seed)
+    bk = rng.integers(0, nb, size=(nh, L)).astype(np.int32)
+    perm, inv, _ = ora.sort(bk, m)
+    nc = ora.union_mask(bk, perm, inv, m, causal=False)
+    assert np.array_equal(nc, bf.union_mask(bk, m, causal=False))
+    # the causal sets are the non-causal ones cut to j <= i
+    c = ora.union_mask(bk, perm, inv, m)
+    assert np.array_equal(c, nc & np.tril(np.ones((L, L), dtype=bool)))
+
+
+@pytest.mark.parametrize("seed,L,nb,m", [(61, 128, 4, 8), (62, 256, 16, 16), (63, 96, 2, 32)])
+def test_noncausal_round_set_is_symmetric_within_a_chunk(seed, L, nb, m):
+    # Same bucket and same chunk is a symmetric relation; across chunks only
+    # the later chunk sees the earlier one.
+    rng = np.random.default_rng(seed)
+    bk = rng.integers(0, nb, size=(1, L)).astype(np.int32)
+    perm, inv, _ = ora.sort(bk, m)
+    a = ora.union_mask(bk, perm, inv, m, causal=False)
+    c = inv[0] // m
+    same = c[:, None] == c[None, :]
+    assert np.array_equal(a & same, (a & same).T)
+    later = c[:, None] > c[None, :]
+    assert not np.any(a & later & a.T)
+
+
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(71, 64, 8, 4, 1, 8), (72, 128, 16, 8, 3, 16),
+                                              (73, 256, 32, 16, 2, 32), (74, 96, 4, 2, 4, 96),
+                                              (75, 160, 8, 64, 2, 16)])
+def test_noncausal_forward_matches_dense_bruteforce(seed, L, d, nb, nh, m):
+    q, v, rot, _ = _rand_problem(seed, L, d, nh, nb, scale_q=1.5)
+    scale = 1 / np.sqrt(d)
+    res = ora.head(q, v, rot, nb, m, scale, causal=False)
+    out, lse = bf.attention(q, v, bf.union_mask(bf.buckets(q, rot), m, causal=False), scale)
+    np.testing.assert_allclose(res["out"], out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse, rtol=1e-12, atol=1e-12)
+
+
+def test_noncausal_one_bucket_is_full_shared_qk_attention():
+    # One bucket and m = L: every query attends to every other token, which is
+    # torch SDPA with only the diagonal masked.
+    rng = np.random.default_rng(77)
+    L, d = 128, 16
+    rot = rng.standard_normal((1, d, 1))
+    q = _one_side(rng.standard_normal((L, d)), rot[0, :, 0])
+    v = rng.standard_normal((L, d))
+    res = ora.head(q, v, rot, 2, L, 0.37, causal=False)
+    assert np.all(res["buckets"] == 0)
+    np.testing.assert_allclose(res["out"], _sdpa(q, v, ~np.eye(L, dtype=bool), 0.37), rtol=1e-12, atol=1e-12)
+
+
+def test_noncausal_one_bucket_chunked_is_banded_attention():
+    # One bucket and m < L: query i sees every j != i of its own chunk and
+    # the chunk before, and nothing of the chunk after.
+    rng = np.random.default_rng(78)
+    L, d, m = 96, 8, 16
+    rot = rng.standard_normal((1, d, 1))
+    q = _one_side(rng.standard_normal((L, d)), rot[0, :, 0])
+    v = rng.standard_normal((L, d))
+    res = ora.head(q, v, rot, 2, m, 0.5, causal=False)
+    c = np.arange(L) // m
+    dc = c[:, None] - c[None, :]
+    mask = ((dc == 0) | (dc == 1)) & ~np.eye(L, dtype=bool)
+    np.testing.assert_allclose(res["out"], _sdpa(q, v, mask, 0.5), rtol=1e-12, atol=1e-12)
+
+
+def test_noncausal_m_equals_L_is_exact_per_bucket_attention():
+    q, v, rot, _ = _rand_problem(79, 128, 8, 1, 8)
+    res = ora.head(q, v, rot, 8, 128, 0.7, causal=False)
+    bk = res["buckets"][0]
+    mask = (bk[:, None] == bk[None, :]) & ~np.eye(128, dtype=bool)
+    alone = ~mask.any(axis=1)
+    mask[alone, np.nonzero(alone)[0]] = True
+    np.testing.assert_allclose(res["out"], _sdpa(q, v, mask, 0.7), rtol=1e-12, atol=1e-12)
+
+
+def test_noncausal_repeated_rotation_equals_one_round():
+    q, v, rot, _ = _rand_problem(80, 256, 16, 1, 16)
+    one = ora.head(q, v, rot, 16, 32, 0.3, causal=False)
+    three = ora.head(q, v, np.repeat(rot, 3, axis=0), 16, 32, 0.3, causal=False)
+    np.testing.assert_allclose(three["out"], one["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(three["lse"], one["lse"], rtol=1e-13, atol=1e-13)
+
+
+def test_noncausal_backward_finite_differences():
+    seed, L, d, nb, nh, m, scale = 81, 48, 6, 4, 2, 8, 0.8
+    q, v, rot, do = _rand_problem(seed, L, d, nh, nb)
+    bk = ora.hash_(q, rot, nb)
+    perm, inv, _ = ora.sort(bk, m)
+    out, lse = ora.forward(q, v, bk, perm, inv, m, scale, causal=False)
+    dq, dv = ora.backward(q, v, do, bk, perm, inv, out, lse, m, scale, causal=False)
+    h = 1e-6
+    rng = np.random.default_rng(seed)
+    for (t, c) in zip(rng.integers(0, L, 40), rng.integers(0, d, 40)):
+        for x, g in ((q, dq), (v, dv)):
+            xp, xm = x.copy(), x.copy()
+            xp[t, c] += h
+            xm[t, c] -= h
+            args_p = (xp, v) if x is q else (q, xp)
+            args_m = (xm, v) if x is q else (q, xm)
+            lp = float((ora.forward(*args_p, bk, perm, inv, m, scale, causal=False)[0] * do).sum())
+            lm = float((ora.forward(*args_m, bk, perm, inv, m, scale, causal=False)[0] * do).sum())
+            assert (lp - lm) / (2 * h) == pytest.approx(g[t, c], rel=1e-6, abs=1e-7)
+
+
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(82, 128, 16, 8, 3, 16), (83, 160, 32, 32, 4, 8)])
+def test_noncausal_backward_matches_dense_autograd(seed, L, d, nb, nh, m):
+    q, v, rot, do = _rand_problem(seed, L, d, nh, nb, scale_q=1.3)
+    scale = 1 / np.sqrt(d)
+    res = ora.head(q, v, rot, nb, m, scale, dout=do, causal=False)
+    allowed = bf.union_mask(res["buckets"], m, causal=False) & ~np.eye(L, dtype=bool)
+    empty = ~allowed.any(axis=1)
+    allowed[empty, np.nonzero(empty)[0]] = True
+    qt = torch.tensor(q, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    logits = (scale * qt @ kt.T).masked_fill(~torch.from_numpy(allowed), float("-inf"))
+    out = torch.softmax(logits, dim=-1) @ vt
+    (out * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(res["dq"], qt.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(res["dv"], vt.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(res["dv"].sum(axis=0), do.sum(axis=0), rtol=1e-11, atol=1e-11)
+
+
 # ----------------------------------------------------------------------------- inputs
 
 def test_generator_reproducible_and_margin():
