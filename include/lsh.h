@@ -5,9 +5,9 @@
  * "Reformer: The Efficient Transformer" (Kitaev, Kaiser, Levskaya): angular
  * LSH by random rotation, a stable sort by (bucket, position), attention over
  * chunks of the sorted order (each chunk sees itself and one chunk back, with
- * causal, self and duplicate masking), a logsumexp-weighted combine over the
- * hash rounds with the unsort, and the backward pass through the fixed
- * permutation.
+ * self and duplicate masking, and causal masking unless the problem is
+ * non-causal), a logsumexp-weighted combine over the hash rounds with the
+ * unsort, and the backward pass through the fixed permutation.
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers to contiguous row-major arrays,
@@ -64,8 +64,13 @@ typedef enum {
  *   n_hashes: nh >= 1 hash rounds (<= 16).
  *   n_buckets: nb, even, 2 <= nb <= 4096; nb = 2 * columns of the rotation.
  *   chunk_len: m, 1 <= m, L % m == 0 (m == L gives one chunk).
- *   causal: must be 1 (the pages spell out causal masking only); 0 returns
- *       LSH_ERR_UNSUPPORTED.
+ *   causal: 1 = causal sets ("Reformer" §2: a query attends to no position
+ *       after its own); 0 = non-causal (encoder) sets, which the paper does
+ *       not spell out and are read here as the causal ones without that one
+ *       condition: same bucket, own chunk or the one before (no look-ahead
+ *       into the next chunk, no wrap-around from the first chunk to the
+ *       last), self only when nothing else is there.  Other values:
+ *       LSH_ERR_INVALID.
  *   scale: the softmax scale applied to q_i . k_j (1/sqrt(d) for standard
  *       scaled dot-product attention).
  *   dtype: element type of q, v, rot, out, dout, dq, dv and o_rounds.
@@ -117,7 +122,11 @@ int lsh_hash(const lsh_problem_t *prob, const void *q, const void *rot, int32_t 
  *           sorted index of the round's attended set of t (same bucket, not
  *           after t, own chunk or the one before):
  *           max(first sorted index of t's bucket, (inv[t]/m - 1) * m).
- *           The set is exactly the sorted range [win_lo[t], inv[t]].
+ *           The causal set is exactly the sorted range [win_lo[t], inv[t]].
+ *           The non-causal set starts at the same index and ends at the last
+ *           sorted index of t's bucket inside t's chunk; lsh_attn_fwd and
+ *           the backwards derive that end from perm and win_lo, so the
+ *           output of lsh_sort is the same for both kinds of problem.
  *   ws      workspace of lsh_workspace_bytes(prob, LSH_WS_SORT) bytes.
  * Bucket values outside [0, nb) are undefined behaviour (not checked on the
  * device).
@@ -127,8 +136,9 @@ int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, i
 
 /*
  * lsh_attn_fwd -- per-round chunked attention ("Reformer" §2 and App. A):
- * in round r, query t attends to the members of its attended set other than
- * itself, with logits scale * q_t . k_j, k_j = q_j / |q_j|.  A member j that
+ * in round r, query t attends to the members of its attended set (causal or
+ * not, see lsh_problem_t) other than itself, with logits
+ * scale * q_t . k_j, k_j = q_j / |q_j|.  A member j that
  * already belongs to the attended set of t in an earlier round is masked
  * (the duplicate correction of App. A, folded into the mask), so that the
  * rounds together count every member of the union once.  Outputs are
@@ -142,7 +152,8 @@ int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, i
  *   ws         workspace of lsh_workspace_bytes(prob, LSH_WS_FWD) bytes, or
  *              of LSH_WS_TRAIN bytes to keep what the forward derives from
  *              q, perm, inv and win_lo (packed sorted records, inverse norms,
- *              per-block key data) for lsh_attn_bwd_saved.
+ *              per-block key data; for non-causal problems also the window
+ *              ends) for lsh_attn_bwd_saved.
  */
 int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const int32_t *perm,
                  const int32_t *inv, const int32_t *win_lo, void *o_rounds, float *lse_rounds,
@@ -226,8 +237,9 @@ typedef enum {
     LSH_KERNEL_SORT_SCAN = 2,   /* lsh_sort: offsets of (tile, bucket) runs         */
     LSH_KERNEL_SORT_SCATTER = 3,/* lsh_sort: stable ranks, perm / inv / win_lo      */
     LSH_KERNEL_PREP = 4,        /* lsh_attn_fwd / lsh_attn_bwd: packed records,
-                                   inverse norms (and dO . O in the backward;
-                                   only that in lsh_attn_bwd_saved)                */
+                                   inverse norms, non-causal window ends (and
+                                   dO . O in the backward; only that in
+                                   lsh_attn_bwd_saved)                             */
     LSH_KERNEL_FWD = 5,         /* lsh_attn_fwd: per-round chunk attention          */
     LSH_KERNEL_COMBINE = 6,     /* lsh_combine                                      */
     LSH_KERNEL_BWD_DQ = 7,      /* lsh_attn_bwd: query-side gradient per round      */

@@ -9,7 +9,9 @@
 // duplicates are masked; per-round outputs combined by logsumexp weights).
 //
 // Round r of query i (sorted index s) attends to the sorted range
-// [s - w, s - 1], w = s - win_lo.  A member j is skipped in round r when it
+// [s - w, s - 1], w = s - win_lo; without causality (encoder attention) to
+// [s - w, hi] minus s itself, hi being the last row of its bucket in its
+// chunk (see window_kernel).  A member j is skipped in round r when it
 // is also in the attended set of i in an earlier round r' < r, so that every
 // member of the union is counted in exactly one round (the first that holds
 // it).  Lanes of a wave take keys for the scores and head-dim components for
@@ -78,6 +80,38 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *
     }
 }
 
+// Non-causal window records: for every (b, h, round) and sorted row s, the
+// attended set is the sorted range [s - w(s), hi(s)], hi(s) being the last
+// row of s's bucket inside s's chunk (same bucket, own chunk or the one
+// before, with no "not after the query" condition).  Along the sorted order
+// the window starts s' - w(s') do not decrease, and a later row s' of s's
+// chunk starts its window at or before s exactly when it is in s's bucket
+// (a later bucket starts after s), so hi(s) is found by bisection over
+// [s, end of chunk).  Writes wmeta[tok nh + r] = hi | (hi - win_lo) << 16.
+__global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, size_t total,
+                                                          const uint32_t *__restrict__ srec,
+                                                          uint32_t *__restrict__ wmeta)
+{
+    const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= total)
+        return;
+    const size_t seg = idx / L;   // bh * nh + r
+    const int s = (int)(idx % L), r = (int)(seg % nh);
+    const size_t bh = seg / nh;
+    const uint32_t *sr = srec + seg * L;
+    const uint32_t rec = sr[s];
+    const int lo = s - (int)rec_hi(rec);
+    int a = s, b = min((s / m + 1) * m, L) - 1;   // hi(s) in [a, b]
+    while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if (mid - (int)rec_hi(sr[mid]) <= s)
+            a = mid;
+        else
+            b = mid - 1;
+    }
+    wmeta[(bh * L + rec_lo(rec)) * nh + r] = (uint32_t)a | ((uint32_t)(a - lo) << 16);
+}
+
 // Dot of a per-lane row (global) with a wave-distributed vector whose
 // component c sits in lane c % 64 of reg[c / 64].
 template <typename T, int D>
@@ -96,14 +130,35 @@ __device__ __forceinline__ float dot_row_bcast(const T *row, const float (&reg)[
 }
 
 // Is key j masked in round r for query i because it belongs to i's
-// attended set in an earlier round?
+// attended set in an earlier round?  wm_i: i's non-causal window records, or
+// null for causal problems.
 __device__ __forceinline__ bool owned_earlier(const uint32_t *__restrict__ meta_i,
+                                              const uint32_t *__restrict__ wm_i,
                                               const uint32_t *__restrict__ meta_j, int r)
 {
     bool hit = false;
-    for (int rr = 0; rr < r; ++rr)
-        hit |= in_window(meta_i[rr], rec_lo(meta_j[rr]));
+    if (wm_i) {
+        for (int rr = 0; rr < r; ++rr)
+            hit |= in_span(wm_i[rr], rec_lo(meta_j[rr]));
+    } else {
+        for (int rr = 0; rr < r; ++rr)
+            hit |= in_window(meta_i[rr], rec_lo(meta_j[rr]));
+    }
     return hit;
+}
+
+// Round-r key range of a sorted query row s: n candidates from sorted index
+// lo on (causal: [s - w, s - 1]; non-causal: [s - w, hi], where s itself is
+// skipped by the caller).
+struct KeyRange {
+    int lo, n;
+};
+__device__ __forceinline__ KeyRange key_range(int s, int w, const uint32_t *wm_i, int r)
+{
+    if (!wm_i)
+        return KeyRange{s - w, w};
+    const uint32_t x = wm_i[r];
+    return KeyRange{(int)rec_lo(x) - (int)rec_hi(x), (int)rec_hi(x) + 1};
 }
 
 // ---------------------------------------------------------------------------
@@ -113,6 +168,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scale, const T *__restrict__ q,
                                                        const T *__restrict__ v, const uint32_t *__restrict__ meta,
                                                        const uint32_t *__restrict__ srec,
+                                                       const uint32_t *__restrict__ wmeta,
                                                        const float *__restrict__ rnorm, T *__restrict__ o_rounds,
                                                        float *__restrict__ lse_rounds)
 {
@@ -128,6 +184,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
         const uint32_t rec = sr[s];
         const int i = (int)rec_lo(rec), w = (int)rec_hi(rec);
         const uint32_t *mi = meta + (tok0 + i) * nh;
+        const uint32_t *wi = wmeta ? wmeta + (tok0 + i) * nh : nullptr;
+        const KeyRange kr0 = key_range(s, w, wi, r);
         float qreg[NC], acc[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -136,13 +194,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
             acc[c] = 0.f;
         }
         float M = -INFINITY, l = 0.f;
-        for (int kb = 0; kb < w; kb += kWave) {
+        for (int kb = 0; kb < kr0.n; kb += kWave) {
             const int idx = kb + lane;
-            bool valid = idx < w;
-            const uint32_t kr = valid ? sr[s - w + idx] : rec;
+            bool valid = idx < kr0.n && kr0.lo + idx != s;
+            const uint32_t kr = valid ? sr[kr0.lo + idx] : rec;
             const int j = (int)rec_lo(kr);
             if (valid)
-                valid = !owned_earlier(mi, meta + (tok0 + j) * nh, r);
+                valid = !owned_earlier(mi, wi, meta + (tok0 + j) * nh, r);
             const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
             const float logit = valid ? dp * scale * rnorm[tok0 + j] : -INFINITY;
             const float bm = wave_max(logit);
@@ -156,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
             for (int c = 0; c < NC; ++c)
                 acc[c] *= corr;
             M = Mn;
-            const int nk = min(kWave, w - kb);
+            const int nk = min(kWave, kr0.n - kb);
             for (int kk = 0; kk < nk; ++kk) {
                 const float pk = readlane(p, kk);
                 if (pk == 0.f)
@@ -270,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
                                                           const float *__restrict__ Dvec,
                                                           const uint32_t *__restrict__ meta,
                                                           const uint32_t *__restrict__ srec,
+                                                          const uint32_t *__restrict__ wmeta,
                                                           const float *__restrict__ rnorm,
                                                           float *__restrict__ dq_part)
 {
@@ -285,6 +344,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
         const uint32_t rec = sr[s];
         const int i = (int)rec_lo(rec), w = (int)rec_hi(rec);
         const uint32_t *mi = meta + (tok0 + i) * nh;
+        const uint32_t *wi = wmeta ? wmeta + (tok0 + i) * nh : nullptr;
+        const KeyRange kr0 = key_range(s, w, wi, r);
         const float lse_i = lse[tok0 + i], D_i = Dvec[tok0 + i];
         float qreg[NC], goreg[NC], acc[NC];
 #pragma unroll
@@ -294,19 +355,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
             goreg[c] = e < D ? ld(dout, (tok0 + i) * D + e) : 0.f;
             acc[c] = 0.f;
         }
-        for (int kb = 0; kb < w; kb += kWave) {
+        for (int kb = 0; kb < kr0.n; kb += kWave) {
             const int idx = kb + lane;
-            bool valid = idx < w;
-            const uint32_t kr = valid ? sr[s - w + idx] : rec;
+            bool valid = idx < kr0.n && kr0.lo + idx != s;
+            const uint32_t kr = valid ? sr[kr0.lo + idx] : rec;
             const int j = (int)rec_lo(kr);
             if (valid)
-                valid = !owned_earlier(mi, meta + (tok0 + j) * nh, r);
+                valid = !owned_earlier(mi, wi, meta + (tok0 + j) * nh, r);
             const float rn = rnorm[tok0 + j];
             const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
             const float dv = dot_row_bcast<T, D>(v + (tok0 + j) * D, goreg);
             const float p = valid ? expf(dp * scale * rn - lse_i) : 0.f;
             const float coef = scale * p * (dv - D_i) * rn;
-            const int nk = min(kWave, w - kb);
+            const int nk = min(kWave, kr0.n - kb);
             for (int kk = 0; kk < nk; ++kk) {
                 const float ck = readlane(coef, kk);
                 if (ck == 0.f)
@@ -335,7 +396,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
 // backward, key side: dk_j and dv_j of round r (wave per sorted key row).
 // The queries whose round-r set holds key j (sorted index s) are the sorted
 // rows s' > s with s' - w(s') <= s; win_lo is non-decreasing along the sorted
-// order, so they form a prefix of s+1, s+2, ...
+// order, so they form a prefix of s+1, s+2, ...  Without causality also the
+// rows s' < s with hi(s') >= s (same bucket and chunk), all within
+// [s - w(s), s - 1].
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float scale, const T *__restrict__ q,
@@ -344,6 +407,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
                                                            const float *__restrict__ Dvec,
                                                            const uint32_t *__restrict__ meta,
                                                            const uint32_t *__restrict__ srec,
+                                                           const uint32_t *__restrict__ wmeta,
                                                            const float *__restrict__ rnorm,
                                                            float *__restrict__ dk_part, float *__restrict__ dv_part)
 {
@@ -356,7 +420,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
         const int s = (blockIdx.x * kWaves + wave) * kRowsPerWave + k;
         if (s >= L)
             break;
-        const int j = (int)rec_lo(sr[s]);
+        const uint32_t krec = sr[s];
+        const int j = (int)rec_lo(krec);
         const uint32_t *mj = meta + (tok0 + j) * nh;
         const float rn = rnorm[tok0 + j];
         float kreg[NC], vreg[NC], dk[NC], dv[NC];
@@ -367,24 +432,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
             vreg[c] = e < D ? ld(v, (tok0 + j) * D + e) : 0.f;
             dk[c] = dv[c] = 0.f;
         }
-        for (int qb = s + 1; qb < L; qb += kWave) {
-            const int si = qb + lane;
-            bool inwin = false;
-            int i = j;
-            if (si < L) {
-                const uint32_t qrec = sr[si];
-                i = (int)rec_lo(qrec);
-                inwin = (si - (int)rec_hi(qrec)) <= s;
-            }
-            const bool more = __ballot(!inwin) == 0ull;  // whole batch in window: look further
-            bool valid = inwin;
+        // one batch of candidate queries (lane: query i, valid if it attends j)
+        auto batch = [&](bool valid, int i, int nk) {
             if (valid)
-                valid = !owned_earlier(meta + (tok0 + i) * nh, mj, r);
+                valid = !owned_earlier(meta + (tok0 + i) * nh, wmeta ? wmeta + (tok0 + i) * nh : nullptr, mj, r);
             const float dp = dot_row_bcast<T, D>(q + (tok0 + i) * D, kreg);
             const float dg = dot_row_bcast<T, D>(dout + (tok0 + i) * D, vreg);
             const float p = valid ? expf(dp * scale - lse[tok0 + i]) : 0.f;
             const float g = valid ? scale * p * (dg - Dvec[tok0 + i]) : 0.f;
-            const int nk = min(kWave, L - qb);
             for (int kk = 0; kk < nk; ++kk) {
                 const float pk = readlane(p, kk);
                 if (pk == 0.f)
@@ -401,6 +456,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
                     }
                 }
             }
+        };
+        if (wmeta) {
+            // earlier rows of j's bucket in j's chunk (non-causal only)
+            for (int qb = s - (int)rec_hi(krec); qb < s; qb += kWave) {
+                const int si = qb + lane;
+                bool ok = false;
+                int i = j;
+                if (si < s) {
+                    i = (int)rec_lo(sr[si]);
+                    ok = (int)rec_lo(wmeta[(tok0 + i) * nh + r]) >= s;
+                }
+                batch(ok, i, min(kWave, s - qb));
+            }
+        }
+        for (int qb = s + 1; qb < L; qb += kWave) {
+            const int si = qb + lane;
+            bool inwin = false;
+            int i = j;
+            if (si < L) {
+                const uint32_t qrec = sr[si];
+                i = (int)rec_lo(qrec);
+                inwin = (si - (int)rec_hi(qrec)) <= s;
+            }
+            const bool more = __ballot(!inwin) == 0ull;  // whole batch in window: look further
+            batch(inwin, i, min(kWave, L - qb));
             if (!more)
                 break;
         }
@@ -424,6 +504,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int ntok, const T *__restrict__ q,
                                                               const T *__restrict__ dout,
                                                               const uint32_t *__restrict__ meta,
+                                                              const uint32_t *__restrict__ wmeta,
                                                               const float *__restrict__ rnorm,
                                                               const float *__restrict__ dq_part,
                                                               const float *__restrict__ dk_part,
@@ -442,7 +523,8 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int
         aq[c] = ak[c] = av[c] = 0.f;
     bool alone = true;
     for (int r = 0; r < nh; ++r) {
-        alone &= rec_hi(meta[(size_t)tok * nh + r]) == 0u;
+        // no member but itself: w = 0 (causal) or span = 0 (non-causal)
+        alone &= rec_hi((wmeta ? wmeta : meta)[(size_t)tok * nh + r]) == 0u;
         const size_t row = (((size_t)bh * nh + r) * L + t) * D;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -481,25 +563,31 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int
 
 template <typename T, int D>
 hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32_t *win_lo, uint32_t *meta,
-                   uint32_t *srec, float *rnorm, const void *out, const void *dout, float *Dv, hipStream_t st)
+                   uint32_t *srec, uint32_t *wmeta, float *rnorm, const void *out, const void *dout, float *Dv,
+                   hipStream_t st)
 {
     constexpr int TPB = kThreads / (D / 8);
     dim3 grid((P.L + TPB - 1) / TPB, P.BH());
     ProfScope prof(LSH_KERNEL_PREP, st);
     hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, (const T *)q, inv, win_lo,
                        meta, srec, rnorm, (const T *)out, (const T *)dout, Dv);
+    if (meta && wmeta) {
+        const size_t total = (size_t)P.BH() * P.nh * P.L;
+        hipLaunchKernelGGL(window_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                           st, P.L, P.nh, P.m, total, srec, wmeta);
+    }
     return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
-                  const float *rnorm, void *o_rounds, float *lse_rounds, hipStream_t st)
+                  const uint32_t *wmeta, const float *rnorm, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
     ProfScope prof(LSH_KERNEL_FWD, st);
     hipLaunchKernelGGL((fwd_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                       (const T *)v, meta, srec, rnorm, (T *)o_rounds, lse_rounds);
+                       (const T *)v, meta, srec, wmeta, rnorm, (T *)o_rounds, lse_rounds);
     return hipGetLastError();
 }
 
@@ -527,21 +615,22 @@ hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o
 }
 
 template <typename T, int D>
-hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const float *rnorm,
-                     const float *dq_part, const float *dk_part, const float *dv_part, void *dq, void *dv,
-                     hipStream_t st);
+hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const uint32_t *wmeta,
+                     const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part, void *dq,
+                     void *dv, hipStream_t st);
 
 template <typename T, int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
-                  const float *Dv, const uint32_t *meta, const uint32_t *srec, const float *rnorm, float *dq_part,
-                  float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t st)
+                  const float *Dv, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
+                  const float *rnorm, float *dq_part, float *dk_part, float *dv_part, void *dq, void *dv,
+                  hipStream_t st)
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dq_part);
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, rnorm, dq_part);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -549,22 +638,22 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DKV, st);
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, rnorm, dk_part, dv_part);
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, rnorm, dk_part, dv_part);
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return reduce_go<T, D>(P, q, dout, meta, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
+    return reduce_go<T, D>(P, q, dout, meta, wmeta, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
 }
 
 template <typename T, int D>
-hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const float *rnorm,
-                     const float *dq_part, const float *dk_part, const float *dv_part, void *dq, void *dv,
-                     hipStream_t st)
+hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const uint32_t *wmeta,
+                     const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part, void *dq,
+                     void *dv, hipStream_t st)
 {
     const int ntok = P.BH() * P.L;
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
     hipLaunchKernelGGL((bwd_reduce_kernel<T, D>), dim3((ntok + kWaves - 1) / kWaves), dim3(kThreads), 0, st,
-                       P.L, P.nh, ntok, (const T *)q, (const T *)dout, meta, rnorm, dq_part, dk_part, dv_part,
+                       P.L, P.nh, ntok, (const T *)q, (const T *)dout, meta, wmeta, rnorm, dq_part, dk_part, dv_part,
                        (T *)dq, (T *)dv);
     return hipGetLastError();
 }
@@ -586,18 +675,18 @@ hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint3
 }  // namespace
 
 hipError_t launch_prep(const Dims &P, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
-                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, float *rnorm, const void *out,
-                       const void *dout, float *Dv, hipStream_t st)
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, float *rnorm,
+                       const void *out, const void *dout, float *Dv, hipStream_t st)
 {
     (void)perm;
-    LSH_DISPATCH(dtype, P.d, (prep_go<T, D>(P, q, inv, win_lo, meta, srec, rnorm, out, dout, Dv, st)));
+    LSH_DISPATCH(dtype, P.d, (prep_go<T, D>(P, q, inv, win_lo, meta, srec, wmeta, rnorm, out, dout, Dv, st)));
 }
 
 hipError_t launch_attn_fwd(const Dims &P, int dtype, const void *q, const void *v, const uint32_t *meta,
-                           const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
-                           hipStream_t st)
+                           const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, void *o_rounds,
+                           float *lse_rounds, hipStream_t st)
 {
-    LSH_DISPATCH(dtype, P.d, (fwd_go<T, D>(P, q, v, meta, srec, rnorm, o_rounds, lse_rounds, st)));
+    LSH_DISPATCH(dtype, P.d, (fwd_go<T, D>(P, q, v, meta, srec, wmeta, rnorm, o_rounds, lse_rounds, st)));
 }
 
 hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v, const void *o_rounds,
@@ -606,20 +695,13 @@ hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v
     LSH_DISPATCH(dtype, P.d, (combine_go<T, D>(P, q, v, o_rounds, lse_rounds, out, lse, st)));
 }
 
-hipError_t launch_bwd_reduce(const Dims &P, int dtype, const void *q, const void *dout, const uint32_t *meta,
-                             const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,
-                             void *dq, void *dv, hipStream_t st)
-{
-    LSH_DISPATCH(dtype, P.d, (reduce_go<T, D>(P, q, dout, meta, rnorm, dq_part, dk_part, dv_part, dq, dv, st)));
-}
-
 hipError_t launch_attn_bwd(const Dims &P, int dtype, const void *q, const void *v, const void *dout,
                            const float *lse, const float *Dv, const uint32_t *meta, const uint32_t *srec,
-                           const float *rnorm, float *dq_part, float *dk_part, float *dv_part, void *dq, void *dv,
-                           hipStream_t st)
+                           const uint32_t *wmeta, const float *rnorm, float *dq_part, float *dk_part, float *dv_part,
+                           void *dq, void *dv, hipStream_t st)
 {
-    LSH_DISPATCH(dtype, P.d,
-                 (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, rnorm, dq_part, dk_part, dv_part, dq, dv, st)));
+    LSH_DISPATCH(dtype, P.d, (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, wmeta, rnorm, dq_part, dk_part,
+                                           dv_part, dq, dv, st)));
 }
 
 }  // namespace lsh

@@ -200,10 +200,16 @@ __device__ __forceinline__ void clear_hits(bool (&ok)[16], const uint32_t (&hit)
 
 // One wave per tile of 32 sorted rows: lanes 0..31 fill the key tile (unless
 // ktile is null), lanes 32..63 the query tile (unless qtile is null); every
-// field is written as one contiguous run.
+// field is written as one contiguous run.  Query windows: causal problems
+// store w for the tile's round and (s - 1, w) for the earlier ones (the set
+// without the query is [s - w, s - 1]); non-causal problems (wmeta not null)
+// store w | (hi - s) << 8 for the tile's round (w < 256 and hi - s < 128 as
+// chunks are at most 128 rows) and (hi, span + 1) for the earlier ones (the
+// set with the query is [hi - span, hi]).
 __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int ntiles, float scale_log2,
                                                              const uint32_t *__restrict__ srec,
                                                              const uint32_t *__restrict__ meta,
+                                                             const uint32_t *__restrict__ wmeta,
                                                              const float *__restrict__ rnorm,
                                                              const float *__restrict__ lse,
                                                              const float *__restrict__ Dvec,
@@ -231,11 +237,22 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
         uint8_t *qt = qtile + (size_t)tile * qtile_stride(nh);
         reinterpret_cast<float *>(qt)[k] = lse[tok] * kLog2e;
         reinterpret_cast<float *>(qt + 128)[k] = Dvec[tok];
-        reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
-        for (int rr = 0; rr < nr; ++rr) {
-            const uint32_t mr = m[rr];
-            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(rec_lo(mr) - 1u);
-            reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)rec_hi(mr);
+        if (wmeta) {
+            const uint32_t *wm = wmeta + tok * nh;
+            const uint32_t u = rec_lo(wm[r]) - (uint32_t)(blk * kBlk + k);
+            reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)(rec_hi(rec) | (u << 8));
+            for (int rr = 0; rr < nr; ++rr) {
+                const uint32_t x = wm[rr];
+                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)rec_lo(x);
+                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)(rec_hi(x) + 1u);
+            }
+        } else {
+            reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
+            for (int rr = 0; rr < nr; ++rr) {
+                const uint32_t mr = m[rr];
+                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(rec_lo(mr) - 1u);
+                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)rec_hi(mr);
+            }
         }
     }
 }
@@ -872,8 +889,9 @@ constexpr bool kv_sk_in_regs() { return D < 128 || NR <= 3; }
 // One query block against this wave's 16 keys.  The queries' windows, lse
 // and D are read with the operand rows, before any arithmetic.  skp[rr]:
 // this lane's key's sorted index in round rr (NR >= r), both halves of a
-// pair, or (see kv_sk_in_regs) entry ke of the key tile kt.
-template <int D, int NR>
+// pair, or (see kv_sk_in_regs) entry ke of the key tile kt.  NC: non-causal
+// windows (the query tile layout of tile_prep_kernel).
+template <int D, int NR, bool NC>
 __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt, const uint8_t *T, const uint8_t *kt,
                                           int ke, int r, int qb, int sk, int g, int c, int lane, float krn2,
                                           float scale, const uint32_t (&skp)[NR], const bf16x8_t (&kop)[D / 32],
@@ -917,8 +935,15 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
                            (int)(w4[u].y >> 16)};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int sq = qb + 16 * u + 4 * g + t;   // key in [sq - w, sq)
-            ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
+            const int sq = qb + 16 * u + 4 * g + t;
+            if constexpr (NC) {
+                // key in [sq - w, sq + hi - sq], not the query itself
+                const int w = wv[t] & 0xff, n = w + (wv[t] >> 8) + 1;
+                ok[4 * u + t] = (unsigned)(sk - sq + w) < (unsigned)n && sk != sq;
+            } else {
+                // key in [sq - w, sq)
+                ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
+            }
         }
     }
     if (r > 0) {
@@ -1024,9 +1049,9 @@ __device__ __forceinline__ void dkv_store(bf16 *dkr_part, bf16 *dv_part, size_t 
     store_row16<D>(dv_part + row, g, 1.f, dva);
 }
 
-template <int D, int NR>
+template <int D, int NR, bool NC>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_stream_kernel(
-    int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
+    int L, int nh, int T, int m, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
     const uint8_t *__restrict__ qtile, bf16 *__restrict__ dkr_part, bf16 *__restrict__ dv_part)
 {
@@ -1143,10 +1168,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         auto work = [&](int b) __attribute__((always_inline)) {
             const int qb = k0 + b * kBlk, st = (a0 + b) % kStreamStages;
             const int blk_lo = qb - (int)rec_hi(recs[qb % kRecRing]);
-            if (qb + kBlk - 1 <= wk0 || blk_lo > wk0 + 15)
+            // causal: a block entirely at or before the keys sees none of
+            // them; non-causal: one entirely before the chunk of the first key
+            // (m is a power of two)
+            const bool before = NC ? qb + kBlk - 1 < (wk0 & -m) : qb + kBlk - 1 <= wk0;
+            if (before || blk_lo > wk0 + 15)
                 return;
-            dkv_block<D, NR>(Qs[st], Gs[st], Ts[st], kt, ke, r, qb, sk, g, c, lane, krn2, scale, skp, kop, vop, dka,
-                             dva);
+            dkv_block<D, NR, NC>(Qs[st], Gs[st], Ts[st], kt, ke, r, qb, sk, g, c, lane, krn2, scale, skp, kop, vop,
+                                 dka, dva);
         };
         for (int b = 0; b < 4 && b < nb; ++b)
             work(b);
@@ -1198,12 +1227,12 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // blocks (and the next tile's query rows are loaded into registers) while
 // the tile's own four blocks are worked on.
 
-template <int D, bool BWD, int NR>
+template <int D, bool BWD, int NR, bool NC>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(
     int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dvec,
-    const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
-    bf16 *__restrict__ out, float *__restrict__ lse_rounds)
+    const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const uint32_t *__restrict__ wmeta,
+    const uint8_t *__restrict__ ktile, bf16 *__restrict__ out, float *__restrict__ lse_rounds)
 {
     __shared__ __align__(16) uint16_t Ks[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
@@ -1247,11 +1276,15 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
     // this lane's query of tile t (16 per wave) in registers; its q row is
     // not among them: the tile's own key blocks hold the query rows (shared
-    // QK), so the operand is read from LDS once the tile's blocks are in
+    // QK), so the operand is read from LDS once the tile's blocks are in.
+    // Windows: causal, the keys [s - qw, s - 1] of the round and the records
+    // (s, w) of the earlier rounds; non-causal (NC), the keys [qhi - qw + 1,
+    // qhi] of the round (the query itself skipped) and the window records
+    // (hi, span) of the earlier rounds.
     struct QRegs {
         bf16x8_t gop[D / 32];
         uint32_t qm[NR];   // the query's records in the earlier rounds (NR >= r)
-        int qpos, qw;
+        int qpos, qw, qhi;
         float lse2, Di;
     };
     auto load_q = [&](int t, QRegs &R) __attribute__((always_inline)) {
@@ -1260,6 +1293,11 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         R.qpos = (int)rec_lo(rec);
         R.qw = (int)rec_hi(rec);
         const size_t tok = tok0 + R.qpos;
+        if constexpr (NC) {
+            const uint32_t x = wmeta[tok * nh + r];
+            R.qhi = (int)rec_lo(x);
+            R.qw = (int)rec_hi(x) + 1;
+        }
         if constexpr (BWD) {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
@@ -1270,8 +1308,12 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr)
             if (rr < r)
-                R.qm[rr] = meta[tok * nh + rr];
+                R.qm[rr] = (NC ? wmeta : meta)[tok * nh + rr];
     };
+    // the earlier-round test of a query record: key sorted index sk hits
+    // when (x - sk) mod 2^16 < n, as pairs of 16-bit halves
+    auto win_x = [](uint32_t qm) { return bcast16(NC ? rec_lo(qm) : rec_lo(qm) - 1u); };
+    auto win_n = [](uint32_t qm) { return bcast16(NC ? rec_hi(qm) + 1u : rec_hi(qm)); };
 
     // prologue: records [s0 - 128, s0 + 256), then the first tile's eight blocks and query rows
     if (tid < kStreamStages)
@@ -1339,24 +1381,27 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
         const int wq0 = s0 + qg * 16;
         const int sq = wq0 + c;
-        const int qlo = sq - cur.qw;
-        const int wlo = __builtin_amdgcn_readlane(qlo, 0);   // window starts do not decrease
+        const int qlo = NC ? cur.qhi - cur.qw + 1 : sq - cur.qw;
+        // window starts and ends do not decrease along the sorted order: the
+        // wave's keys lie in [wlo, whi]
+        const int wlo = __builtin_amdgcn_readlane(qlo, 0);
+        const int whi = NC ? __builtin_amdgcn_readlane(cur.qhi, 15) : wq0 + 14;
 
-        // earlier-round window tests: (start - 1, length) of the query's set
-        // in round rr, both halves of a packed pair (kept for up to seven
-        // rounds, formed per block from LDS beyond that)
+        // earlier-round window tests: (end, length) of the query's set in
+        // round rr (see win_x), both halves of a packed pair (kept for up to
+        // seven rounds, formed per block from LDS beyond that)
         uint32_t si1p[kKeepWin ? NR : 1], wp[kKeepWin ? NR : 1];
         if constexpr (kKeepWin) {
 #pragma unroll
             for (int rr = 0; rr < NR; ++rr) {
-                si1p[rr] = bcast16(rec_lo(cur.qm[rr]) - 1u);
-                wp[rr] = bcast16(rec_hi(cur.qm[rr]));
+                si1p[rr] = win_x(cur.qm[rr]);
+                wp[rr] = win_n(cur.qm[rr]);
             }
         }
 
         auto work = [&](int a) __attribute__((always_inline)) {
             const int kb = a * kBlk, st = a % kStreamStages;
-            if (kb > wq0 + 14 || kb + kBlk - 1 < wlo)
+            if (kb > whi || kb + kBlk - 1 < wlo)
                 return;
             const uint16_t *K = Ks[st], *V = Vs[st];
             const float *rnk = reinterpret_cast<const float *>(Kts[st]);
@@ -1423,8 +1468,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
             bool ok[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                ok[e] = (unsigned)(kb + 16 * (e / 4) + 4 * g + (e % 4) - qlo) < (unsigned)cur.qw;
+            for (int e = 0; e < 8; ++e) {
+                const int key = kb + 16 * (e / 4) + 4 * g + (e % 4);
+                ok[e] = (unsigned)(key - qlo) < (unsigned)cur.qw && (!NC || key != sq);
+            }
             if (r > 0) {
                 uint32_t hit[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -1434,8 +1481,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                         for (int kk = 0; kk < 2; ++kk) {
                             const uint2 k2 = kEarlySk ? kp[kEarlySk ? rr : 0][kk] : read_sk(rr, kk);
                             const uint32_t qmr = kKeepWin ? 0u : qmL[kKeepWin ? 0 : wave][kKeepWin ? 0 : rr][c];
-                            const uint32_t s1 = kKeepWin ? si1p[kKeepWin ? rr : 0] : bcast16(rec_lo(qmr) - 1u);
-                            const uint32_t w1 = kKeepWin ? wp[kKeepWin ? rr : 0] : bcast16(rec_hi(qmr));
+                            const uint32_t s1 = kKeepWin ? si1p[kKeepWin ? rr : 0] : win_x(qmr);
+                            const uint32_t w1 = kKeepWin ? wp[kKeepWin ? rr : 0] : win_n(qmr);
                             hit[2 * kk] |= win_hits2(s1, w1, k2.x);
                             hit[2 * kk + 1] |= win_hits2(s1, w1, k2.y);
                         }
@@ -1560,6 +1607,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
                                                           const float *__restrict__ rnorm,
                                                           const bf16 *__restrict__ dout,
                                                           const uint32_t *__restrict__ meta,
+                                                          const uint32_t *__restrict__ wmeta,
                                                           const bf16 *__restrict__ dq_part,
                                                           const bf16 *__restrict__ dkr_part,
                                                           const bf16 *__restrict__ dv_part, bf16 *__restrict__ dq,
@@ -1582,7 +1630,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
             xq[r] = ld16(dq_part + off);
             xk[r] = ld16(dkr_part + off);
             xv[r] = ld16(dv_part + off);
-            alone = alone && rec_hi(meta[(size_t)tok * nh + r]) == 0u;
+            // no member but itself: w = 0 (causal) or span = 0 (non-causal)
+            alone = alone && rec_hi((wmeta ? wmeta : meta)[(size_t)tok * nh + r]) == 0u;
         }
     float qv[8];
     load8(q + (size_t)tok * D + ch * 8, qv);
@@ -1639,19 +1688,19 @@ int stream_run_tiles(int nt, int segs)
 int max_window(const Dims &P) { return (2 * P.m + kBlk - 1) / kBlk * kBlk; }
 
 // The query-side stream kernel for the bound NR on the earlier rounds
-// (n_hashes - 1 rounded up to 1, 3, 7 or 13).
-template <int D, bool BWD>
-void q_stream_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-                 const uint32_t *meta, const uint32_t *srec, const uint8_t *ktile, void *out, float *lse_rounds,
-                 hipStream_t st)
+// (n_hashes - 1 rounded up to 1, 3, 7 or 13), causal or not.
+template <int D, bool BWD, bool NC>
+void q_stream_nc(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
+                 const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *ktile, void *out,
+                 float *lse_rounds, hipStream_t st)
 {
     const int nt = P.L / kRows, segs = P.BH() * P.nh;
     const int T = stream_run_tiles(nt, segs);
     const dim3 grid(segs * ((nt + T - 1) / T));
-#define LSH_QSTREAM(NR)                                                                                           \
-    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,       \
-                       (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile, (bf16 *)out, \
-                       lse_rounds)
+#define LSH_QSTREAM(NR)                                                                                            \
+    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR, NC>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,    \
+                       (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, wmeta, ktile,     \
+                       (bf16 *)out, lse_rounds)
     if (P.nh <= 2)
         LSH_QSTREAM(1);
     else if (P.nh <= 4)
@@ -1663,13 +1712,26 @@ void q_stream_go(const Dims &P, const void *q, const void *v, const void *dout, 
 #undef LSH_QSTREAM
 }
 
+template <int D, bool BWD>
+void q_stream_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
+                 const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *ktile, void *out,
+                 float *lse_rounds, hipStream_t st)
+{
+    if (P.causal)
+        q_stream_nc<D, BWD, false>(P, q, v, dout, lse, Dv, meta, srec, nullptr, ktile, out, lse_rounds, st);
+    else
+        q_stream_nc<D, BWD, true>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, out, lse_rounds, st);
+}
+
+// (non-causal problems take the stream kernels only: mfma_path_ok)
 template <int D>
 hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
-                  const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
+                  const uint32_t *wmeta, const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     ProfScope prof(LSH_KERNEL_FWD, st);
     if (kRows % P.m == 0) {
-        q_stream_go<D, false>(P, q, v, nullptr, nullptr, nullptr, meta, srec, ktile, o_rounds, lse_rounds, st);
+        q_stream_go<D, false>(P, q, v, nullptr, nullptr, nullptr, meta, srec, wmeta, ktile, o_rounds, lse_rounds,
+                              st);
     } else {
         hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
                            max_window(P), P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile,
@@ -1680,8 +1742,8 @@ hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *m
 
 template <int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-                  const uint32_t *meta, const uint32_t *srec, const float *rnorm, const uint8_t *ktile,
-                  const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
+                  const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const float *rnorm,
+                  const uint8_t *ktile, const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
 {
     // rows of one (token, round) are dq, dk rn, dv in turn (part_row)
     bf16 *dq_part = (bf16 *)part, *dkr_part = dq_part + D, *dv_part = dq_part + 2 * D;
@@ -1689,7 +1751,7 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         if (kRows % P.m == 0) {
-            q_stream_go<D, true>(P, q, v, dout, lse, Dv, meta, srec, ktile, dq_part, nullptr, st);
+            q_stream_go<D, true>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, dq_part, nullptr, st);
         } else {
             hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, max_window(P), P.scale,
                                (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile,
@@ -1705,17 +1767,25 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
             const int nt = P.L / kRows, segs = P.BH() * P.nh;
             const int T = stream_run_tiles(nt, segs);
             const int runs = segs * ((nt + T - 1) / T);
-#define LSH_DKV(NR)                                                                                       \
-    hipLaunchKernelGGL((dkv_stream_kernel<D, NR>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,   \
-                       (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part, dv_part)
-            if (P.nh <= 2)
-                LSH_DKV(1);
-            else if (P.nh <= 4)
-                LSH_DKV(3);
-            else if (P.nh <= 8)
-                LSH_DKV(7);
-            else
-                LSH_DKV(13);
+#define LSH_DKV(NR, NC)                                                                                        \
+    hipLaunchKernelGGL((dkv_stream_kernel<D, NR, NC>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T, P.m,     \
+                       P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part,  \
+                       dv_part)
+#define LSH_DKV_NR(NC)              \
+    if (P.nh <= 2)                  \
+        LSH_DKV(1, NC);             \
+    else if (P.nh <= 4)             \
+        LSH_DKV(3, NC);             \
+    else if (P.nh <= 8)             \
+        LSH_DKV(7, NC);             \
+    else                            \
+        LSH_DKV(13, NC)
+            if (P.causal) {
+                LSH_DKV_NR(false);
+            } else {
+                LSH_DKV_NR(true);
+            }
+#undef LSH_DKV_NR
 #undef LSH_DKV
         } else {
             hipLaunchKernelGGL((dkv_kernel<D>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, P.scale, (const bf16 *)q,
@@ -1729,8 +1799,8 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
 #define LSH_REDUCE(NH)                                                                                            \
     hipLaunchKernelGGL((reduce_kernel<D, NH>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok, \
-                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, dq_part, dkr_part, dv_part, (bf16 *)dq,     \
-                       (bf16 *)dv)
+                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, P.causal ? nullptr : wmeta, dq_part,       \
+                       dkr_part, dv_part, (bf16 *)dq, (bf16 *)dv)
     if (P.nh <= 2)
         LSH_REDUCE(2);
     else if (P.nh <= 4)
@@ -1743,14 +1813,15 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     return hipGetLastError();
 }
 
-hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, const float *rnorm, const float *lse,
-                    const float *Dv, uint8_t *ktile, uint8_t *qtile, hipStream_t st)
+hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, const uint32_t *wmeta,
+                    const float *rnorm, const float *lse, const float *Dv, uint8_t *ktile, uint8_t *qtile,
+                    hipStream_t st)
 {
     const int ntiles = P.BH() * P.nh * (P.L / kBlk);
     const int per_block = kThreads / kWave;
     ProfScope prof(LSH_KERNEL_TILES, st);
     hipLaunchKernelGGL(tile_prep_kernel, dim3((ntiles + per_block - 1) / per_block), dim3(kThreads), 0, st, P.L, P.nh,
-                       ntiles, P.scale * kLog2e, srec, meta, rnorm, lse, Dv, ktile, qtile);
+                       ntiles, P.scale * kLog2e, srec, meta, wmeta, rnorm, lse, Dv, ktile, qtile);
     return hipGetLastError();
 }
 
@@ -1759,42 +1830,44 @@ hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, c
 bool mfma_path_ok(const Dims &P, int dtype)
 {
     // the streamed range of a workgroup (at most 128 + 2 m + 31 sorted rows)
-    // must fit the LDS record cache, and the metadata tiles hold 13 earlier rounds
+    // must fit the LDS record cache, and the metadata tiles hold 13 earlier
+    // rounds; non-causal problems run on the stream kernels only (chunk
+    // lengths that divide 128)
     return dtype == LSH_BF16 && (P.d == 64 || P.d == 128) && P.L % kRows == 0 && P.nh <= kMaxEarlier + 1 &&
-           kRows + 2 * P.m + kBlk <= kRecCache;
+           kRows + 2 * P.m + kBlk <= kRecCache && (P.causal || kRows % P.m == 0);
 }
 
 size_t mfma_ktile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * ktile_stride(P.nh); }
 size_t mfma_qtile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * qtile_stride(P.nh); }
 size_t bwd_mfma_part_bytes(const Dims &P) { return 3 * (size_t)P.BH() * P.nh * P.L * P.d * sizeof(uint16_t); }
 
-hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, const int32_t *inv, const int32_t *win_lo,
-                                const uint32_t *meta, const uint32_t *srec, const float *rnorm, uint8_t *ktile,
+hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, const uint32_t *meta,
+                                const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, uint8_t *ktile,
                                 void *o_rounds, float *lse_rounds, hipStream_t st)
 {
-    (void)inv;
-    (void)win_lo;
-    hipError_t e = tiles_go(P, srec, meta, rnorm, nullptr, nullptr, ktile, nullptr, st);
+    if (P.causal)
+        wmeta = nullptr;
+    hipError_t e = tiles_go(P, srec, meta, wmeta, rnorm, nullptr, nullptr, ktile, nullptr, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)
-        return fwd_go<128>(P, q, v, meta, srec, ktile, o_rounds, lse_rounds, st);
-    return fwd_go<64>(P, q, v, meta, srec, ktile, o_rounds, lse_rounds, st);
+        return fwd_go<128>(P, q, v, meta, srec, wmeta, ktile, o_rounds, lse_rounds, st);
+    return fwd_go<64>(P, q, v, meta, srec, wmeta, ktile, o_rounds, lse_rounds, st);
 }
 
 hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
-                                const float *Dv, const int32_t *inv, const int32_t *win_lo, const uint32_t *meta,
-                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, bool make_ktile,
-                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
+                                const float *Dv, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
+                                const float *rnorm, uint8_t *ktile, bool make_ktile, uint8_t *qtile, void *part,
+                                void *dq, void *dv, hipStream_t st)
 {
-    (void)inv;
-    (void)win_lo;
-    hipError_t e = tiles_go(P, srec, meta, rnorm, lse, Dv, make_ktile ? ktile : nullptr, qtile, st);
+    if (P.causal)
+        wmeta = nullptr;
+    hipError_t e = tiles_go(P, srec, meta, wmeta, rnorm, lse, Dv, make_ktile ? ktile : nullptr, qtile, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)
-        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, rnorm, ktile, qtile, part, dq, dv, st);
-    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, rnorm, ktile, qtile, part, dq, dv, st);
+        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, wmeta, rnorm, ktile, qtile, part, dq, dv, st);
+    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, wmeta, rnorm, ktile, qtile, part, dq, dv, st);
 }
 
 }  // namespace lsh

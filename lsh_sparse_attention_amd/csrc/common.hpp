@@ -64,16 +64,26 @@ __device__ __forceinline__ bool in_window(uint32_t qrec, uint32_t sj)
     return (si - 1u - sj) < wi;   // unsigned: 0 <= si-1-sj < wi
 }
 
+// Non-causal window record, per (position, round): low 16 bits = hi, the
+// last sorted index of the round's attended set (the last row of the
+// position's bucket inside its chunk), high 16 bits = span = hi - win_lo.
+// The set, self included, is the sorted range [hi - span, hi].
+__device__ __forceinline__ bool in_span(uint32_t wrec, uint32_t sj)
+{
+    return (rec_lo(wrec) - sj) <= rec_hi(wrec);   // unsigned: 0 <= hi-sj <= span
+}
+
 struct Dims {
     int B, H, L, d, nh, nb, m;
     float scale;
+    bool causal;
     int BH() const { return B * H; }
 };
 
 inline Dims dims_of(const lsh_problem_t *p)
 {
     return Dims{p->batch, p->heads, p->seq_len, p->head_dim, p->n_hashes, p->n_buckets, p->chunk_len,
-                p->scale};
+                p->scale, p->causal != 0};
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -95,20 +105,22 @@ hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, 
 hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv,
                        int32_t *win_lo, void *ws, hipStream_t);
 size_t sort_ws_bytes(const Dims &);
-// Packed records, inverse norms and (with out, dout) D = dO . O; with meta
-// null only D is written (the records are already in place).
+// Packed records, inverse norms, the non-causal window records (wmeta,
+// non-causal problems only; null otherwise) and (with out, dout)
+// D = dO . O; with meta null only D is written (the records are already in
+// place).
 hipError_t launch_prep(const Dims &, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
-                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, float *rnorm,
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, float *rnorm,
                        const void *out, const void *dout, float *D, hipStream_t);
 hipError_t launch_attn_fwd(const Dims &, int dtype, const void *q, const void *v, const uint32_t *meta,
-                           const uint32_t *srec, const float *rnorm, void *o_rounds, float *lse_rounds,
-                           hipStream_t);
+                           const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, void *o_rounds,
+                           float *lse_rounds, hipStream_t);
 hipError_t launch_combine(const Dims &, int dtype, const void *q, const void *v, const void *o_rounds,
                           const float *lse_rounds, void *out, float *lse, hipStream_t);
 hipError_t launch_attn_bwd(const Dims &, int dtype, const void *q, const void *v, const void *dout,
                            const float *lse, const float *D, const uint32_t *meta, const uint32_t *srec,
-                           const float *rnorm, float *dq_part, float *dk_part, float *dv_part,
-                           void *dq, void *dv, hipStream_t);
+                           const uint32_t *wmeta, const float *rnorm, float *dq_part, float *dk_part,
+                           float *dv_part, void *dq, void *dv, hipStream_t);
 
 }  // namespace lsh
 
@@ -298,15 +310,12 @@ size_t mfma_qtile_bytes(const Dims &);
 // bf16 per-round partials dq (query side), dk rn (key side, before the key
 // normalisation) and dv, [B*H*L][nh][3][d] (token-major), in one buffer of this size
 size_t bwd_mfma_part_bytes(const Dims &);
-hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const int32_t *inv,
-                                const int32_t *win_lo, const uint32_t *meta, const uint32_t *srec,
-                                const float *rnorm, uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t);
+hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const uint32_t *meta,
+                                const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, uint8_t *ktile,
+                                void *o_rounds, float *lse_rounds, hipStream_t);
 hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
-                                const float *D, const int32_t *inv, const int32_t *win_lo, const uint32_t *meta,
-                                const uint32_t *srec, const float *rnorm, uint8_t *ktile, bool make_ktile,
-                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t);
-hipError_t launch_bwd_reduce(const Dims &, int dtype, const void *q, const void *dout, const uint32_t *meta,
-                             const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part,
-                             void *dq, void *dv, hipStream_t);
+                                const float *D, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
+                                const float *rnorm, uint8_t *ktile, bool make_ktile, uint8_t *qtile, void *part,
+                                void *dq, void *dv, hipStream_t);
 
 }  // namespace lsh

@@ -45,10 +45,8 @@ int validate(const lsh_problem_t *p)
         return LSH_ERR_INVALID;
     if (p->batch < 0 || p->heads < 0 || p->seq_len < 0 || p->head_dim < 1 || p->n_hashes < 1 ||
         p->n_buckets < 2 || (p->n_buckets & 1) || p->chunk_len < 1 || p->seq_len % p->chunk_len ||
-        !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16))
+        !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16) || (p->causal != 0 && p->causal != 1))
         return LSH_ERR_INVALID;
-    if (p->causal != 1)
-        return LSH_ERR_UNSUPPORTED;
     if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128)
         return LSH_ERR_UNSUPPORTED;
     if (p->seq_len > kMaxLen || p->n_hashes > kMaxHashes || p->n_buckets > kMaxBucketsAbi)
@@ -66,15 +64,17 @@ bool empty(const lsh_problem_t *p) { return p->batch == 0 || p->heads == 0 || p-
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
+// wmeta (the non-causal window records) exists for non-causal problems
+// only, and is null otherwise.
 struct FwdWs {
-    uint32_t *meta, *srec;
+    uint32_t *meta, *srec, *wmeta;
     float *rnorm;
     uint8_t *ktile;
     size_t bytes;
 };
 
 struct BwdWs {
-    uint32_t *meta, *srec;
+    uint32_t *meta, *srec, *wmeta;
     float *rnorm, *D, *dq_part, *dk_part, *dv_part;
     uint8_t *ktile, *qtile;
     size_t bytes;
@@ -90,6 +90,9 @@ FwdWs fwd_layout(const Dims &P, void *base)
     w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
     w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
+    if (!P.causal) {
+        w.wmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+    }
     w.bytes = o;
     return w;
 }
@@ -103,9 +106,12 @@ BwdWs bwd_layout(const Dims &P, void *base)
     w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
+    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
+    if (!P.causal) {
+        w.wmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+    }
     // up to here the same offsets as the forward's workspace, so that a
     // backward can take over the forward's records
-    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
     w.D = (float *)(b + o); o += align_up(tok * 4, 256);
     w.dq_part = (float *)(b + o); o += align_up(part, 256);
     w.dk_part = (float *)(b + o); o += align_up(part, 256);
@@ -171,14 +177,14 @@ int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void
         return LSH_ERR_INVALID;
     const bool derive = perm != nullptr;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, derive ? w.meta : nullptr, w.srec, w.rnorm,
-                               out, dout, w.D, s);
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, derive ? w.meta : nullptr, w.srec, w.wmeta,
+                               w.rnorm, out, dout, w.D, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype)) {
-            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, inv, win_lo, w.meta, w.srec, w.rnorm, w.ktile, derive,
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.rnorm, w.ktile, derive,
                                      w.qtile, w.dq_part, dq, dv, s);
         } else {
-            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.rnorm, w.dq_part,
+            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.rnorm, w.dq_part,
                                 w.dk_part, w.dv_part, dq, dv, s);
         }
     }
@@ -200,7 +206,7 @@ const char *lsh_status_string(int status)
     }
 }
 
-int lsh_version(void) { return 200; }
+int lsh_version(void) { return 300; }
 
 const char *lsh_kernel_name(int kernel)
 {
@@ -271,14 +277,13 @@ int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     if (ws_bytes < w.bytes)
         return LSH_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.rnorm, nullptr, nullptr,
-                               nullptr, s);
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.wmeta, w.rnorm, nullptr,
+                               nullptr, nullptr, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype))
-            e = launch_attn_fwd_mfma(P, q, v, inv, win_lo, w.meta, w.srec, w.rnorm, w.ktile, o_rounds, lse_rounds,
-                                     s);
+            e = launch_attn_fwd_mfma(P, q, v, w.meta, w.srec, w.wmeta, w.rnorm, w.ktile, o_rounds, lse_rounds, s);
         else
-            e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.rnorm, o_rounds, lse_rounds, s);
+            e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.wmeta, w.rnorm, o_rounds, lse_rounds, s);
     }
     return hip_status(e);
 }

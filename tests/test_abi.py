@@ -75,11 +75,23 @@ def test_empty_problems_are_no_ops(kw):
     assert L.lsh_hash(ctypes.byref(bad), n, n, n, n) == 2
 
 
-def test_non_causal_is_unsupported():
+def test_causal_flag_values():
+    # 1 (causal) and 0 (non-causal) are valid; anything else is malformed and
+    # rejected before any pointer is looked at
+    L = _lib.lib()
     p = _prob()
-    p.causal = 0
+    p.causal = 2
     dummy = ctypes.c_void_p(256)
-    assert _lib.lib().lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == 2
+    assert L.lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == 1
+    assert L.lsh_workspace_bytes(ctypes.byref(p), 1) == 0
+    c, n = _prob(), _prob()
+    n.causal = 0
+    # the non-causal forward keeps one more 32-bit record per (token, round)
+    rnd = c.batch * c.heads * c.seq_len * c.n_hashes
+    extra = (rnd * 4 + 255) // 256 * 256
+    for kind in (1, 2, 3):
+        assert L.lsh_workspace_bytes(ctypes.byref(n), kind) == L.lsh_workspace_bytes(ctypes.byref(c), kind) + extra
+    assert L.lsh_workspace_bytes(ctypes.byref(n), 0) == L.lsh_workspace_bytes(ctypes.byref(c), 0)
 
 
 def test_null_and_misaligned_pointers_rejected():

@@ -180,6 +180,98 @@ def test_rehash_backward_matches_stored_order(idx):
     assert torch.equal(bits(dq), bits(dq2)) and torch.equal(bits(dv), bits(dv2))
 
 
+# ----------------------------------------------------------------------------- non-causal
+# Encoder (non-causal) sets: same bucket, own chunk or the one before, no
+# "not after the query" condition.  bf16 problems whose chunk length divides
+# 128 run on the matrix-core stream kernels; the others (fp32, other chunk
+# lengths, lengths not a multiple of 128) on the per-query kernels.
+
+# name, B, H, L, d, nb, nh, m, dtype, clustered
+NC_SMALL = [
+    ("nc-f32-base", 1, 2, 1024, 64, 16, 3, 32, "f32", False),
+    ("nc-f32-d32", 1, 1, 512, 32, 8, 2, 16, "f32", False),
+    ("nc-f32-d128", 1, 1, 1024, 128, 64, 2, 64, "f32", False),
+    ("nc-f32-one-chunk", 1, 1, 256, 64, 8, 2, 256, "f32", False),
+    ("nc-f32-chunk-1", 1, 1, 128, 32, 4, 2, 1, "f32", False),
+    ("nc-f32-two-buckets", 1, 2, 512, 64, 2, 2, 32, "f32", False),
+    ("nc-tiny-L", 1, 1, 8, 32, 4, 2, 2, "f32", False),
+    ("nc-single-token", 1, 1, 1, 32, 2, 1, 1, "f32", False),
+    ("nc-bf16-base", 2, 2, 1024, 64, 16, 3, 32, "bf16", False),
+    ("nc-bf16-d128", 1, 2, 2048, 128, 32, 2, 64, "bf16", False),
+    ("nc-bf16-one-round", 1, 2, 1024, 64, 32, 1, 64, "bf16", False),
+    ("nc-bf16-m128", 1, 4, 4096, 64, 64, 2, 128, "bf16", False),
+    ("nc-bf16-m8", 1, 1, 1024, 64, 128, 2, 8, "bf16", False),
+    ("nc-bf16-m1", 1, 2, 512, 64, 8, 2, 1, "bf16", False),
+    ("nc-bf16-nh6", 1, 1, 1024, 128, 64, 6, 128, "bf16", False),
+    ("nc-bf16-nh12-d128", 1, 1, 1024, 128, 32, 12, 64, "bf16", False),
+    ("nc-bf16-nh16", 1, 1, 512, 64, 16, 16, 32, "bf16", False),
+    ("nc-bf16-clustered", 1, 2, 2048, 64, 64, 4, 64, "bf16", True),
+    ("nc-bf16-clustered-d128", 1, 1, 2048, 128, 64, 8, 128, "bf16", True),
+    ("nc-bf16-m96", 1, 2, 1536, 64, 32, 3, 96, "bf16", False),
+    ("nc-bf16-m256", 1, 1, 2048, 128, 16, 2, 256, "bf16", False),
+    ("nc-bf16-ragged", 1, 2, 2016, 64, 64, 2, 32, "bf16", False),
+    ("nc-bf16-d32", 1, 2, 512, 32, 8, 2, 16, "bf16", False),
+]
+
+
+def _nc_cfg(case):
+    name, B, H, L, d, nb, nh, m, dt, cl = case
+    return gen.Config(name, B, H, L, d, nb, nh, m, dt, cl, True, 300 + NC_SMALL.index(case), n_clusters=16,
+                      causal=False)
+
+
+@pytest.mark.parametrize("case", NC_SMALL, ids=[c[0] for c in NC_SMALL])
+def test_noncausal_small_shapes_match_oracle(case):
+    cfg = _nc_cfg(case)
+    gu.say(f"[gpu] non-causal small case {cfg}")
+    x = gen.generate(cfg)
+    res = gu.run_gpu(x)
+    gu.check_sort_properties(res, cfg)
+    gu.compare_slices(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
+
+
+NC_SAMPLES = {"image": [(0, 5)], "text": [(0, 2)]}
+
+
+@pytest.mark.parametrize("name", list(NC_SAMPLES))
+def test_noncausal_workload_shapes_match_oracle(name):
+    # the same inputs as the causal full-size case, non-causal sets
+    x = dict(_full(name))
+    x["cfg"] = x["cfg"].with_(causal=False)
+    gu.say(f"[gpu] non-causal full-size {name}: running the library")
+    res = gu.run_gpu(x)
+    gu.check_sort_properties(res, x["cfg"])
+    gu.say(f"[gpu] non-causal full-size {name}: oracle on slices {NC_SAMPLES[name]}")
+    gu.compare_slices(x, res, NC_SAMPLES[name])
+
+
+@pytest.mark.parametrize("idx", [0, 8, 9, 15, 19])
+def test_noncausal_saved_standalone_and_rehash_backwards_agree(idx):
+    # the three backward entry points give the same bits on non-causal problems
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    cfg = _nc_cfg(NC_SMALL[idx])
+    gu.say(f"[gpu] non-causal backward entry points {cfg}")
+    x = gen.generate(cfg)
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=False)
+    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
+    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
+    mod = lsh.LshAttention(prob)
+    mod.forward(q, v, rot)
+    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
+    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
+    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
+    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
+    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
+    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
+    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for a, b in ((dq, dq_s), (dv, dv_s), (dq2, dq_s), (dv2, dv_s)):
+        assert torch.equal(bits(a), bits(b))
+
+
 def test_empty_problem_is_a_no_op():
     import lsh_sparse_attention_amd as lsh
     gu.say("[gpu] empty problem L=0")
