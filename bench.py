@@ -149,6 +149,44 @@ def rehash_variant(prob, mod, q, v, rot, do, steps, cfg) -> dict:
             "kept_between_passes": "out, lse (no buckets, sorted order or records)"}
 
 
+def noncausal_variant(q, v, rot, do, steps, cfg, hip) -> dict:
+    """The same training step (forward and saved-records backward) on the same inputs with
+    non-causal (encoder) sets: same bucket, own chunk or the one before, no ordering condition."""
+    import torch
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib as L_
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=False)
+    mod = lsh.LshAttention(prob)
+
+    def step():
+        mod.forward(q, v, rot)
+        mod.backward(q, v, do)
+
+    step()
+    L = L_.lib()
+    evs = [(hip.event(), hip.event()) for _ in L_.KERNELS]
+    for k, (a, b) in enumerate(evs):
+        L.lsh_profile_kernel(k, a, b)
+    step()
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for k, (a, b) in enumerate(evs):
+        per_kernel[L_.KERNELS[k]] = round(hip.elapsed_ms(a, b) * 1e3, 2)
+        L.lsh_profile_kernel(k, None, None)
+        hip.destroy(a)
+        hip.destroy(b)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del mod
+    return {"ms_per_step": ms, "value": cfg.batch * cfg.seq_len / (ms * 1e-3), "unit": "tokens/s",
+            "causal": False, "kernels_us": per_kernel}
+
+
 def source_sha(kernel: str) -> str:
     """Digest of the sources a kernel is compiled from (its file and the shared header)."""
     h = hashlib.sha256()
@@ -362,6 +400,8 @@ def main() -> int:
         "variants": {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)},
     }
     del mod
+    torch.cuda.empty_cache()
+    result["variants"]["non_causal"] = noncausal_variant(q, v, rot, do, args.steps, cfg, hip)
     torch.cuda.empty_cache()
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
