@@ -289,6 +289,9 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads of batch 0 the oracle times (0: skip)")
     ap.add_argument("--sweep", choices=("length", "rounds"),
                     help="instead of the bench line: a length sweep at fixed total tokens, or a rounds sweep")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the rehash-backward and non-causal variant steps (profiler runs: only the main "
+                         "step's launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 1 GiB (reference point for HBM byte counters)")
     args = ap.parse_args()
@@ -397,11 +400,14 @@ def main() -> int:
                    "causal": True, "clustered_inputs": cfg.clustered},
         "roofline": roof,
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
-        "variants": {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)},
+        "variants": None,
     }
+    if not args.no_variants:
+        result["variants"] = {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)}
     del mod
     torch.cuda.empty_cache()
-    result["variants"]["non_causal"] = noncausal_variant(q, v, rot, do, args.steps, cfg, hip)
+    if not args.no_variants:
+        result["variants"]["non_causal"] = noncausal_variant(q, v, rot, do, args.steps, cfg, hip)
     torch.cuda.empty_cache()
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
