@@ -53,6 +53,7 @@ class Config:
     n_clusters: int = 256
     cluster_sigma: float = 0.1
     causal: bool = True
+    bucket_mask: bool = True
 
     @property
     def scale(self) -> float:

@@ -31,6 +31,10 @@
  *     condition j <= i is dropped and nothing else changes: same bucket,
  *     own chunk or the one before (no look-ahead to the next chunk, and the
  *     first chunk has no chunk before it: no wrap-around).
+ *     And a `bucket_mask` flag: with bucket_mask = 0 the condition
+ *     h_r(j) = h_r(i) is dropped (the alternative reading in which the
+ *     chunks of the sorted order alone restrict attention), nothing else
+ *     changes.
  *   - the query attends to the union U_i of its round sets, each key once
  *     (duplicate correction); self is dropped from the union unless nothing
  *     else is in it, in which case o_i = v_i and lse_i = scale * q_i . k_i.
@@ -103,12 +107,13 @@ static int cmp_i64(const void *a, const void *b)
 }
 
 /* Round-r attended-set predicate (self included), §2 and App. A:
- * same bucket, not in the future (causal only), and in the own chunk or the
- * one before. */
-static int in_round_set(int L, int m, int causal, const int32_t *bk, const int32_t *inv, int i, int j)
+ * same bucket (unless bucket_mask is 0), not in the future (causal only),
+ * and in the own chunk or the one before. */
+static int in_round_set(int L, int m, int causal, int bucket_mask, const int32_t *bk, const int32_t *inv, int i,
+                        int j)
 {
     (void)L;
-    if (bk[j] != bk[i] || (causal && j > i))
+    if ((bucket_mask && bk[j] != bk[i]) || (causal && j > i))
         return 0;
     int ci = inv[i] / m, cj = inv[j] / m;
     return (ci - cj == 0) || (ci - cj == 1);
@@ -141,7 +146,7 @@ int lsh_oracle_sort(int L, int nh, int m, const int32_t *buckets, int32_t *perm,
             int hi = (c + 1) * m > L ? L : (c + 1) * m;
             int best = iv[t];
             for (int s = lo; s < hi; ++s)
-                if (in_round_set(L, m, 1, bk, iv, t, pr[s]) && s < best)
+                if (in_round_set(L, m, 1, 1, bk, iv, t, pr[s]) && s < best)
                     best = s;
             wl[t] = best;
         }
@@ -157,7 +162,7 @@ int lsh_oracle_sort(int L, int nh, int m, const int32_t *buckets, int32_t *perm,
  * Writes the members of U_i \ {i} to list (capacity nh*2m) and returns their
  * number; stamp is a per-thread scratch array of L ints.                     */
 
-static int union_set(int L, int nh, int m, int causal, const int32_t *buckets, const int32_t *perm,
+static int union_set(int L, int nh, int m, int causal, int bucket_mask, const int32_t *buckets, const int32_t *perm,
                      const int32_t *inv, int i, int *stamp, int stamp_val, int32_t *list)
 {
     int n = 0;
@@ -168,7 +173,7 @@ static int union_set(int L, int nh, int m, int causal, const int32_t *buckets, c
         int hi = (c + 1) * m > L ? L : (c + 1) * m;
         for (int s = lo; s < hi; ++s) {
             int j = pr[s];
-            if (j != i && stamp[j] != stamp_val && in_round_set(L, m, causal, bk, iv, i, j)) {
+            if (j != i && stamp[j] != stamp_val && in_round_set(L, m, causal, bucket_mask, bk, iv, i, j)) {
                 stamp[j] = stamp_val;
                 list[n++] = j;
             }
@@ -178,7 +183,8 @@ static int union_set(int L, int nh, int m, int causal, const int32_t *buckets, c
 }
 
 /* Dense membership of U_i (self included), for tiny problems. */
-int lsh_oracle_union_mask(int L, int nh, int m, int causal, const int32_t *buckets, const int32_t *perm,
+int lsh_oracle_union_mask(int L, int nh, int m, int causal, int bucket_mask, const int32_t *buckets,
+                          const int32_t *perm,
                           const int32_t *inv, uint8_t *mask /* [L][L] */)
 {
     if (L <= 0 || nh <= 0 || m <= 0 || L % m)
@@ -187,7 +193,7 @@ int lsh_oracle_union_mask(int L, int nh, int m, int causal, const int32_t *bucke
     int32_t *list = (int32_t *)malloc(sizeof(int32_t) * (size_t)(2 * m * nh + 1));
     memset(mask, 0, (size_t)L * L);
     for (int i = 0; i < L; ++i) {
-        int n = union_set(L, nh, m, causal, buckets, perm, inv, i, stamp, i + 1, list);
+        int n = union_set(L, nh, m, causal, bucket_mask, buckets, perm, inv, i, stamp, i + 1, list);
         mask[(size_t)i * L + i] = 1;
         for (int a = 0; a < n; ++a)
             mask[(size_t)i * L + list[a]] = 1;
@@ -223,7 +229,8 @@ static void make_keys(int L, int d, const double *q, double *k, double *qnorm)
  * empty set attends only to itself (§2 causal-masking bullet, App. A masking
  * bullet: the first token attends only to itself).                           */
 
-int lsh_oracle_forward(int L, int d, int nh, int m, int causal, double scale, const double *q, const double *v,
+int lsh_oracle_forward(int L, int d, int nh, int m, int causal, int bucket_mask, double scale, const double *q,
+                       const double *v,
                        const int32_t *buckets, const int32_t *perm, const int32_t *inv,
                        double *out /* [L][d] */, double *lse /* [L] */)
 {
@@ -242,7 +249,7 @@ int lsh_oracle_forward(int L, int d, int nh, int m, int causal, double scale, co
         for (int i = 0; i < L; ++i) {
             const double *qi = q + (size_t)i * d;
             double *oi = out + (size_t)i * d;
-            int n = union_set(L, nh, m, causal, buckets, perm, inv, i, stamp, i + 1, list);
+            int n = union_set(L, nh, m, causal, bucket_mask, buckets, perm, inv, i, stamp, i + 1, list);
             if (n == 0) {
                 for (int c = 0; c < d; ++c)
                     oi[c] = v[(size_t)i * d + c];
@@ -290,15 +297,17 @@ int lsh_oracle_forward(int L, int d, int nh, int m, int causal, double scale, co
  * Query-side sums run over each query's set; key-side sums run over the
  * queries whose set contains the key, found through the same predicate.     */
 
-static int in_union(int L, int nh, int m, int causal, const int32_t *buckets, const int32_t *inv, int i, int j)
+static int in_union(int L, int nh, int m, int causal, int bucket_mask, const int32_t *buckets, const int32_t *inv,
+                    int i, int j)
 {
     for (int r = 0; r < nh; ++r)
-        if (in_round_set(L, m, causal, buckets + (size_t)r * L, inv + (size_t)r * L, i, j))
+        if (in_round_set(L, m, causal, bucket_mask, buckets + (size_t)r * L, inv + (size_t)r * L, i, j))
             return 1;
     return 0;
 }
 
-int lsh_oracle_backward(int L, int d, int nh, int m, int causal, double scale, const double *q, const double *v,
+int lsh_oracle_backward(int L, int d, int nh, int m, int causal, int bucket_mask, double scale, const double *q,
+                        const double *v,
                         const double *dout, const int32_t *buckets, const int32_t *perm,
                         const int32_t *inv, const double *out, const double *lse,
                         double *dq_out /* [L][d] */, double *dv_out /* [L][d] */)
@@ -325,7 +334,7 @@ int lsh_oracle_backward(int L, int d, int nh, int m, int causal, double scale, c
             D[i] = dot(doi, out + (size_t)i * d, d);
             for (int c = 0; c < d; ++c)
                 dqi[c] = 0.0;
-            int n = union_set(L, nh, m, causal, buckets, perm, inv, i, stamp, i + 1, list);
+            int n = union_set(L, nh, m, causal, bucket_mask, buckets, perm, inv, i, stamp, i + 1, list);
             alone[i] = (uint8_t)(n == 0);
             for (int a = 0; a < n; ++a) {
                 int j = list[a];
@@ -359,7 +368,7 @@ int lsh_oracle_backward(int L, int d, int nh, int m, int causal, double scale, c
                 int hi = (c + 2) * m > L ? L : (c + 2) * m;
                 for (int s = lo; s < hi; ++s) {
                     int i = pr[s];
-                    if (i == j || stamp[i] == j + 1 || !in_union(L, nh, m, causal, buckets, inv, i, j))
+                    if (i == j || stamp[i] == j + 1 || !in_union(L, nh, m, causal, bucket_mask, buckets, inv, i, j))
                         continue;
                     stamp[i] = j + 1;
                     const double *qi = q + (size_t)i * d, *doi = dout + (size_t)i * d;
@@ -396,7 +405,7 @@ int lsh_oracle_backward(int L, int d, int nh, int m, int causal, double scale, c
  * not NULL) backward.  Any output pointer may be NULL except those the later
  * stages need internally, which are then allocated here.                    */
 
-int lsh_oracle_head(int L, int d, int nh, int nb, int m, int causal, double scale, const double *q,
+int lsh_oracle_head(int L, int d, int nh, int nb, int m, int causal, int bucket_mask, double scale, const double *q,
                     const double *v, const double *rot, const double *dout, int32_t *buckets,
                     int32_t *perm, int32_t *inv, int32_t *win_lo, double *out, double *lse,
                     double *dq, double *dv)
@@ -414,9 +423,9 @@ int lsh_oracle_head(int L, int d, int nh, int nb, int m, int causal, double scal
     if (!rc)
         rc = lsh_oracle_sort(L, nh, m, bk, pr, iv, wl);
     if (!rc)
-        rc = lsh_oracle_forward(L, d, nh, m, causal, scale, q, v, bk, pr, iv, o, ls);
+        rc = lsh_oracle_forward(L, d, nh, m, causal, bucket_mask, scale, q, v, bk, pr, iv, o, ls);
     if (!rc && dout && dq && dv)
-        rc = lsh_oracle_backward(L, d, nh, m, causal, scale, q, v, dout, bk, pr, iv, o, ls, dq, dv);
+        rc = lsh_oracle_backward(L, d, nh, m, causal, bucket_mask, scale, q, v, dout, bk, pr, iv, o, ls, dq, dv);
     if (!buckets) free(bk);
     if (!perm) free(pr);
     if (!inv) free(iv);

@@ -5,7 +5,8 @@ benchmark's CPU-baseline leg.  The GPU library never imports it.
 
 Arrays are per (batch, head) slice: q, v, dout [L, d] fp64, rot [nh, d, nb/2]
 fp64; integer outputs are int32 [nh, L].  ``causal`` selects the causal sets
-(the default) or the non-causal ones (no "not after the query" condition).
+(the default) or the non-causal ones (no "not after the query" condition);
+``bucket_mask`` False drops the same-bucket condition (chunks alone restrict).
 """
 from __future__ import annotations
 
@@ -81,18 +82,19 @@ def sort(buckets, chunk_len):
     return perm, inv, win_lo
 
 
-def union_mask(buckets, perm, inv, chunk_len, causal=True):
+def union_mask(buckets, perm, inv, chunk_len, causal=True, bucket_mask=True):
     bk, perm, inv = _i32(buckets), _i32(perm), _i32(inv)
     nh, L = bk.shape
     mask = np.empty((L, L), np.uint8)
     rc = lib().lsh_oracle_union_mask(ctypes.c_int(L), ctypes.c_int(nh), ctypes.c_int(chunk_len),
-                                     ctypes.c_int(int(bool(causal))), _p(bk), _p(perm), _p(inv), _p(mask))
+                                     ctypes.c_int(int(bool(causal))), ctypes.c_int(int(bool(bucket_mask))),
+                                     _p(bk), _p(perm), _p(inv), _p(mask))
     if rc:
         raise ValueError("oracle union_mask: invalid arguments")
     return mask.astype(bool)
 
 
-def forward(q, v, buckets, perm, inv, chunk_len, scale, causal=True):
+def forward(q, v, buckets, perm, inv, chunk_len, scale, causal=True, bucket_mask=True):
     q, v = _f64(q), _f64(v)
     bk, perm, inv = _i32(buckets), _i32(perm), _i32(inv)
     L, d = q.shape
@@ -101,14 +103,14 @@ def forward(q, v, buckets, perm, inv, chunk_len, scale, causal=True):
     lse = np.empty(L, np.float64)
     rc = lib().lsh_oracle_forward(ctypes.c_int(L), ctypes.c_int(d), ctypes.c_int(nh),
                                   ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))),
-                                  ctypes.c_double(scale), _p(q), _p(v),
+                                  ctypes.c_int(int(bool(bucket_mask))), ctypes.c_double(scale), _p(q), _p(v),
                                   _p(bk), _p(perm), _p(inv), _p(out), _p(lse))
     if rc:
         raise ValueError("oracle forward: invalid arguments")
     return out, lse
 
 
-def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=True):
+def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=True, bucket_mask=True):
     q, v, dout, out, lse = _f64(q), _f64(v), _f64(dout), _f64(out), _f64(lse)
     bk, perm, inv = _i32(buckets), _i32(perm), _i32(inv)
     L, d = q.shape
@@ -117,7 +119,7 @@ def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=
     dv = np.empty((L, d), np.float64)
     rc = lib().lsh_oracle_backward(ctypes.c_int(L), ctypes.c_int(d), ctypes.c_int(nh),
                                    ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))),
-                                   ctypes.c_double(scale), _p(q), _p(v),
+                                   ctypes.c_int(int(bool(bucket_mask))), ctypes.c_double(scale), _p(q), _p(v),
                                    _p(dout), _p(bk), _p(perm), _p(inv), _p(out), _p(lse), _p(dq),
                                    _p(dv))
     if rc:
@@ -125,7 +127,7 @@ def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=
     return dq, dv
 
 
-def head(q, v, rot, n_buckets, chunk_len, scale, dout=None, causal=True):
+def head(q, v, rot, n_buckets, chunk_len, scale, dout=None, causal=True, bucket_mask=True):
     """Hash, sort, forward and (with ``dout``) backward of one slice."""
     q, v, rot = _f64(q), _f64(v), _f64(rot)
     L, d = q.shape
@@ -139,7 +141,8 @@ def head(q, v, rot, n_buckets, chunk_len, scale, dout=None, causal=True):
         res["dv"] = np.empty((L, d), np.float64)
     rc = lib().lsh_oracle_head(
         ctypes.c_int(L), ctypes.c_int(d), ctypes.c_int(nh), ctypes.c_int(n_buckets),
-        ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))), ctypes.c_double(scale), _p(q), _p(v),
+        ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))), ctypes.c_int(int(bool(bucket_mask))),
+        ctypes.c_double(scale), _p(q), _p(v),
         _p(rot), _p(dout),
         _p(res["buckets"]), _p(res["perm"]), _p(res["inv"]), _p(res["win_lo"]), _p(res["out"]),
         _p(res["lse"]), _p(res.get("dq")), _p(res.get("dv")))
@@ -165,5 +168,6 @@ def run_inputs(inputs, slices=None, backward=None):
         q = to_f64(inputs["q"][b, h], cfg.dtype)
         v = to_f64(inputs["v"][b, h], cfg.dtype)
         do = to_f64(inputs["dout"][b, h], cfg.dtype) if backward else None
-        res[(b, h)] = head(q, v, rot, cfg.n_buckets, cfg.chunk_len, cfg.scale, do, causal=cfg.causal)
+        res[(b, h)] = head(q, v, rot, cfg.n_buckets, cfg.chunk_len, cfg.scale, do, causal=cfg.causal,
+                           bucket_mask=cfg.bucket_mask)
     return res

@@ -29,9 +29,10 @@ def sort(bk):
     return perm, inv
 
 
-def round_masks(bk, m, causal=True):
+def round_masks(bk, m, causal=True, bucket_mask=True):
     """[nh, L, L] bool: j in A_i^r (self included).  Without ``causal`` the
-    condition j <= i is dropped (same bucket, own chunk or the one before)."""
+    condition j <= i is dropped (same bucket, own chunk or the one before);
+    without ``bucket_mask`` the same-bucket condition is dropped."""
     nh, L = bk.shape
     _, inv = sort(bk)
     i = np.arange(L)[:, None]
@@ -39,15 +40,15 @@ def round_masks(bk, m, causal=True):
     out = []
     for r in range(nh):
         c = inv[r] // m
-        same = bk[r][:, None] == bk[r][None, :]
+        same = (bk[r][:, None] == bk[r][None, :]) if bucket_mask else np.ones((L, L), dtype=bool)
         dc = c[:, None] - c[None, :]
         order = (j <= i) if causal else np.ones((L, L), dtype=bool)
         out.append(same & order & ((dc == 0) | (dc == 1)))
     return np.asarray(out)
 
 
-def union_mask(bk, m, causal=True):
-    return round_masks(bk, m, causal).any(axis=0)
+def union_mask(bk, m, causal=True, bucket_mask=True):
+    return round_masks(bk, m, causal, bucket_mask).any(axis=0)
 
 
 def attention(q, v, mask, scale):

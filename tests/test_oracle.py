@@ -502,6 +502,88 @@ def test_noncausal_backward_matches_dense_autograd(seed, L, d, nb, nh, m):
     np.testing.assert_allclose(res["dv"].sum(axis=0), do.sum(axis=0), rtol=1e-11, atol=1e-11)
 
 
+# ----------------------------------------------------------------------------- no bucket mask
+# The alternative reading in which the chunks of the sorted order alone
+# restrict attention: the same-bucket condition is dropped, nothing else.
+
+def test_no_bucket_mask_union_and_forward_golden():
+    g = _golden()["attention_no_bucket_mask"]
+    bk = np.array(g["buckets"], np.int32)
+    L, m = g["L"], g["chunk_len"]
+    q = np.random.default_rng(0).standard_normal((L, L))
+    for key, nh in (("round0_only", 1), ("both_rounds", 2)):
+        perm, inv, _ = ora.sort(bk[:nh], m)
+        mask = ora.union_mask(bk[:nh], perm, inv, m, bucket_mask=False)
+        for i, members in enumerate(g[key]["sets"]):
+            assert sorted(set(np.nonzero(mask[i])[0].tolist()) - {i}) == members, (key, i)
+        out, lse = ora.forward(q, np.eye(L), bk[:nh], perm, inv, m, g["scale"], bucket_mask=False)
+        np.testing.assert_allclose(out, _weights_to_rows(g[key]["out_rows_as_weights"], L), atol=1e-15)
+        sizes = np.array([len(x) for x in g[key]["sets"]])
+        np.testing.assert_allclose(lse, np.where(sizes > 0, np.log(np.maximum(sizes, 1)), 0.0), atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("seed,L,nb,nh,m", [(91, 64, 4, 1, 8), (92, 128, 8, 3, 16), (93, 200, 4, 2, 8),
+                                            (94, 256, 32, 4, 32), (95, 64, 2, 2, 1)])
+def test_no_bucket_mask_union_matches_bruteforce(seed, L, nb, nh, m, causal):
+    rng = np.random.default_rng(seed)
+    bk = rng.integers(0, nb, size=(nh, L)).astype(np.int32)
+    perm, inv, _ = ora.sort(bk, m)
+    nb_mask = ora.union_mask(bk, perm, inv, m, causal=causal, bucket_mask=False)
+    assert np.array_equal(nb_mask, bf.union_mask(bk, m, causal=causal, bucket_mask=False))
+    # the bucket-restricted sets are contained in these
+    with_b = ora.union_mask(bk, perm, inv, m, causal=causal)
+    assert not np.any(with_b & ~nb_mask)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_no_bucket_mask_one_chunk_is_full_attention(causal):
+    # m = L: one chunk, so every other position (causal: every earlier one)
+    # is attended whatever the buckets; torch SDPA with the plain mask.
+    q, v, rot, _ = _rand_problem(96, 128, 16, 2, 16)
+    res = ora.head(q, v, rot, 16, 128, 0.45, causal=causal, bucket_mask=False)
+    assert len(np.unique(res["buckets"])) > 4
+    L = 128
+    if causal:
+        mask = np.tril(np.ones((L, L), dtype=bool), k=-1)
+        mask[0, 0] = True
+    else:
+        mask = ~np.eye(L, dtype=bool)
+    np.testing.assert_allclose(res["out"], _sdpa(q, v, mask, 0.45), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_no_bucket_mask_is_moot_with_one_bucket(causal):
+    rng = np.random.default_rng(97)
+    L, d, m = 192, 8, 16
+    rot = rng.standard_normal((1, d, 1))
+    q = _one_side(rng.standard_normal((L, d)), rot[0, :, 0])
+    v = rng.standard_normal((L, d))
+    a = ora.head(q, v, rot, 2, m, 0.5, causal=causal)
+    b = ora.head(q, v, rot, 2, m, 0.5, causal=causal, bucket_mask=False)
+    np.testing.assert_array_equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(98, 128, 16, 8, 3, 16), (99, 160, 32, 32, 2, 8)])
+def test_no_bucket_mask_matches_dense_autograd(seed, L, d, nb, nh, m, causal):
+    q, v, rot, do = _rand_problem(seed, L, d, nh, nb, scale_q=1.3)
+    scale = 1 / np.sqrt(d)
+    res = ora.head(q, v, rot, nb, m, scale, dout=do, causal=causal, bucket_mask=False)
+    allowed = bf.union_mask(res["buckets"], m, causal=causal, bucket_mask=False) & ~np.eye(L, dtype=bool)
+    empty = ~allowed.any(axis=1)
+    allowed[empty, np.nonzero(empty)[0]] = True
+    qt = torch.tensor(q, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    logits = (scale * qt @ kt.T).masked_fill(~torch.from_numpy(allowed), float("-inf"))
+    out = torch.softmax(logits, dim=-1) @ vt
+    (out * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(res["out"], out.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["dq"], qt.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(res["dv"], vt.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
 # ----------------------------------------------------------------------------- inputs
 
 def test_generator_reproducible_and_margin():
