@@ -46,6 +46,15 @@ typedef enum {
 
 typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype_t;
 
+/* Bits of lsh_problem_t.flags. */
+typedef enum {
+    /* Drop the same-bucket condition from the attended sets: the chunks of
+     * the sorted order alone restrict attention (the alternative reading of
+     * "Reformer" §2, where restricting each query to its own bucket is what
+     * sorting and chunking approximate). */
+    LSH_FLAG_NO_BUCKET_MASK = 1
+} lsh_flag_t;
+
 /* Which call a workspace is for (lsh_workspace_bytes). */
 typedef enum {
     LSH_WS_SORT = 0,
@@ -74,6 +83,9 @@ typedef enum {
  *   scale: the softmax scale applied to q_i . k_j (1/sqrt(d) for standard
  *       scaled dot-product attention).
  *   dtype: element type of q, v, rot, out, dout, dq, dv and o_rounds.
+ *   flags: 0, or LSH_FLAG_NO_BUCKET_MASK (round set of a query: every
+ *       position of its own chunk and the one before, not after it when
+ *       causal; the rest as above).  Unknown bits: LSH_ERR_INVALID.
  */
 typedef struct {
     int32_t batch, heads, seq_len, head_dim;
@@ -81,6 +93,7 @@ typedef struct {
     int32_t causal;
     float scale;
     int32_t dtype; /* lsh_dtype_t */
+    int32_t flags; /* lsh_flag_t bits */
 } lsh_problem_t;
 
 /* Human-readable text of a status code (static storage). */
@@ -126,7 +139,9 @@ int lsh_hash(const lsh_problem_t *prob, const void *q, const void *rot, int32_t 
  *           The non-causal set starts at the same index and ends at the last
  *           sorted index of t's bucket inside t's chunk; lsh_attn_fwd and
  *           the backwards derive that end from perm and win_lo, so the
- *           output of lsh_sort is the same for both kinds of problem.
+ *           output of lsh_sort is the same for both kinds of problem (and
+ *           with LSH_FLAG_NO_BUCKET_MASK, whose sets the attention calls
+ *           take from the chunks alone).
  *   ws      workspace of lsh_workspace_bytes(prob, LSH_WS_SORT) bytes.
  * Bucket values outside [0, nb) are undefined behaviour (not checked on the
  * device).

@@ -21,6 +21,7 @@ KERNELS = ("hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd",
 LSH_OK, LSH_ERR_INVALID, LSH_ERR_UNSUPPORTED, LSH_ERR_HIP = 0, 1, 2, 3
 LSH_F32, LSH_BF16 = 0, 1
 LSH_WS_SORT, LSH_WS_FWD, LSH_WS_BWD, LSH_WS_TRAIN, LSH_WS_REHASH = 0, 1, 2, 3, 4
+LSH_FLAG_NO_BUCKET_MASK = 1
 
 
 class Problem(ctypes.Structure):
@@ -28,7 +29,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n_hashes", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
                 ("chunk_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class LshError(RuntimeError):

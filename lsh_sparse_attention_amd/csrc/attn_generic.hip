@@ -26,10 +26,12 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kRowsPerWave = 4;
 
 // ---------------------------------------------------------------------------
-// prep: packed records, inverse norms, and (backward) D = dO . O
+// prep: packed records, inverse norms, and (backward) D = dO . O.  The
+// records' window start is win_lo, or with chunk_only (no bucket condition)
+// the start of the chunk before the row's chunk.
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *__restrict__ q,
+__global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, int m, int chunk_only, const T *__restrict__ q,
                                                         const int32_t *__restrict__ inv,
                                                         const int32_t *__restrict__ win_lo,
                                                         uint32_t *__restrict__ meta, uint32_t *__restrict__ srec,
@@ -59,7 +61,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *
             for (int r = ch; r < nh; r += CPT) {
                 const size_t idx = ((size_t)bh * nh + r) * L + t;
                 const uint32_t s = (uint32_t)inv[idx];
-                const uint32_t w = s - (uint32_t)win_lo[idx];
+                const int c = (int)s / m;
+                const uint32_t w = s - (chunk_only ? (uint32_t)max(0, (c - 1) * m) : (uint32_t)win_lo[idx]);
                 meta[tok * nh + r] = s | (w << 16);
                 srec[((size_t)bh * nh + r) * L + s] = (uint32_t)t | (w << 16);
             }
@@ -80,17 +83,46 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, const T *
     }
 }
 
-// Non-causal window records: for every (b, h, round) and sorted row s, the
-// attended set is the sorted range [s - w(s), hi(s)], hi(s) being the last
-// row of s's bucket inside s's chunk (same bucket, own chunk or the one
-// before, with no "not after the query" condition).  Along the sorted order
-// the window starts s' - w(s') do not decrease, and a later row s' of s's
-// chunk starts its window at or before s exactly when it is in s's bucket
-// (a later bucket starts after s), so hi(s) is found by bisection over
-// [s, end of chunk).  Writes wmeta[tok nh + r] = hi | (hi - win_lo) << 16.
-__global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, size_t total,
+// Smallest position in each chunk of every (b, h, round): one wave per
+// chunk, cmin[seg * (L / m) + c].
+__global__ __launch_bounds__(kThreads) void chunk_min_kernel(int L, int m, size_t nchunks,
+                                                             const uint32_t *__restrict__ srec,
+                                                             uint32_t *__restrict__ cmin)
+{
+    const size_t ch = (size_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (ch >= nchunks)
+        return;
+    const size_t nc = L / m, seg = ch / nc;
+    const uint32_t *sr = srec + seg * L + (ch % nc) * m;
+    uint32_t mn = 0xffffffffu;
+    for (int k = lane; k < m; k += kWave)
+        mn = min(mn, rec_lo(sr[k]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    if (lane == 0)
+        cmin[ch] = mn;
+}
+
+// Window records of kRange / kRangePos problems: for every (b, h, round) and
+// sorted row s, the candidates are the sorted range [s - w(s), hi(s)].  With
+// the bucket condition (non-causal), hi(s) is the last row of s's bucket
+// inside s's chunk: along the sorted order the window starts s' - w(s') do
+// not decrease, and a later row s' of s's chunk starts its window at or
+// before s exactly when it is in s's bucket (a later bucket starts after
+// s), so hi(s) is found by bisection over [s, end of chunk).  Without it
+// (chunk_only), hi(s) is the end of s's chunk.  Writes wmeta[tok nh + r] =
+// hi | (hi - start) << 16.  With alone (causal, no bucket condition: the
+// candidates not after the query are the members), alone[tok nh + r] = 1
+// when no other position of the window comes before the row's: its
+// position is the smallest of its chunk and below every position of the
+// chunk before (cmin).
+__global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, int chunk_only, size_t total,
                                                           const uint32_t *__restrict__ srec,
-                                                          uint32_t *__restrict__ wmeta)
+                                                          uint32_t *__restrict__ wmeta,
+                                                          const uint32_t *__restrict__ cmin,
+                                                          uint8_t *__restrict__ alone)
 {
     const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (idx >= total)
@@ -101,7 +133,10 @@ __global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, 
     const uint32_t *sr = srec + seg * L;
     const uint32_t rec = sr[s];
     const int lo = s - (int)rec_hi(rec);
-    int a = s, b = min((s / m + 1) * m, L) - 1;   // hi(s) in [a, b]
+    const int c = s / m;
+    int a = s, b = min((c + 1) * m, L) - 1;   // hi(s) in [a, b]
+    if (chunk_only)
+        a = b;
     while (a < b) {
         const int mid = (a + b + 1) >> 1;
         if (mid - (int)rec_hi(sr[mid]) <= s)
@@ -109,7 +144,12 @@ __global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, 
         else
             b = mid - 1;
     }
-    wmeta[(bh * L + rec_lo(rec)) * nh + r] = (uint32_t)a | ((uint32_t)(a - lo) << 16);
+    const size_t tok = bh * L + rec_lo(rec);
+    wmeta[tok * nh + r] = (uint32_t)a | ((uint32_t)(a - lo) << 16);
+    if (alone) {
+        const uint32_t pos = rec_lo(rec), *cm = cmin + seg * (size_t)(L / m);
+        alone[tok * nh + r] = (uint8_t)(pos == cm[c] && (c == 0 || pos < cm[c - 1]));
+    }
 }
 
 // Dot of a per-lane row (global) with a wave-distributed vector whose
@@ -168,7 +208,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scale, const T *__restrict__ q,
                                                        const T *__restrict__ v, const uint32_t *__restrict__ meta,
                                                        const uint32_t *__restrict__ srec,
-                                                       const uint32_t *__restrict__ wmeta,
+                                                       const uint32_t *__restrict__ wmeta, int pos_test,
                                                        const float *__restrict__ rnorm, T *__restrict__ o_rounds,
                                                        float *__restrict__ lse_rounds)
 {
@@ -199,6 +239,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
             bool valid = idx < kr0.n && kr0.lo + idx != s;
             const uint32_t kr = valid ? sr[kr0.lo + idx] : rec;
             const int j = (int)rec_lo(kr);
+            if (pos_test)
+                valid = valid && j < i;   // not after the query (chunk window without buckets)
             if (valid)
                 valid = !owned_earlier(mi, wi, meta + (tok0 + j) * nh, r);
             const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
@@ -328,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
                                                           const float *__restrict__ Dvec,
                                                           const uint32_t *__restrict__ meta,
                                                           const uint32_t *__restrict__ srec,
-                                                          const uint32_t *__restrict__ wmeta,
+                                                          const uint32_t *__restrict__ wmeta, int pos_test,
                                                           const float *__restrict__ rnorm,
                                                           float *__restrict__ dq_part)
 {
@@ -360,6 +402,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
             bool valid = idx < kr0.n && kr0.lo + idx != s;
             const uint32_t kr = valid ? sr[kr0.lo + idx] : rec;
             const int j = (int)rec_lo(kr);
+            if (pos_test)
+                valid = valid && j < i;   // not after the query (chunk window without buckets)
             if (valid)
                 valid = !owned_earlier(mi, wi, meta + (tok0 + j) * nh, r);
             const float rn = rnorm[tok0 + j];
@@ -407,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
                                                            const float *__restrict__ Dvec,
                                                            const uint32_t *__restrict__ meta,
                                                            const uint32_t *__restrict__ srec,
-                                                           const uint32_t *__restrict__ wmeta,
+                                                           const uint32_t *__restrict__ wmeta, int pos_test,
                                                            const float *__restrict__ rnorm,
                                                            float *__restrict__ dk_part, float *__restrict__ dv_part)
 {
@@ -434,6 +478,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
         }
         // one batch of candidate queries (lane: query i, valid if it attends j)
         auto batch = [&](bool valid, int i, int nk) {
+            if (pos_test)
+                valid = valid && j < i;
             if (valid)
                 valid = !owned_earlier(meta + (tok0 + i) * nh, wmeta ? wmeta + (tok0 + i) * nh : nullptr, mj, r);
             const float dp = dot_row_bcast<T, D>(q + (tok0 + i) * D, kreg);
@@ -458,7 +504,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
             }
         };
         if (wmeta) {
-            // earlier rows of j's bucket in j's chunk (non-causal only)
+            // earlier rows of j's bucket (or, without buckets, of j's window) in
+        // j's chunk: kRange and kRangePos only
             for (int qb = s - (int)rec_hi(krec); qb < s; qb += kWave) {
                 const int si = qb + lane;
                 bool ok = false;
@@ -505,6 +552,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int
                                                               const T *__restrict__ dout,
                                                               const uint32_t *__restrict__ meta,
                                                               const uint32_t *__restrict__ wmeta,
+                                                              const uint8_t *__restrict__ aflag,
                                                               const float *__restrict__ rnorm,
                                                               const float *__restrict__ dq_part,
                                                               const float *__restrict__ dk_part,
@@ -523,8 +571,11 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int
         aq[c] = ak[c] = av[c] = 0.f;
     bool alone = true;
     for (int r = 0; r < nh; ++r) {
-        // no member but itself: w = 0 (causal) or span = 0 (non-causal)
-        alone &= rec_hi((wmeta ? wmeta : meta)[(size_t)tok * nh + r]) == 0u;
+        // no member but itself: w = 0 (kBand), span = 0 (kRange) or the lone flag (kRangePos)
+        if (aflag)
+            alone &= aflag[(size_t)tok * nh + r] != 0;
+        else
+            alone &= rec_hi((wmeta ? wmeta : meta)[(size_t)tok * nh + r]) == 0u;
         const size_t row = (((size_t)bh * nh + r) * L + t) * D;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -563,18 +614,24 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int
 
 template <typename T, int D>
 hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32_t *win_lo, uint32_t *meta,
-                   uint32_t *srec, uint32_t *wmeta, float *rnorm, const void *out, const void *dout, float *Dv,
-                   hipStream_t st)
+                   uint32_t *srec, uint32_t *wmeta, uint8_t *alone, uint32_t *cmin, float *rnorm, const void *out,
+                   const void *dout, float *Dv, hipStream_t st)
 {
     constexpr int TPB = kThreads / (D / 8);
     dim3 grid((P.L + TPB - 1) / TPB, P.BH());
     ProfScope prof(LSH_KERNEL_PREP, st);
-    hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, (const T *)q, inv, win_lo,
-                       meta, srec, rnorm, (const T *)out, (const T *)dout, Dv);
+    const int chunk_only = P.bucket_mask ? 0 : 1;
+    hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.m, chunk_only, (const T *)q,
+                       inv, win_lo, meta, srec, rnorm, (const T *)out, (const T *)dout, Dv);
     if (meta && wmeta) {
+        if (alone) {
+            const size_t nchunks = (size_t)P.BH() * P.nh * (P.L / P.m);
+            hipLaunchKernelGGL(chunk_min_kernel, dim3((unsigned)((nchunks + kWaves - 1) / kWaves)), dim3(kThreads),
+                               0, st, P.L, P.m, nchunks, srec, cmin);
+        }
         const size_t total = (size_t)P.BH() * P.nh * P.L;
         hipLaunchKernelGGL(window_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                           st, P.L, P.nh, P.m, total, srec, wmeta);
+                           st, P.L, P.nh, P.m, chunk_only, total, srec, wmeta, cmin, alone);
     }
     return hipGetLastError();
 }
@@ -587,7 +644,8 @@ hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *m
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
     ProfScope prof(LSH_KERNEL_FWD, st);
     hipLaunchKernelGGL((fwd_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                       (const T *)v, meta, srec, wmeta, rnorm, (T *)o_rounds, lse_rounds);
+                       (const T *)v, meta, srec, wmeta, P.kind() == kRangePos ? 1 : 0, rnorm, (T *)o_rounds,
+                       lse_rounds);
     return hipGetLastError();
 }
 
@@ -616,21 +674,22 @@ hipError_t combine_go(const Dims &P, const void *q, const void *v, const void *o
 
 template <typename T, int D>
 hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const uint32_t *wmeta,
-                     const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part, void *dq,
-                     void *dv, hipStream_t st);
+                     const uint8_t *alone, const float *rnorm, const float *dq_part, const float *dk_part,
+                     const float *dv_part, void *dq, void *dv, hipStream_t st);
 
 template <typename T, int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
                   const float *Dv, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
-                  const float *rnorm, float *dq_part, float *dk_part, float *dv_part, void *dq, void *dv,
-                  hipStream_t st)
+                  const uint8_t *alone, const float *rnorm, float *dq_part, float *dk_part, float *dv_part, void *dq,
+                  void *dv, hipStream_t st)
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
+    const int pos_test = P.kind() == kRangePos ? 1 : 0;
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, rnorm, dq_part);
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, pos_test, rnorm, dq_part);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -638,22 +697,24 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DKV, st);
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, rnorm, dk_part, dv_part);
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, pos_test, rnorm, dk_part,
+                           dv_part);
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return reduce_go<T, D>(P, q, dout, meta, wmeta, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
+    return reduce_go<T, D>(P, q, dout, meta, wmeta, alone, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
 }
 
 template <typename T, int D>
 hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint32_t *meta, const uint32_t *wmeta,
-                     const float *rnorm, const float *dq_part, const float *dk_part, const float *dv_part, void *dq,
-                     void *dv, hipStream_t st)
+                     const uint8_t *alone, const float *rnorm, const float *dq_part, const float *dk_part,
+                     const float *dv_part, void *dq, void *dv, hipStream_t st)
 {
     const int ntok = P.BH() * P.L;
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
     hipLaunchKernelGGL((bwd_reduce_kernel<T, D>), dim3((ntok + kWaves - 1) / kWaves), dim3(kThreads), 0, st,
-                       P.L, P.nh, ntok, (const T *)q, (const T *)dout, meta, wmeta, rnorm, dq_part, dk_part, dv_part,
+                       P.L, P.nh, ntok, (const T *)q, (const T *)dout, meta, wmeta, alone, rnorm, dq_part, dk_part,
+                       dv_part,
                        (T *)dq, (T *)dv);
     return hipGetLastError();
 }
@@ -675,11 +736,12 @@ hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint3
 }  // namespace
 
 hipError_t launch_prep(const Dims &P, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
-                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, float *rnorm,
-                       const void *out, const void *dout, float *Dv, hipStream_t st)
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, uint8_t *alone,
+                       uint32_t *cmin, float *rnorm, const void *out, const void *dout, float *Dv, hipStream_t st)
 {
     (void)perm;
-    LSH_DISPATCH(dtype, P.d, (prep_go<T, D>(P, q, inv, win_lo, meta, srec, wmeta, rnorm, out, dout, Dv, st)));
+    LSH_DISPATCH(dtype, P.d,
+                 (prep_go<T, D>(P, q, inv, win_lo, meta, srec, wmeta, alone, cmin, rnorm, out, dout, Dv, st)));
 }
 
 hipError_t launch_attn_fwd(const Dims &P, int dtype, const void *q, const void *v, const uint32_t *meta,
@@ -697,11 +759,11 @@ hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v
 
 hipError_t launch_attn_bwd(const Dims &P, int dtype, const void *q, const void *v, const void *dout,
                            const float *lse, const float *Dv, const uint32_t *meta, const uint32_t *srec,
-                           const uint32_t *wmeta, const float *rnorm, float *dq_part, float *dk_part, float *dv_part,
-                           void *dq, void *dv, hipStream_t st)
+                           const uint32_t *wmeta, const uint8_t *alone, const float *rnorm, float *dq_part,
+                           float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t st)
 {
-    LSH_DISPATCH(dtype, P.d, (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, wmeta, rnorm, dq_part, dk_part,
-                                           dv_part, dq, dv, st)));
+    LSH_DISPATCH(dtype, P.d, (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, wmeta, alone, rnorm, dq_part,
+                                           dk_part, dv_part, dq, dv, st)));
 }
 
 }  // namespace lsh

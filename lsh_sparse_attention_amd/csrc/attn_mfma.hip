@@ -889,11 +889,14 @@ constexpr bool kv_sk_in_regs() { return D < 128 || NR <= 3; }
 // One query block against this wave's 16 keys.  The queries' windows, lse
 // and D are read with the operand rows, before any arithmetic.  skp[rr]:
 // this lane's key's sorted index in round rr (NR >= r), both halves of a
-// pair, or (see kv_sk_in_regs) entry ke of the key tile kt.  NC: non-causal
-// windows (the query tile layout of tile_prep_kernel).
-template <int D, int NR, bool NC>
+// pair, or (see kv_sk_in_regs) entry ke of the key tile kt.  MODE: the kind
+// of set (SetKind; kRange and kRangePos use the range layout of the query
+// tile, kRangePos also compares positions: qrec are the block's 32 sorted
+// records, kpos the lane's key position).
+template <int D, int NR, int MODE>
 __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt, const uint8_t *T, const uint8_t *kt,
-                                          int ke, int r, int qb, int sk, int g, int c, int lane, float krn2,
+                                          const uint32_t *qrec, int kpos, int ke, int r, int qb, int sk, int g, int c,
+                                          int lane, float krn2,
                                           float scale, const uint32_t (&skp)[NR], const bf16x8_t (&kop)[D / 32],
                                           const bf16x8_t (&vop)[D / 32], f32x4_t (&dka)[D / 16],
                                           f32x4_t (&dva)[D / 16])
@@ -909,6 +912,7 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
             qa[u][ks] = tile_row<D>(Qt, 16 * u + c, 32 * ks + 8 * g);
             ga[u][ks] = tile_row<D>(Gt, 16 * u + c, 32 * ks + 8 * g);
         }
+    constexpr bool NC = MODE != kBand;
     uint2 w4[2];
     float4 l4[2], d4[2];
 #pragma unroll
@@ -933,13 +937,21 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
     for (int u = 0; u < 2; ++u) {
         const int wv[4] = {(int)(w4[u].x & 0xffffu), (int)(w4[u].x >> 16), (int)(w4[u].y & 0xffffu),
                            (int)(w4[u].y >> 16)};
+        uint4 p4{};   // the queries' records (positions), kRangePos only: read after the products
+        if constexpr (MODE == kRangePos)
+            p4 = *reinterpret_cast<const uint4 *>(qrec + 16 * u + 4 * g);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int sq = qb + 16 * u + 4 * g + t;
             if constexpr (NC) {
-                // key in [sq - w, sq + hi - sq], not the query itself
+                // key in [sq - w, sq + hi - sq], not the query itself (and,
+                // kRangePos, not after it)
                 const int w = wv[t] & 0xff, n = w + (wv[t] >> 8) + 1;
                 ok[4 * u + t] = (unsigned)(sk - sq + w) < (unsigned)n && sk != sq;
+                if constexpr (MODE == kRangePos) {
+                    const uint32_t pr4[4] = {p4.x, p4.y, p4.z, p4.w};
+                    ok[4 * u + t] = ok[4 * u + t] && (uint32_t)kpos < rec_lo(pr4[t]);
+                }
             } else {
                 // key in [sq - w, sq)
                 ok[4 * u + t] = (unsigned)(sk - sq + wv[t]) < (unsigned)wv[t];
@@ -1049,7 +1061,7 @@ __device__ __forceinline__ void dkv_store(bf16 *dkr_part, bf16 *dv_part, size_t 
     store_row16<D>(dv_part + row, g, 1.f, dva);
 }
 
-template <int D, int NR, bool NC>
+template <int D, int NR, int MODE>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_stream_kernel(
     int L, int nh, int T, int m, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
@@ -1171,11 +1183,11 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             // causal: a block entirely at or before the keys sees none of
             // them; non-causal: one entirely before the chunk of the first key
             // (m is a power of two)
-            const bool before = NC ? qb + kBlk - 1 < (wk0 & -m) : qb + kBlk - 1 <= wk0;
+            const bool before = MODE != kBand ? qb + kBlk - 1 < (wk0 & -m) : qb + kBlk - 1 <= wk0;
             if (before || blk_lo > wk0 + 15)
                 return;
-            dkv_block<D, NR, NC>(Qs[st], Gs[st], Ts[st], kt, ke, r, qb, sk, g, c, lane, krn2, scale, skp, kop, vop,
-                                 dka, dva);
+            dkv_block<D, NR, MODE>(Qs[st], Gs[st], Ts[st], kt, recs + qb % kRecRing, kpos, ke, r, qb, sk, g, c, lane,
+                                   krn2, scale, skp, kop, vop, dka, dva);
         };
         for (int b = 0; b < 4 && b < nb; ++b)
             work(b);
@@ -1227,13 +1239,16 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // blocks (and the next tile's query rows are loaded into registers) while
 // the tile's own four blocks are worked on.
 
-template <int D, bool BWD, int NR, bool NC>
+template <int D, bool BWD, int NR, int MODE>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(
     int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dvec,
     const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const uint32_t *__restrict__ wmeta,
     const uint8_t *__restrict__ ktile, bf16 *__restrict__ out, float *__restrict__ lse_rounds)
 {
+    // the kind of set: kRange and kRangePos take the query's window from
+    // wmeta; kRangePos also compares positions
+    constexpr bool NC = MODE != kBand;
     __shared__ __align__(16) uint16_t Ks[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint8_t Kts[kStreamStages][kKTile];
@@ -1472,6 +1487,17 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 const int key = kb + 16 * (e / 4) + 4 * g + (e % 4);
                 ok[e] = (unsigned)(key - qlo) < (unsigned)cur.qw && (!NC || key != sq);
             }
+            if constexpr (MODE == kRangePos) {
+                // keys not after the query (positions from the record ring)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const uint4 p = *reinterpret_cast<const uint4 *>(recs + (kb + 16 * kk + 4 * g) % kRecRing);
+                    const uint32_t pk[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        ok[4 * kk + t] = ok[4 * kk + t] && rec_lo(pk[t]) < (uint32_t)cur.qpos;
+                }
+            }
             if (r > 0) {
                 uint32_t hit[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -1608,6 +1634,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
                                                           const bf16 *__restrict__ dout,
                                                           const uint32_t *__restrict__ meta,
                                                           const uint32_t *__restrict__ wmeta,
+                                                          const uint8_t *__restrict__ aflag,
                                                           const bf16 *__restrict__ dq_part,
                                                           const bf16 *__restrict__ dkr_part,
                                                           const bf16 *__restrict__ dv_part, bf16 *__restrict__ dq,
@@ -1630,8 +1657,9 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
             xq[r] = ld16(dq_part + off);
             xk[r] = ld16(dkr_part + off);
             xv[r] = ld16(dv_part + off);
-            // no member but itself: w = 0 (causal) or span = 0 (non-causal)
-            alone = alone && rec_hi((wmeta ? wmeta : meta)[(size_t)tok * nh + r]) == 0u;
+            // no member but itself: w = 0 (kBand), span = 0 (kRange) or the lone flag (kRangePos)
+            alone = alone && (aflag ? aflag[(size_t)tok * nh + r] != 0
+                                    : rec_hi((wmeta ? wmeta : meta)[(size_t)tok * nh + r]) == 0u);
         }
     float qv[8];
     load8(q + (size_t)tok * D + ch * 8, qv);
@@ -1688,8 +1716,8 @@ int stream_run_tiles(int nt, int segs)
 int max_window(const Dims &P) { return (2 * P.m + kBlk - 1) / kBlk * kBlk; }
 
 // The query-side stream kernel for the bound NR on the earlier rounds
-// (n_hashes - 1 rounded up to 1, 3, 7 or 13), causal or not.
-template <int D, bool BWD, bool NC>
+// (n_hashes - 1 rounded up to 1, 3, 7 or 13) and the kind of set.
+template <int D, bool BWD, int MODE>
 void q_stream_nc(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
                  const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *ktile, void *out,
                  float *lse_rounds, hipStream_t st)
@@ -1698,7 +1726,7 @@ void q_stream_nc(const Dims &P, const void *q, const void *v, const void *dout, 
     const int T = stream_run_tiles(nt, segs);
     const dim3 grid(segs * ((nt + T - 1) / T));
 #define LSH_QSTREAM(NR)                                                                                            \
-    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR, NC>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,    \
+    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR, MODE>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,  \
                        (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, wmeta, ktile,     \
                        (bf16 *)out, lse_rounds)
     if (P.nh <= 2)
@@ -1717,10 +1745,12 @@ void q_stream_go(const Dims &P, const void *q, const void *v, const void *dout, 
                  const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *ktile, void *out,
                  float *lse_rounds, hipStream_t st)
 {
-    if (P.causal)
-        q_stream_nc<D, BWD, false>(P, q, v, dout, lse, Dv, meta, srec, nullptr, ktile, out, lse_rounds, st);
+    if (P.kind() == kBand)
+        q_stream_nc<D, BWD, kBand>(P, q, v, dout, lse, Dv, meta, srec, nullptr, ktile, out, lse_rounds, st);
+    else if (P.kind() == kRange)
+        q_stream_nc<D, BWD, kRange>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, out, lse_rounds, st);
     else
-        q_stream_nc<D, BWD, true>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, out, lse_rounds, st);
+        q_stream_nc<D, BWD, kRangePos>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, out, lse_rounds, st);
 }
 
 // (non-causal problems take the stream kernels only: mfma_path_ok)
@@ -1742,8 +1772,9 @@ hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *m
 
 template <int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-                  const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const float *rnorm,
-                  const uint8_t *ktile, const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
+                  const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *alone,
+                  const float *rnorm, const uint8_t *ktile, const uint8_t *qtile, void *part, void *dq, void *dv,
+                  hipStream_t st)
 {
     // rows of one (token, round) are dq, dk rn, dv in turn (part_row)
     bf16 *dq_part = (bf16 *)part, *dkr_part = dq_part + D, *dv_part = dq_part + 2 * D;
@@ -1780,10 +1811,12 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
         LSH_DKV(7, NC);             \
     else                            \
         LSH_DKV(13, NC)
-            if (P.causal) {
-                LSH_DKV_NR(false);
+            if (P.kind() == kBand) {
+                LSH_DKV_NR(kBand);
+            } else if (P.kind() == kRange) {
+                LSH_DKV_NR(kRange);
             } else {
-                LSH_DKV_NR(true);
+                LSH_DKV_NR(kRangePos);
             }
 #undef LSH_DKV_NR
 #undef LSH_DKV
@@ -1799,8 +1832,8 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
 #define LSH_REDUCE(NH)                                                                                            \
     hipLaunchKernelGGL((reduce_kernel<D, NH>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok, \
-                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, P.causal ? nullptr : wmeta, dq_part,       \
-                       dkr_part, dv_part, (bf16 *)dq, (bf16 *)dv)
+                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, wmeta, alone, dq_part, dkr_part, dv_part,   \
+                       (bf16 *)dq, (bf16 *)dv)
     if (P.nh <= 2)
         LSH_REDUCE(2);
     else if (P.nh <= 4)
@@ -1831,10 +1864,10 @@ bool mfma_path_ok(const Dims &P, int dtype)
 {
     // the streamed range of a workgroup (at most 128 + 2 m + 31 sorted rows)
     // must fit the LDS record cache, and the metadata tiles hold 13 earlier
-    // rounds; non-causal problems run on the stream kernels only (chunk
-    // lengths that divide 128)
+    // rounds; sets other than the causal band run on the stream kernels only
+    // (chunk lengths that divide 128)
     return dtype == LSH_BF16 && (P.d == 64 || P.d == 128) && P.L % kRows == 0 && P.nh <= kMaxEarlier + 1 &&
-           kRows + 2 * P.m + kBlk <= kRecCache && (P.causal || kRows % P.m == 0);
+           kRows + 2 * P.m + kBlk <= kRecCache && (P.kind() == kBand || kRows % P.m == 0);
 }
 
 size_t mfma_ktile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * ktile_stride(P.nh); }
@@ -1845,7 +1878,7 @@ hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, con
                                 const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, uint8_t *ktile,
                                 void *o_rounds, float *lse_rounds, hipStream_t st)
 {
-    if (P.causal)
+    if (P.kind() == kBand)
         wmeta = nullptr;
     hipError_t e = tiles_go(P, srec, meta, wmeta, rnorm, nullptr, nullptr, ktile, nullptr, st);
     if (e != hipSuccess)
@@ -1857,17 +1890,19 @@ hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, con
 
 hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
                                 const float *Dv, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
-                                const float *rnorm, uint8_t *ktile, bool make_ktile, uint8_t *qtile, void *part,
-                                void *dq, void *dv, hipStream_t st)
+                                const uint8_t *alone, const float *rnorm, uint8_t *ktile, bool make_ktile,
+                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
 {
-    if (P.causal)
+    if (P.kind() == kBand)
         wmeta = nullptr;
+    if (P.kind() != kRangePos)
+        alone = nullptr;
     hipError_t e = tiles_go(P, srec, meta, wmeta, rnorm, lse, Dv, make_ktile ? ktile : nullptr, qtile, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)
-        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, wmeta, rnorm, ktile, qtile, part, dq, dv, st);
-    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, wmeta, rnorm, ktile, qtile, part, dq, dv, st);
+        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, wmeta, alone, rnorm, ktile, qtile, part, dq, dv, st);
+    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, wmeta, alone, rnorm, ktile, qtile, part, dq, dv, st);
 }
 
 }  // namespace lsh

@@ -73,17 +73,24 @@ __device__ __forceinline__ bool in_span(uint32_t wrec, uint32_t sj)
     return (rec_lo(wrec) - sj) <= rec_hi(wrec);   // unsigned: 0 <= hi-sj <= span
 }
 
+// Kinds of attended set (see include/lsh.h): the causal band of a bucket
+// run (kBand), a sorted range [win_lo, hi] per query (kRange: non-causal
+// problems, with or without the bucket condition), or, causal without the
+// bucket condition, the chunk window filtered by position (kRangePos).
+enum SetKind { kBand = 0, kRange = 1, kRangePos = 2 };
+
 struct Dims {
     int B, H, L, d, nh, nb, m;
     float scale;
-    bool causal;
+    bool causal, bucket_mask;
     int BH() const { return B * H; }
+    int kind() const { return causal ? (bucket_mask ? kBand : kRangePos) : kRange; }
 };
 
 inline Dims dims_of(const lsh_problem_t *p)
 {
     return Dims{p->batch, p->heads, p->seq_len, p->head_dim, p->n_hashes, p->n_buckets, p->chunk_len,
-                p->scale, p->causal != 0};
+                p->scale, p->causal != 0, (p->flags & LSH_FLAG_NO_BUCKET_MASK) == 0};
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -105,13 +112,14 @@ hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, 
 hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv,
                        int32_t *win_lo, void *ws, hipStream_t);
 size_t sort_ws_bytes(const Dims &);
-// Packed records, inverse norms, the non-causal window records (wmeta,
-// non-causal problems only; null otherwise) and (with out, dout)
-// D = dO . O; with meta null only D is written (the records are already in
-// place).
+// Packed records, inverse norms, the window records of kRange / kRangePos
+// problems (wmeta, null for kBand), the per-(token, round) lone flags of
+// kRangePos problems (alone, with cmin as scratch of L/m words per
+// (b, h, round); both null otherwise) and (with out, dout) D = dO . O; with
+// meta null only D is written (the records are already in place).
 hipError_t launch_prep(const Dims &, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
-                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, float *rnorm,
-                       const void *out, const void *dout, float *D, hipStream_t);
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, uint8_t *alone,
+                       uint32_t *cmin, float *rnorm, const void *out, const void *dout, float *D, hipStream_t);
 hipError_t launch_attn_fwd(const Dims &, int dtype, const void *q, const void *v, const uint32_t *meta,
                            const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, void *o_rounds,
                            float *lse_rounds, hipStream_t);
@@ -119,8 +127,8 @@ hipError_t launch_combine(const Dims &, int dtype, const void *q, const void *v,
                           const float *lse_rounds, void *out, float *lse, hipStream_t);
 hipError_t launch_attn_bwd(const Dims &, int dtype, const void *q, const void *v, const void *dout,
                            const float *lse, const float *D, const uint32_t *meta, const uint32_t *srec,
-                           const uint32_t *wmeta, const float *rnorm, float *dq_part, float *dk_part,
-                           float *dv_part, void *dq, void *dv, hipStream_t);
+                           const uint32_t *wmeta, const uint8_t *alone, const float *rnorm, float *dq_part,
+                           float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t);
 
 }  // namespace lsh
 
@@ -315,7 +323,7 @@ hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, cons
                                 void *o_rounds, float *lse_rounds, hipStream_t);
 hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
                                 const float *D, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
-                                const float *rnorm, uint8_t *ktile, bool make_ktile, uint8_t *qtile, void *part,
-                                void *dq, void *dv, hipStream_t);
+                                const uint8_t *alone, const float *rnorm, uint8_t *ktile, bool make_ktile,
+                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t);
 
 }  // namespace lsh

@@ -45,7 +45,8 @@ int validate(const lsh_problem_t *p)
         return LSH_ERR_INVALID;
     if (p->batch < 0 || p->heads < 0 || p->seq_len < 0 || p->head_dim < 1 || p->n_hashes < 1 ||
         p->n_buckets < 2 || (p->n_buckets & 1) || p->chunk_len < 1 || p->seq_len % p->chunk_len ||
-        !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16) || (p->causal != 0 && p->causal != 1))
+        !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16) || (p->causal != 0 && p->causal != 1) ||
+        (p->flags & ~(int32_t)LSH_FLAG_NO_BUCKET_MASK))
         return LSH_ERR_INVALID;
     if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128)
         return LSH_ERR_UNSUPPORTED;
@@ -64,36 +65,50 @@ bool empty(const lsh_problem_t *p) { return p->batch == 0 || p->heads == 0 || p-
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
-// wmeta (the non-causal window records) exists for non-causal problems
-// only, and is null otherwise.
+// Window records (wmeta) exist for kRange / kRangePos problems, lone flags
+// (alone) and per-chunk minimum positions (cmin, scratch) for kRangePos
+// only; they are null otherwise.
 struct FwdWs {
-    uint32_t *meta, *srec, *wmeta;
+    uint32_t *meta, *srec, *wmeta, *cmin;
+    uint8_t *alone;
     float *rnorm;
     uint8_t *ktile;
     size_t bytes;
 };
 
 struct BwdWs {
-    uint32_t *meta, *srec, *wmeta;
+    uint32_t *meta, *srec, *wmeta, *cmin;
+    uint8_t *alone;
     float *rnorm, *D, *dq_part, *dk_part, *dv_part;
     uint8_t *ktile, *qtile;
     size_t bytes;
 };
 
-FwdWs fwd_layout(const Dims &P, void *base)
+// The forward's part, shared by both layouts (a backward takes it over
+// from lsh_attn_fwd in lsh_attn_bwd_saved).
+template <typename W>
+size_t fwd_part(const Dims &P, uintptr_t b, W &w)
 {
     const size_t tok = (size_t)P.BH() * P.L, rnd = tok * P.nh;
-    const uintptr_t b = (uintptr_t)base;
-    FwdWs w{};
     size_t o = 0;
     w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
     w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
-    if (!P.causal) {
+    if (P.kind() != kBand) {
         w.wmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     }
-    w.bytes = o;
+    if (P.kind() == kRangePos) {
+        w.alone = (uint8_t *)(b + o); o += align_up(rnd, 256);
+        w.cmin = (uint32_t *)(b + o); o += align_up((size_t)P.BH() * P.nh * (P.L / P.m) * 4, 256);
+    }
+    return o;
+}
+
+FwdWs fwd_layout(const Dims &P, void *base)
+{
+    FwdWs w{};
+    w.bytes = fwd_part(P, (uintptr_t)base, w);
     return w;
 }
 
@@ -102,14 +117,7 @@ BwdWs bwd_layout(const Dims &P, void *base)
     const size_t tok = (size_t)P.BH() * P.L, rnd = tok * P.nh, part = rnd * P.d * sizeof(float);
     const uintptr_t b = (uintptr_t)base;
     BwdWs w{};
-    size_t o = 0;
-    w.meta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
-    w.srec = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
-    w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
-    w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
-    if (!P.causal) {
-        w.wmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
-    }
+    size_t o = fwd_part(P, b, w);
     // up to here the same offsets as the forward's workspace, so that a
     // backward can take over the forward's records
     w.D = (float *)(b + o); o += align_up(tok * 4, 256);
@@ -178,14 +186,14 @@ int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void
     const bool derive = perm != nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, derive ? w.meta : nullptr, w.srec, w.wmeta,
-                               w.rnorm, out, dout, w.D, s);
+                               w.alone, w.cmin, w.rnorm, out, dout, w.D, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype)) {
-            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.rnorm, w.ktile, derive,
-                                     w.qtile, w.dq_part, dq, dv, s);
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.alone, w.rnorm, w.ktile,
+                                     derive, w.qtile, w.dq_part, dq, dv, s);
         } else {
-            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.rnorm, w.dq_part,
-                                w.dk_part, w.dv_part, dq, dv, s);
+            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.alone, w.rnorm,
+                                w.dq_part, w.dk_part, w.dv_part, dq, dv, s);
         }
     }
     return hip_status(e);
@@ -206,7 +214,7 @@ const char *lsh_status_string(int status)
     }
 }
 
-int lsh_version(void) { return 300; }
+int lsh_version(void) { return 400; }
 
 const char *lsh_kernel_name(int kernel)
 {
@@ -277,8 +285,8 @@ int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     if (ws_bytes < w.bytes)
         return LSH_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.wmeta, w.rnorm, nullptr,
-                               nullptr, nullptr, s);
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.wmeta, w.alone, w.cmin,
+                               w.rnorm, nullptr, nullptr, nullptr, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype))
             e = launch_attn_fwd_mfma(P, q, v, w.meta, w.srec, w.wmeta, w.rnorm, w.ktile, o_rounds, lse_rounds, s);

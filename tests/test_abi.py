@@ -94,6 +94,27 @@ def test_causal_flag_values():
     assert L.lsh_workspace_bytes(ctypes.byref(n), 0) == L.lsh_workspace_bytes(ctypes.byref(c), 0)
 
 
+def test_flags_values():
+    L = _lib.lib()
+    dummy = ctypes.c_void_p(256)
+    p = _prob()
+    p.flags = 2                      # unknown bit
+    assert L.lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == 1
+    assert L.lsh_workspace_bytes(ctypes.byref(p), 1) == 0
+    c = _prob()
+    rnd = c.batch * c.heads * c.seq_len * c.n_hashes
+    a256 = lambda x: (x + 255) // 256 * 256
+    # without the bucket condition: window records, and for causal problems
+    # also the lone flags (one byte per token-round) and per-chunk minima
+    nbc = _prob(bucket_mask=False)
+    extra = a256(rnd * 4) + a256(rnd) + a256(rnd // c.chunk_len * 4)
+    nbn = _prob(bucket_mask=False, causal=False)
+    for kind in (1, 2, 3):
+        base = L.lsh_workspace_bytes(ctypes.byref(c), kind)
+        assert L.lsh_workspace_bytes(ctypes.byref(nbc), kind) == base + extra
+        assert L.lsh_workspace_bytes(ctypes.byref(nbn), kind) == base + a256(rnd * 4)
+
+
 def test_null_and_misaligned_pointers_rejected():
     p = _prob()
     L = _lib.lib()

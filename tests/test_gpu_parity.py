@@ -272,6 +272,83 @@ def test_noncausal_saved_standalone_and_rehash_backwards_agree(idx):
         assert torch.equal(bits(a), bits(b))
 
 
+# ----------------------------------------------------------------------------- no bucket mask
+# LSH_FLAG_NO_BUCKET_MASK: the chunks of the sorted order alone restrict
+# attention (causal: positions not after the query; non-causal: all).
+
+# name, B, H, L, d, nb, nh, m, dtype, clustered, causal
+NB_SMALL = [
+    ("nb-f32-causal", 1, 2, 1024, 64, 16, 3, 32, "f32", False, True),
+    ("nb-f32-noncausal", 1, 1, 512, 32, 8, 2, 16, "f32", False, False),
+    ("nb-f32-d128-m1", 1, 1, 256, 128, 8, 2, 1, "f32", False, True),
+    ("nb-f32-one-chunk", 1, 1, 256, 64, 8, 2, 256, "f32", False, True),
+    ("nb-tiny-L", 1, 1, 8, 32, 4, 2, 2, "f32", False, True),
+    ("nb-bf16-causal", 2, 2, 1024, 64, 16, 3, 32, "bf16", False, True),
+    ("nb-bf16-causal-d128", 1, 2, 2048, 128, 32, 2, 64, "bf16", False, True),
+    ("nb-bf16-causal-m128", 1, 2, 4096, 64, 64, 1, 128, "bf16", False, True),
+    ("nb-bf16-causal-m8", 1, 1, 1024, 64, 128, 2, 8, "bf16", False, True),
+    ("nb-bf16-causal-nh8", 1, 1, 1024, 128, 64, 8, 128, "bf16", False, True),
+    ("nb-bf16-causal-nh14", 1, 1, 512, 64, 16, 14, 32, "bf16", False, True),
+    ("nb-bf16-noncausal", 1, 2, 2048, 64, 32, 3, 64, "bf16", False, False),
+    ("nb-bf16-noncausal-d128-nh12", 1, 1, 1024, 128, 32, 12, 64, "bf16", False, False),
+    ("nb-bf16-clustered", 1, 2, 2048, 64, 64, 4, 64, "bf16", True, True),
+    ("nb-bf16-m96", 1, 2, 1536, 64, 32, 3, 96, "bf16", False, True),
+    ("nb-bf16-ragged-noncausal", 1, 1, 2016, 64, 64, 2, 32, "bf16", False, False),
+]
+
+
+def _nb_cfg(case):
+    name, B, H, L, d, nb, nh, m, dt, cl, causal = case
+    return gen.Config(name, B, H, L, d, nb, nh, m, dt, cl, True, 500 + NB_SMALL.index(case), n_clusters=16,
+                      causal=causal, bucket_mask=False)
+
+
+@pytest.mark.parametrize("case", NB_SMALL, ids=[c[0] for c in NB_SMALL])
+def test_no_bucket_mask_small_shapes_match_oracle(case):
+    cfg = _nb_cfg(case)
+    gu.say(f"[gpu] no-bucket-mask small case {cfg}")
+    x = gen.generate(cfg)
+    res = gu.run_gpu(x)
+    gu.check_sort_properties(res, cfg)
+    gu.compare_slices(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
+
+
+@pytest.mark.parametrize("name,causal,sl", [("text", True, (0, 4)), ("image", False, (0, 1))])
+def test_no_bucket_mask_workload_shapes_match_oracle(name, causal, sl):
+    x = dict(_full(name))
+    x["cfg"] = x["cfg"].with_(causal=causal, bucket_mask=False)
+    gu.say(f"[gpu] no-bucket-mask full-size {name} causal={causal}: running the library")
+    res = gu.run_gpu(x)
+    gu.say(f"[gpu] no-bucket-mask full-size {name}: oracle on slice {sl}")
+    gu.compare_slices(x, res, [sl])
+
+
+@pytest.mark.parametrize("idx", [0, 5, 7, 11, 14])
+def test_no_bucket_mask_backward_entry_points_agree(idx):
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    cfg = _nb_cfg(NB_SMALL[idx])
+    gu.say(f"[gpu] no-bucket-mask backward entry points {cfg}")
+    x = gen.generate(cfg)
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=cfg.causal, bucket_mask=False)
+    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
+    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
+    mod = lsh.LshAttention(prob)
+    mod.forward(q, v, rot)
+    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
+    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
+    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
+    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
+    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
+    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
+    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for a, b in ((dq, dq_s), (dv, dv_s), (dq2, dq_s), (dv2, dv_s)):
+        assert torch.equal(bits(a), bits(b))
+
+
 def test_empty_problem_is_a_no_op():
     import lsh_sparse_attention_amd as lsh
     gu.say("[gpu] empty problem L=0")
