@@ -54,6 +54,7 @@ class Config:
     cluster_sigma: float = 0.1
     causal: bool = True
     bucket_mask: bool = True
+    dup_by_bucket: bool = False
 
     @property
     def scale(self) -> float:

@@ -35,6 +35,12 @@
  *     h_r(j) = h_r(i) is dropped (the alternative reading in which the
  *     chunks of the sorted order alone restrict attention), nothing else
  *     changes.
+ *   - duplicate correction: by default every member of the union counts
+ *     once.  With `dup_by_bucket` (forward, backward), the count N_ij that
+ *     divides a pair is the number of rounds in which j shares i's bucket,
+ *     whether or not the round's chunks let i attend to j; a member that
+ *     i attends to in k_ij rounds then carries weight k_ij / N_ij (the two
+ *     readings agree when no bucket is cut by the chunk window).
  *   - the query attends to the union U_i of its round sets, each key once
  *     (duplicate correction); self is dropped from the union unless nothing
  *     else is in it, in which case o_i = v_i and lse_i = scale * q_i . k_i.
@@ -203,6 +209,23 @@ int lsh_oracle_union_mask(int L, int nh, int m, int causal, int bucket_mask, con
     return 0;
 }
 
+/* Weight of member j of U_i under the duplicate correction (App. A): 1, or
+ * with dup_by_bucket k_ij / N_ij, k_ij = rounds whose set holds j, N_ij =
+ * rounds in which j is in i's bucket. */
+static double dup_weight(int L, int nh, int m, int causal, int bucket_mask, int dup_by_bucket,
+                         const int32_t *buckets, const int32_t *inv, int i, int j)
+{
+    if (!dup_by_bucket)
+        return 1.0;
+    int k = 0, n = 0;
+    for (int r = 0; r < nh; ++r) {
+        const int32_t *bk = buckets + (size_t)r * L, *iv = inv + (size_t)r * L;
+        k += in_round_set(L, m, causal, bucket_mask, bk, iv, i, j);
+        n += bk[i] == bk[j];
+    }
+    return (double)k / (double)n;
+}
+
 static double dot(const double *a, const double *b, int d)
 {
     double s = 0.0;
@@ -229,8 +252,8 @@ static void make_keys(int L, int d, const double *q, double *k, double *qnorm)
  * empty set attends only to itself (§2 causal-masking bullet, App. A masking
  * bullet: the first token attends only to itself).                           */
 
-int lsh_oracle_forward(int L, int d, int nh, int m, int causal, int bucket_mask, double scale, const double *q,
-                       const double *v,
+int lsh_oracle_forward(int L, int d, int nh, int m, int causal, int bucket_mask, int dup_by_bucket, double scale,
+                       const double *q, const double *v,
                        const int32_t *buckets, const int32_t *perm, const int32_t *inv,
                        double *out /* [L][d] */, double *lse /* [L] */)
 {
@@ -258,7 +281,8 @@ int lsh_oracle_forward(int L, int d, int nh, int m, int causal, int bucket_mask,
             }
             double mx = -INFINITY;
             for (int a = 0; a < n; ++a) {
-                logit[a] = scale * dot(qi, k + (size_t)list[a] * d, d);
+                logit[a] = scale * dot(qi, k + (size_t)list[a] * d, d) +
+                           log(dup_weight(L, nh, m, causal, bucket_mask, dup_by_bucket, buckets, inv, i, list[a]));
                 if (logit[a] > mx)
                     mx = logit[a];
             }
@@ -306,8 +330,8 @@ static int in_union(int L, int nh, int m, int causal, int bucket_mask, const int
     return 0;
 }
 
-int lsh_oracle_backward(int L, int d, int nh, int m, int causal, int bucket_mask, double scale, const double *q,
-                        const double *v,
+int lsh_oracle_backward(int L, int d, int nh, int m, int causal, int bucket_mask, int dup_by_bucket, double scale,
+                        const double *q, const double *v,
                         const double *dout, const int32_t *buckets, const int32_t *perm,
                         const int32_t *inv, const double *out, const double *lse,
                         double *dq_out /* [L][d] */, double *dv_out /* [L][d] */)
@@ -338,7 +362,8 @@ int lsh_oracle_backward(int L, int d, int nh, int m, int causal, int bucket_mask
             alone[i] = (uint8_t)(n == 0);
             for (int a = 0; a < n; ++a) {
                 int j = list[a];
-                double p = exp(scale * dot(qi, k + (size_t)j * d, d) - lse[i]);
+                double p = exp(scale * dot(qi, k + (size_t)j * d, d) - lse[i]) *
+                           dup_weight(L, nh, m, causal, bucket_mask, dup_by_bucket, buckets, inv, i, j);
                 double g = p * (dot(doi, v + (size_t)j * d, d) - D[i]);
                 for (int c = 0; c < d; ++c)
                     dqi[c] += scale * g * k[(size_t)j * d + c];
@@ -372,7 +397,8 @@ int lsh_oracle_backward(int L, int d, int nh, int m, int causal, int bucket_mask
                         continue;
                     stamp[i] = j + 1;
                     const double *qi = q + (size_t)i * d, *doi = dout + (size_t)i * d;
-                    double p = exp(scale * dot(qi, kj, d) - lse[i]);
+                    double p = exp(scale * dot(qi, kj, d) - lse[i]) *
+                               dup_weight(L, nh, m, causal, bucket_mask, dup_by_bucket, buckets, inv, i, j);
                     double g = p * (dot(doi, vj, d) - D[i]);
                     for (int cc = 0; cc < d; ++cc) {
                         dvj[cc] += p * doi[cc];
@@ -405,7 +431,8 @@ int lsh_oracle_backward(int L, int d, int nh, int m, int causal, int bucket_mask
  * not NULL) backward.  Any output pointer may be NULL except those the later
  * stages need internally, which are then allocated here.                    */
 
-int lsh_oracle_head(int L, int d, int nh, int nb, int m, int causal, int bucket_mask, double scale, const double *q,
+int lsh_oracle_head(int L, int d, int nh, int nb, int m, int causal, int bucket_mask, int dup_by_bucket, double scale,
+                    const double *q,
                     const double *v, const double *rot, const double *dout, int32_t *buckets,
                     int32_t *perm, int32_t *inv, int32_t *win_lo, double *out, double *lse,
                     double *dq, double *dv)
@@ -423,9 +450,10 @@ int lsh_oracle_head(int L, int d, int nh, int nb, int m, int causal, int bucket_
     if (!rc)
         rc = lsh_oracle_sort(L, nh, m, bk, pr, iv, wl);
     if (!rc)
-        rc = lsh_oracle_forward(L, d, nh, m, causal, bucket_mask, scale, q, v, bk, pr, iv, o, ls);
+        rc = lsh_oracle_forward(L, d, nh, m, causal, bucket_mask, dup_by_bucket, scale, q, v, bk, pr, iv, o, ls);
     if (!rc && dout && dq && dv)
-        rc = lsh_oracle_backward(L, d, nh, m, causal, bucket_mask, scale, q, v, dout, bk, pr, iv, o, ls, dq, dv);
+        rc = lsh_oracle_backward(L, d, nh, m, causal, bucket_mask, dup_by_bucket, scale, q, v, dout, bk, pr, iv, o,
+                                 ls, dq, dv);
     if (!buckets) free(bk);
     if (!perm) free(pr);
     if (!inv) free(iv);

@@ -6,7 +6,9 @@ benchmark's CPU-baseline leg.  The GPU library never imports it.
 Arrays are per (batch, head) slice: q, v, dout [L, d] fp64, rot [nh, d, nb/2]
 fp64; integer outputs are int32 [nh, L].  ``causal`` selects the causal sets
 (the default) or the non-causal ones (no "not after the query" condition);
-``bucket_mask`` False drops the same-bucket condition (chunks alone restrict).
+``bucket_mask`` False drops the same-bucket condition (chunks alone restrict);
+``dup_by_bucket`` True counts duplicates over bucket co-membership in every
+round instead of over the attended sets.
 """
 from __future__ import annotations
 
@@ -94,7 +96,7 @@ def union_mask(buckets, perm, inv, chunk_len, causal=True, bucket_mask=True):
     return mask.astype(bool)
 
 
-def forward(q, v, buckets, perm, inv, chunk_len, scale, causal=True, bucket_mask=True):
+def forward(q, v, buckets, perm, inv, chunk_len, scale, causal=True, bucket_mask=True, dup_by_bucket=False):
     q, v = _f64(q), _f64(v)
     bk, perm, inv = _i32(buckets), _i32(perm), _i32(inv)
     L, d = q.shape
@@ -103,14 +105,16 @@ def forward(q, v, buckets, perm, inv, chunk_len, scale, causal=True, bucket_mask
     lse = np.empty(L, np.float64)
     rc = lib().lsh_oracle_forward(ctypes.c_int(L), ctypes.c_int(d), ctypes.c_int(nh),
                                   ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))),
-                                  ctypes.c_int(int(bool(bucket_mask))), ctypes.c_double(scale), _p(q), _p(v),
+                                  ctypes.c_int(int(bool(bucket_mask))), ctypes.c_int(int(bool(dup_by_bucket))),
+                                  ctypes.c_double(scale), _p(q), _p(v),
                                   _p(bk), _p(perm), _p(inv), _p(out), _p(lse))
     if rc:
         raise ValueError("oracle forward: invalid arguments")
     return out, lse
 
 
-def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=True, bucket_mask=True):
+def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=True, bucket_mask=True,
+             dup_by_bucket=False):
     q, v, dout, out, lse = _f64(q), _f64(v), _f64(dout), _f64(out), _f64(lse)
     bk, perm, inv = _i32(buckets), _i32(perm), _i32(inv)
     L, d = q.shape
@@ -119,7 +123,8 @@ def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=
     dv = np.empty((L, d), np.float64)
     rc = lib().lsh_oracle_backward(ctypes.c_int(L), ctypes.c_int(d), ctypes.c_int(nh),
                                    ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))),
-                                   ctypes.c_int(int(bool(bucket_mask))), ctypes.c_double(scale), _p(q), _p(v),
+                                   ctypes.c_int(int(bool(bucket_mask))), ctypes.c_int(int(bool(dup_by_bucket))),
+                                   ctypes.c_double(scale), _p(q), _p(v),
                                    _p(dout), _p(bk), _p(perm), _p(inv), _p(out), _p(lse), _p(dq),
                                    _p(dv))
     if rc:
@@ -127,7 +132,7 @@ def backward(q, v, dout, buckets, perm, inv, out, lse, chunk_len, scale, causal=
     return dq, dv
 
 
-def head(q, v, rot, n_buckets, chunk_len, scale, dout=None, causal=True, bucket_mask=True):
+def head(q, v, rot, n_buckets, chunk_len, scale, dout=None, causal=True, bucket_mask=True, dup_by_bucket=False):
     """Hash, sort, forward and (with ``dout``) backward of one slice."""
     q, v, rot = _f64(q), _f64(v), _f64(rot)
     L, d = q.shape
@@ -142,7 +147,7 @@ def head(q, v, rot, n_buckets, chunk_len, scale, dout=None, causal=True, bucket_
     rc = lib().lsh_oracle_head(
         ctypes.c_int(L), ctypes.c_int(d), ctypes.c_int(nh), ctypes.c_int(n_buckets),
         ctypes.c_int(chunk_len), ctypes.c_int(int(bool(causal))), ctypes.c_int(int(bool(bucket_mask))),
-        ctypes.c_double(scale), _p(q), _p(v),
+        ctypes.c_int(int(bool(dup_by_bucket))), ctypes.c_double(scale), _p(q), _p(v),
         _p(rot), _p(dout),
         _p(res["buckets"]), _p(res["perm"]), _p(res["inv"]), _p(res["win_lo"]), _p(res["out"]),
         _p(res["lse"]), _p(res.get("dq")), _p(res.get("dv")))
@@ -169,5 +174,5 @@ def run_inputs(inputs, slices=None, backward=None):
         v = to_f64(inputs["v"][b, h], cfg.dtype)
         do = to_f64(inputs["dout"][b, h], cfg.dtype) if backward else None
         res[(b, h)] = head(q, v, rot, cfg.n_buckets, cfg.chunk_len, cfg.scale, do, causal=cfg.causal,
-                           bucket_mask=cfg.bucket_mask)
+                           bucket_mask=cfg.bucket_mask, dup_by_bucket=cfg.dup_by_bucket)
     return res

@@ -51,12 +51,23 @@ def union_mask(bk, m, causal=True, bucket_mask=True):
     return round_masks(bk, m, causal, bucket_mask).any(axis=0)
 
 
-def attention(q, v, mask, scale):
+def dup_weights(bk, m, causal=True):
+    """[L, L] k_ij / N_ij: rounds whose set holds j over rounds in which j
+    shares i's bucket (the duplicate count over bucket co-membership)."""
+    k = round_masks(bk, m, causal).sum(axis=0)
+    n = sum((bk[r][:, None] == bk[r][None, :]).astype(np.int64) for r in range(bk.shape[0]))
+    return np.divide(k, n, out=np.zeros(k.shape), where=n > 0)
+
+
+def attention(q, v, mask, scale, weights=None):
     """Dense masked softmax over the union without self; a row with nothing
-    else attends to itself.  Returns (out, lse)."""
+    else attends to itself.  ``weights`` multiply the members' exponentials.
+    Returns (out, lse)."""
     L = q.shape[0]
     k = q / np.linalg.norm(q, axis=1, keepdims=True)
     logits = scale * (q @ k.T)
+    if weights is not None:
+        logits = logits + np.log(np.where(mask & (weights > 0), weights, 1.0))
     allowed = mask & ~np.eye(L, dtype=bool)
     empty = ~allowed.any(axis=1)
     allowed[empty, empty.nonzero()[0]] = True

@@ -584,6 +584,86 @@ def test_no_bucket_mask_matches_dense_autograd(seed, L, d, nb, nh, m, causal):
     np.testing.assert_allclose(res["dv"], vt.grad.numpy(), rtol=1e-10, atol=1e-11)
 
 
+# ----------------------------------------------------------------------------- duplicate count by bucket
+# The alternative duplicate count: N_ij over bucket co-membership in every
+# round; a member attended in k_ij rounds weighs k_ij / N_ij.
+
+def _lse_text(x):
+    return 0.0 if x == "0" else float(np.log(float(x.split()[1])))
+
+
+def test_dup_by_bucket_golden():
+    g = _golden()["attention_dup_by_bucket"]
+    bk = np.array(g["buckets"], np.int32)
+    L, m = g["L"], g["chunk_len"]
+    q = np.random.default_rng(0).standard_normal((L, L))
+    perm, inv, _ = ora.sort(bk, m)
+    out, lse = ora.forward(q, np.eye(L), bk, perm, inv, m, g["scale"], dup_by_bucket=True)
+    np.testing.assert_allclose(out, _weights_to_rows(g["out_rows_as_weights"], L), atol=1e-15)
+    np.testing.assert_allclose(lse, [_lse_text(x) for x in g["lse"]], atol=1e-15)
+    # the default count differs on the rows where a bucket is cut by the window
+    dflt, _ = ora.forward(q, np.eye(L), bk, perm, inv, m, g["scale"])
+    assert np.allclose(dflt[:4], out[:4]) and not np.allclose(dflt[4:], out[4:])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("seed,L,d,nb,nh,m", [(101, 128, 8, 4, 3, 8), (102, 160, 16, 2, 2, 16),
+                                              (103, 256, 8, 8, 4, 8)])
+def test_dup_by_bucket_matches_dense_bruteforce(seed, L, d, nb, nh, m, causal):
+    # few buckets and short chunks: buckets are cut by the window, so the
+    # two counts differ
+    q, v, rot, _ = _rand_problem(seed, L, d, nh, nb, scale_q=1.5)
+    scale = 1 / np.sqrt(d)
+    res = ora.head(q, v, rot, nb, m, scale, causal=causal, dup_by_bucket=True)
+    bk = bf.buckets(q, rot)
+    mask = bf.union_mask(bk, m, causal=causal)
+    out, lse = bf.attention(q, v, mask, scale, weights=bf.dup_weights(bk, m, causal=causal))
+    np.testing.assert_allclose(res["out"], out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse, rtol=1e-12, atol=1e-12)
+    dflt = ora.head(q, v, rot, nb, m, scale, causal=causal)
+    assert not np.allclose(dflt["out"], res["out"], atol=1e-6)
+
+
+def test_dup_by_bucket_equals_default_when_no_bucket_is_cut():
+    # m = L: a query's round set is its whole bucket (up to causality), so
+    # k_ij = N_ij for every member
+    q, v, rot, do = _rand_problem(104, 128, 8, 3, 8)
+    a = ora.head(q, v, rot, 8, 128, 0.6, dout=do)
+    b = ora.head(q, v, rot, 8, 128, 0.6, dout=do, dup_by_bucket=True)
+    for k in ("out", "lse", "dq", "dv"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-13, atol=1e-13)
+
+
+def test_dup_by_bucket_repeated_rotation_equals_one_round():
+    q, v, rot, _ = _rand_problem(105, 256, 16, 1, 4)
+    one = ora.head(q, v, rot, 4, 16, 0.3, dup_by_bucket=True)
+    three = ora.head(q, v, np.repeat(rot, 3, axis=0), 4, 16, 0.3, dup_by_bucket=True)
+    np.testing.assert_allclose(three["out"], one["out"], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dup_by_bucket_matches_dense_autograd(causal):
+    q, v, rot, do = _rand_problem(106, 128, 16, 3, 4, scale_q=1.3)
+    L, m, scale = 128, 8, 0.25
+    res = ora.head(q, v, rot, 4, m, scale, dout=do, causal=causal, dup_by_bucket=True)
+    bk = res["buckets"]
+    allowed = bf.union_mask(bk, m, causal=causal) & ~np.eye(L, dtype=bool)
+    empty = ~allowed.any(axis=1)
+    allowed[empty, np.nonzero(empty)[0]] = True
+    wt = np.where(allowed, bf.dup_weights(bk, m, causal=causal), 1.0)
+    wt[empty, np.nonzero(empty)[0]] = 1.0
+    qt = torch.tensor(q, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    kt = qt / qt.norm(dim=-1, keepdim=True)
+    logits = (scale * qt @ kt.T + torch.from_numpy(np.log(wt))).masked_fill(~torch.from_numpy(allowed),
+                                                                              float("-inf"))
+    out = torch.softmax(logits, dim=-1) @ vt
+    (out * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(res["out"], out.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(res["dq"], qt.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(res["dv"], vt.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
 # ----------------------------------------------------------------------------- inputs
 
 def test_generator_reproducible_and_margin():
