@@ -52,7 +52,14 @@ typedef enum {
      * the sorted order alone restrict attention (the alternative reading of
      * "Reformer" §2, where restricting each query to its own bucket is what
      * sorting and chunking approximate). */
-    LSH_FLAG_NO_BUCKET_MASK = 1
+    LSH_FLAG_NO_BUCKET_MASK = 1,
+    /* Count duplicates over bucket membership ("Reformer" App. A defines the
+     * count N_ij through the rounds in which j is in i's bucket): a member
+     * that the query attends to in k_ij rounds weighs k_ij / N_ij, N_ij =
+     * rounds in which it shares the query's bucket.  Without this flag each
+     * member of the union counts once.  The two agree unless a bucket is
+     * cut by the chunk window.  Not with LSH_FLAG_NO_BUCKET_MASK. */
+    LSH_FLAG_DUP_BY_BUCKET = 2
 } lsh_flag_t;
 
 /* Which call a workspace is for (lsh_workspace_bytes). */
@@ -83,9 +90,11 @@ typedef enum {
  *   scale: the softmax scale applied to q_i . k_j (1/sqrt(d) for standard
  *       scaled dot-product attention).
  *   dtype: element type of q, v, rot, out, dout, dq, dv and o_rounds.
- *   flags: 0, or LSH_FLAG_NO_BUCKET_MASK (round set of a query: every
- *       position of its own chunk and the one before, not after it when
- *       causal; the rest as above).  Unknown bits: LSH_ERR_INVALID.
+ *   flags: 0, LSH_FLAG_NO_BUCKET_MASK (round set of a query: every position
+ *       of its own chunk and the one before, not after it when causal; the
+ *       rest as above) or LSH_FLAG_DUP_BY_BUCKET (duplicate count over
+ *       bucket membership, see lsh_flag_t).  Unknown bits, or both:
+ *       LSH_ERR_INVALID.
  */
 typedef struct {
     int32_t batch, heads, seq_len, head_dim;

@@ -18,8 +18,8 @@ import math
 
 import torch
 
-from ._lib import (LSH_BF16, LSH_F32, LSH_FLAG_NO_BUCKET_MASK, LSH_WS_BWD, LSH_WS_FWD, LSH_WS_REHASH, LSH_WS_SORT,
-                   LSH_WS_TRAIN, LshError, Problem, check, lib)
+from ._lib import (LSH_BF16, LSH_F32, LSH_FLAG_DUP_BY_BUCKET, LSH_FLAG_NO_BUCKET_MASK, LSH_WS_BWD, LSH_WS_FWD,
+                   LSH_WS_REHASH, LSH_WS_SORT, LSH_WS_TRAIN, LshError, Problem, check, lib)
 
 __all__ = ["Problem", "LshError", "problem", "workspace_bytes", "lsh_hash", "lsh_sort", "lsh_attn_fwd",
            "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash", "LshAttention"]
@@ -28,8 +28,9 @@ _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
 
 
 def problem(batch, heads, seq_len, head_dim, n_hashes, n_buckets, chunk_len, scale=None,
-            dtype=torch.bfloat16, causal=True, bucket_mask=True) -> Problem:
-    """lsh_problem_t; ``bucket_mask=False`` sets LSH_FLAG_NO_BUCKET_MASK."""
+            dtype=torch.bfloat16, causal=True, bucket_mask=True, dup_by_bucket=False) -> Problem:
+    """lsh_problem_t; ``bucket_mask=False`` sets LSH_FLAG_NO_BUCKET_MASK, ``dup_by_bucket=True``
+    LSH_FLAG_DUP_BY_BUCKET."""
     if isinstance(dtype, str):
         dtype = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
     if dtype not in _DTYPES:
@@ -37,7 +38,8 @@ def problem(batch, heads, seq_len, head_dim, n_hashes, n_buckets, chunk_len, sca
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
     return Problem(batch, heads, seq_len, head_dim, n_hashes, n_buckets, chunk_len, int(bool(causal)),
-                   float(scale), _DTYPES[dtype], 0 if bucket_mask else LSH_FLAG_NO_BUCKET_MASK)
+                   float(scale), _DTYPES[dtype],
+                   (0 if bucket_mask else LSH_FLAG_NO_BUCKET_MASK) | (LSH_FLAG_DUP_BY_BUCKET if dup_by_bucket else 0))
 
 
 def torch_dtype(prob: Problem):

@@ -21,7 +21,7 @@ KERNELS = ("hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd",
 LSH_OK, LSH_ERR_INVALID, LSH_ERR_UNSUPPORTED, LSH_ERR_HIP = 0, 1, 2, 3
 LSH_F32, LSH_BF16 = 0, 1
 LSH_WS_SORT, LSH_WS_FWD, LSH_WS_BWD, LSH_WS_TRAIN, LSH_WS_REHASH = 0, 1, 2, 3, 4
-LSH_FLAG_NO_BUCKET_MASK = 1
+LSH_FLAG_NO_BUCKET_MASK, LSH_FLAG_DUP_BY_BUCKET = 1, 2
 
 
 class Problem(ctypes.Structure):

@@ -152,6 +152,52 @@ __global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, 
     }
 }
 
+// Start of each row's bucket run, per (b, h, round): a row starts a run
+// exactly when its window length w is 0 (its window start is then itself:
+// the bucket begins there; a row inside a run has a window start before
+// it), so the run start of sorted row s is the last s' <= s with w(s') = 0,
+// a prefix maximum.  One workgroup per (b, h, round); each thread takes a
+// contiguous stretch of rows.  Writes bmeta[tok nh + r].
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void bucket_start_kernel(int L, int nh, const uint32_t *__restrict__ srec,
+                                                                    uint32_t *__restrict__ bmeta)
+{
+    __shared__ int wave_max[kScanThreads / kWave];
+    const size_t seg = blockIdx.x;
+    const int r = (int)(seg % nh);
+    const size_t bh = seg / nh;
+    const uint32_t *sr = srec + seg * L;
+    const int per = (L + kScanThreads - 1) / kScanThreads;
+    const int s0 = min(L, (int)threadIdx.x * per), s1 = min(L, s0 + per);
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int mx = -1;
+    for (int s = s0; s < s1; ++s)
+        if (rec_hi(sr[s]) == 0u)
+            mx = s;
+    // inclusive prefix maximum over the threads
+    int x = mx;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o)
+            x = max(x, y);
+    }
+    if (lane == kWave - 1)
+        wave_max[wave] = x;
+    __syncthreads();
+    int carry = __shfl_up(x, 1, kWave);
+    if (lane == 0)
+        carry = -1;
+    for (int w = 0; w < wave; ++w)
+        carry = max(carry, wave_max[w]);
+    for (int s = s0; s < s1; ++s) {
+        const uint32_t rec = sr[s];
+        if (rec_hi(rec) == 0u)
+            carry = s;
+        bmeta[(bh * L + rec_lo(rec)) * nh + r] = (uint32_t)carry;
+    }
+}
+
 // Dot of a per-lane row (global) with a wave-distributed vector whose
 // component c sits in lane c % 64 of reg[c / 64].
 template <typename T, int D>
@@ -187,6 +233,14 @@ __device__ __forceinline__ bool owned_earlier(const uint32_t *__restrict__ meta_
     return hit;
 }
 
+// Log of the duplicate divisor of a member under LSH_FLAG_DUP_BY_BUCKET: the
+// number of rounds in which key j shares query i's bucket (from the
+// bucket-run starts per round, bmeta); 0 without it (bmeta null).
+__device__ __forceinline__ float dup_log(const uint32_t *__restrict__ bmeta, size_t tok_i, size_t tok_j, int nh)
+{
+    return bmeta ? logf((float)shared_buckets(bmeta + tok_i * nh, bmeta + tok_j * nh, nh)) : 0.f;
+}
+
 // Round-r key range of a sorted query row s: n candidates from sorted index
 // lo on (causal: [s - w, s - 1]; non-causal: [s - w, hi], where s itself is
 // skipped by the caller).
@@ -209,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
                                                        const T *__restrict__ v, const uint32_t *__restrict__ meta,
                                                        const uint32_t *__restrict__ srec,
                                                        const uint32_t *__restrict__ wmeta, int pos_test,
+                                                       const uint32_t *__restrict__ bmeta,
                                                        const float *__restrict__ rnorm, T *__restrict__ o_rounds,
                                                        float *__restrict__ lse_rounds)
 {
@@ -241,10 +296,12 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
             const int j = (int)rec_lo(kr);
             if (pos_test)
                 valid = valid && j < i;   // not after the query (chunk window without buckets)
-            if (valid)
+            // duplicates: the first-owner mask, or (bmeta) the log of the divisor
+            if (valid && !bmeta)
                 valid = !owned_earlier(mi, wi, meta + (tok0 + j) * nh, r);
+            const float dlog = valid ? dup_log(bmeta, tok0 + i, tok0 + j, nh) : 0.f;
             const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
-            const float logit = valid ? dp * scale * rnorm[tok0 + j] : -INFINITY;
+            const float logit = valid ? dp * scale * rnorm[tok0 + j] - dlog : -INFINITY;
             const float bm = wave_max(logit);
             if (bm == -INFINITY)
                 continue;
@@ -371,6 +428,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
                                                           const uint32_t *__restrict__ meta,
                                                           const uint32_t *__restrict__ srec,
                                                           const uint32_t *__restrict__ wmeta, int pos_test,
+                                                          const uint32_t *__restrict__ bmeta,
                                                           const float *__restrict__ rnorm,
                                                           float *__restrict__ dq_part)
 {
@@ -404,12 +462,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(int L, int nh, float s
             const int j = (int)rec_lo(kr);
             if (pos_test)
                 valid = valid && j < i;   // not after the query (chunk window without buckets)
-            if (valid)
+            // duplicates: the first-owner mask, or (bmeta) the log of the divisor
+            if (valid && !bmeta)
                 valid = !owned_earlier(mi, wi, meta + (tok0 + j) * nh, r);
+            const float dlog = valid ? dup_log(bmeta, tok0 + i, tok0 + j, nh) : 0.f;
             const float rn = rnorm[tok0 + j];
             const float dp = dot_row_bcast<T, D>(q + (tok0 + j) * D, qreg);
             const float dv = dot_row_bcast<T, D>(v + (tok0 + j) * D, goreg);
-            const float p = valid ? expf(dp * scale * rn - lse_i) : 0.f;
+            const float p = valid ? expf(dp * scale * rn - lse_i - dlog) : 0.f;
             const float coef = scale * p * (dv - D_i) * rn;
             const int nk = min(kWave, kr0.n - kb);
             for (int kk = 0; kk < nk; ++kk) {
@@ -452,6 +512,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
                                                            const uint32_t *__restrict__ meta,
                                                            const uint32_t *__restrict__ srec,
                                                            const uint32_t *__restrict__ wmeta, int pos_test,
+                                                           const uint32_t *__restrict__ bmeta,
                                                            const float *__restrict__ rnorm,
                                                            float *__restrict__ dk_part, float *__restrict__ dv_part)
 {
@@ -480,11 +541,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(int L, int nh, float 
         auto batch = [&](bool valid, int i, int nk) {
             if (pos_test)
                 valid = valid && j < i;
-            if (valid)
+            if (valid && !bmeta)
                 valid = !owned_earlier(meta + (tok0 + i) * nh, wmeta ? wmeta + (tok0 + i) * nh : nullptr, mj, r);
+            const float dlog = valid ? dup_log(bmeta, tok0 + i, tok0 + j, nh) : 0.f;
             const float dp = dot_row_bcast<T, D>(q + (tok0 + i) * D, kreg);
             const float dg = dot_row_bcast<T, D>(dout + (tok0 + i) * D, vreg);
-            const float p = valid ? expf(dp * scale - lse[tok0 + i]) : 0.f;
+            const float p = valid ? expf(dp * scale - lse[tok0 + i] - dlog) : 0.f;
             const float g = valid ? scale * p * (dg - Dvec[tok0 + i]) : 0.f;
             for (int kk = 0; kk < nk; ++kk) {
                 const float pk = readlane(p, kk);
@@ -614,9 +676,11 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(int L, int nh, int
 
 template <typename T, int D>
 hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32_t *win_lo, uint32_t *meta,
-                   uint32_t *srec, uint32_t *wmeta, uint8_t *alone, uint32_t *cmin, float *rnorm, const void *out,
-                   const void *dout, float *Dv, hipStream_t st)
+                   uint32_t *srec, const Extra &x, float *rnorm, const void *out, const void *dout, float *Dv,
+                   hipStream_t st)
 {
+    uint32_t *wmeta = x.wmeta, *cmin = x.cmin;
+    uint8_t *alone = x.alone;
     constexpr int TPB = kThreads / (D / 8);
     dim3 grid((P.L + TPB - 1) / TPB, P.BH());
     ProfScope prof(LSH_KERNEL_PREP, st);
@@ -633,19 +697,22 @@ hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32
         hipLaunchKernelGGL(window_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                            st, P.L, P.nh, P.m, chunk_only, total, srec, wmeta, cmin, alone);
     }
+    if (meta && x.bmeta)
+        hipLaunchKernelGGL(bucket_start_kernel, dim3((unsigned)(P.BH() * P.nh)), dim3(kScanThreads), 0, st, P.L, P.nh,
+                           srec, x.bmeta);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
-                  const uint32_t *wmeta, const float *rnorm, void *o_rounds, float *lse_rounds, hipStream_t st)
+                  const Extra &x, const float *rnorm, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
     ProfScope prof(LSH_KERNEL_FWD, st);
     hipLaunchKernelGGL((fwd_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                       (const T *)v, meta, srec, wmeta, P.kind() == kRangePos ? 1 : 0, rnorm, (T *)o_rounds,
-                       lse_rounds);
+                       (const T *)v, meta, srec, x.wmeta, P.kind() == kRangePos ? 1 : 0, x.bmeta, rnorm,
+                       (T *)o_rounds, lse_rounds);
     return hipGetLastError();
 }
 
@@ -679,9 +746,8 @@ hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint3
 
 template <typename T, int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
-                  const float *Dv, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
-                  const uint8_t *alone, const float *rnorm, float *dq_part, float *dk_part, float *dv_part, void *dq,
-                  void *dv, hipStream_t st)
+                  const float *Dv, const uint32_t *meta, const uint32_t *srec, const Extra &x, const float *rnorm,
+                  float *dq_part, float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t st)
 {
     const int rows = kWaves * kRowsPerWave;
     dim3 grid((P.L + rows - 1) / rows, P.nh, P.BH());
@@ -689,7 +755,8 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, pos_test, rnorm, dq_part);
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, x.wmeta, pos_test, x.bmeta, rnorm,
+                           dq_part);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -697,12 +764,12 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DKV, st);
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.scale, (const T *)q,
-                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, wmeta, pos_test, rnorm, dk_part,
-                           dv_part);
+                           (const T *)v, (const T *)dout, lse, Dv, meta, srec, x.wmeta, pos_test, x.bmeta, rnorm,
+                           dk_part, dv_part);
     }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return reduce_go<T, D>(P, q, dout, meta, wmeta, alone, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
+    return reduce_go<T, D>(P, q, dout, meta, x.wmeta, x.alone, rnorm, dq_part, dk_part, dv_part, dq, dv, st);
 }
 
 template <typename T, int D>
@@ -736,19 +803,18 @@ hipError_t reduce_go(const Dims &P, const void *q, const void *dout, const uint3
 }  // namespace
 
 hipError_t launch_prep(const Dims &P, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
-                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, uint8_t *alone,
-                       uint32_t *cmin, float *rnorm, const void *out, const void *dout, float *Dv, hipStream_t st)
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, const Extra &x, float *rnorm,
+                       const void *out, const void *dout, float *Dv, hipStream_t st)
 {
     (void)perm;
-    LSH_DISPATCH(dtype, P.d,
-                 (prep_go<T, D>(P, q, inv, win_lo, meta, srec, wmeta, alone, cmin, rnorm, out, dout, Dv, st)));
+    LSH_DISPATCH(dtype, P.d, (prep_go<T, D>(P, q, inv, win_lo, meta, srec, x, rnorm, out, dout, Dv, st)));
 }
 
 hipError_t launch_attn_fwd(const Dims &P, int dtype, const void *q, const void *v, const uint32_t *meta,
-                           const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, void *o_rounds,
+                           const uint32_t *srec, const Extra &x, const float *rnorm, void *o_rounds,
                            float *lse_rounds, hipStream_t st)
 {
-    LSH_DISPATCH(dtype, P.d, (fwd_go<T, D>(P, q, v, meta, srec, wmeta, rnorm, o_rounds, lse_rounds, st)));
+    LSH_DISPATCH(dtype, P.d, (fwd_go<T, D>(P, q, v, meta, srec, x, rnorm, o_rounds, lse_rounds, st)));
 }
 
 hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v, const void *o_rounds,
@@ -759,11 +825,11 @@ hipError_t launch_combine(const Dims &P, int dtype, const void *q, const void *v
 
 hipError_t launch_attn_bwd(const Dims &P, int dtype, const void *q, const void *v, const void *dout,
                            const float *lse, const float *Dv, const uint32_t *meta, const uint32_t *srec,
-                           const uint32_t *wmeta, const uint8_t *alone, const float *rnorm, float *dq_part,
-                           float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t st)
+                           const Extra &x, const float *rnorm, float *dq_part, float *dk_part, float *dv_part,
+                           void *dq, void *dv, hipStream_t st)
 {
-    LSH_DISPATCH(dtype, P.d, (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, wmeta, alone, rnorm, dq_part,
-                                           dk_part, dv_part, dq, dv, st)));
+    LSH_DISPATCH(dtype, P.d,
+                 (bwd_go<T, D>(P, q, v, dout, lse, Dv, meta, srec, x, rnorm, dq_part, dk_part, dv_part, dq, dv, st)));
 }
 
 }  // namespace lsh

@@ -185,6 +185,15 @@ __device__ __forceinline__ void dma_rows(const bf16 *__restrict__ a, const bf16 
     }
 }
 
+// 1 in each 16-bit half where a and b differ, else 0 (the halves of a sum of
+// such values count differing rounds without carrying into each other)
+__device__ __forceinline__ uint32_t ne16(uint32_t a, uint32_t b)
+{
+    const u16x2_t x = __builtin_bit_cast(u16x2_t, a ^ b);
+    const u16x2_t one = {1, 1};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(x, one));
+}
+
 // packed earlier-round test over 16 scores; ok[e] cleared where the key is in
 // the query's set of round rr.  qrec: (si1, w) pairs (query side) and
 // skp: key sorted-index pairs, arranged by the caller.
@@ -206,10 +215,14 @@ __device__ __forceinline__ void clear_hits(bool (&ok)[16], const uint32_t (&hit)
 // store w | (hi - s) << 8 for the tile's round (w < 256 and hi - s < 128 as
 // chunks are at most 128 rows) and (hi, span + 1) for the earlier ones (the
 // set with the query is [hi - span, hi]).
+// With bmeta (duplicates counted over buckets) the nh - 1 entries of both
+// tiles hold the bucket-run starts of the other rounds (round rr < r, then
+// rr + 1), in the key tile's index field and the query tile's first field.
 __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int ntiles, float scale_log2,
                                                              const uint32_t *__restrict__ srec,
                                                              const uint32_t *__restrict__ meta,
                                                              const uint32_t *__restrict__ wmeta,
+                                                             const uint32_t *__restrict__ bmeta,
                                                              const float *__restrict__ rnorm,
                                                              const float *__restrict__ lse,
                                                              const float *__restrict__ Dvec,
@@ -225,14 +238,16 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
     const uint32_t rec = srec[((size_t)bh * nh + r) * L + blk * kBlk + k];
     const size_t tok = (size_t)bh * L + rec_lo(rec);
     const uint32_t *m = meta + tok * nh;
-    const int nr = r < kMaxEarlier ? r : kMaxEarlier;
+    const uint32_t *bm = bmeta ? bmeta + tok * nh : nullptr;
+    const int nr = bm ? nh - 1 : (r < kMaxEarlier ? r : kMaxEarlier);
     if (lane < kBlk) {
         if (!ktile)
             return;
         uint8_t *kt = ktile + (size_t)tile * ktile_stride(nh);
         reinterpret_cast<float *>(kt)[k] = rnorm[tok] * scale_log2;
         for (int rr = 0; rr < nr; ++rr)
-            reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] = (uint16_t)rec_lo(m[rr]);
+            reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] =
+                (uint16_t)(bm ? bm[rr < r ? rr : rr + 1] : rec_lo(m[rr]));
     } else if (qtile) {
         uint8_t *qt = qtile + (size_t)tile * qtile_stride(nh);
         reinterpret_cast<float *>(qt)[k] = lse[tok] * kLog2e;
@@ -241,17 +256,23 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
             const uint32_t *wm = wmeta + tok * nh;
             const uint32_t u = rec_lo(wm[r]) - (uint32_t)(blk * kBlk + k);
             reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)(rec_hi(rec) | (u << 8));
-            for (int rr = 0; rr < nr; ++rr) {
+            for (int rr = 0; rr < (bm ? 0 : nr); ++rr) {
                 const uint32_t x = wm[rr];
                 reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)rec_lo(x);
                 reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)(rec_hi(x) + 1u);
             }
         } else {
             reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
-            for (int rr = 0; rr < nr; ++rr) {
+            for (int rr = 0; rr < (bm ? 0 : nr); ++rr) {
                 const uint32_t mr = m[rr];
                 reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(rec_lo(mr) - 1u);
                 reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)rec_hi(mr);
+            }
+        }
+        if (bm) {
+            for (int rr = 0; rr < nr; ++rr) {
+                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)bm[rr < r ? rr : rr + 1];
+                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = 0;
             }
         }
     }
@@ -885,18 +906,25 @@ constexpr int kRecRing = 512;                 // records of sorted rows x at x m
 // registers for a tile (else they are read from the key tile per block).
 template <int D, int NR>
 constexpr bool kv_sk_in_regs() { return D < 128 || NR <= 3; }
+// the same under the bucket duplicate count, whose divisor arithmetic needs
+// more registers at d = 128
+template <int D, int NR, bool DUPB>
+constexpr bool kv_sk_regs() { return DUPB ? D < 128 : kv_sk_in_regs<D, NR>(); }
 
 // One query block against this wave's 16 keys.  The queries' windows, lse
 // and D are read with the operand rows, before any arithmetic.  skp[rr]:
 // this lane's key's sorted index in round rr (NR >= r), both halves of a
-// pair, or (see kv_sk_in_regs) entry ke of the key tile kt.  MODE: the kind
+// pair, or (see kv_sk_regs) entry ke of the key tile kt.  MODE: the kind
 // of set (SetKind; kRange and kRangePos use the range layout of the query
 // tile, kRangePos also compares positions: qrec are the block's 32 sorted
 // records, kpos the lane's key position).
-template <int D, int NR, int MODE>
+// DUPB: duplicates weighed by the shared-bucket count (the nh - 1 tile
+// entries are bucket-run starts of the other rounds) instead of the
+// first-owner mask.
+template <int D, int NR, int MODE, bool DUPB>
 __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt, const uint8_t *T, const uint8_t *kt,
-                                          const uint32_t *qrec, int kpos, int ke, int r, int qb, int sk, int g, int c,
-                                          int lane, float krn2,
+                                          const uint32_t *qrec, int kpos, int ke, int r, int nh, int qb, int sk, int g,
+                                          int c, int lane, float krn2,
                                           float scale, const uint32_t (&skp)[NR], const bf16x8_t (&kop)[D / 32],
                                           const bf16x8_t (&vop)[D / 32], f32x4_t (&dka)[D / 16],
                                           f32x4_t (&dva)[D / 16])
@@ -958,9 +986,13 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
             }
         }
     }
-    if (r > 0) {
+    // DUPB: rounds in which a query's bucket differs from the key's, per
+    // 16-bit half (score e in half e % 2 of dif[e / 2])
+    uint32_t dif[4] = {0u, 0u, 0u, 0u};
+    if (DUPB ? nh > 1 : r > 0) {
         uint32_t hit[4] = {0u, 0u, 0u, 0u};
-        if constexpr (kv_sk_in_regs<D, NR>()) {
+        const int nrec = DUPB ? nh - 1 : r;
+        if constexpr (kv_sk_regs<D, NR, DUPB>()) {
             // the queries' (start - 1, length) pairs of every round rr < NR,
             // read without a branch so that they go out together (pairs of
             // rounds rr >= r lie within the LDS tile and are not used)
@@ -971,36 +1003,53 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
                 for (int u = 0; u < 2; ++u) {
                     const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
                     qa1[rr][u] = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
-                    qww[rr][u] = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                    if constexpr (!DUPB)   // DUPB uses the first field only
+                        qww[rr][u] = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
                 }
 #pragma unroll
             for (int rr = 0; rr < NR; ++rr)
-                if (rr < r) {
+                if (rr < nrec) {
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
-                        hit[2 * u] |= win_hits2(qa1[rr][u].x, qww[rr][u].x, skp[rr]);
-                        hit[2 * u + 1] |= win_hits2(qa1[rr][u].y, qww[rr][u].y, skp[rr]);
+                        if constexpr (DUPB) {
+                            hit[2 * u] += ne16(qa1[rr][u].x, skp[rr]);
+                            hit[2 * u + 1] += ne16(qa1[rr][u].y, skp[rr]);
+                        } else {
+                            hit[2 * u] |= win_hits2(qa1[rr][u].x, qww[rr][u].x, skp[rr]);
+                            hit[2 * u + 1] |= win_hits2(qa1[rr][u].y, qww[rr][u].y, skp[rr]);
+                        }
                     }
                 }
         } else {
 #pragma unroll
             for (int rr = 0; rr < NR; ++rr)
-                if (rr < r) {
+                if (rr < nrec) {
                     const uint32_t kp = bcast16(reinterpret_cast<const uint16_t *>(kt + 128 + 64 * rr)[ke]);
                     // the queries' (start - 1, length) pairs in round rr
                     const uint16_t *s1 = reinterpret_cast<const uint16_t *>(T + 320 + 128 * rr);
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const uint2 a = *reinterpret_cast<const uint2 *>(s1 + 16 * u + 4 * g);
-                        const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
-                        hit[2 * u] |= win_hits2(a.x, ww.x, kp);
-                        hit[2 * u + 1] |= win_hits2(a.y, ww.y, kp);
+                        if constexpr (DUPB) {
+                            hit[2 * u] += ne16(a.x, kp);
+                            hit[2 * u + 1] += ne16(a.y, kp);
+                        } else {
+                            const uint2 ww = *reinterpret_cast<const uint2 *>(s1 + 32 + 16 * u + 4 * g);
+                            hit[2 * u] |= win_hits2(a.x, ww.x, kp);
+                            hit[2 * u + 1] |= win_hits2(a.y, ww.y, kp);
+                        }
                     }
                 }
         }
+        if constexpr (DUPB) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+            for (int k = 0; k < 4; ++k)
+                dif[k] = hit[k];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+        }
     }
     float pr[8], gr[8];
 #pragma unroll
@@ -1009,7 +1058,9 @@ __device__ __forceinline__ void dkv_block(const uint16_t *Qt, const uint16_t *Gt
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int e = 4 * u + t;
-            pr[e] = ok[e] ? fast_exp2(sacc[u][t] * krn2 - lv[t]) : 0.f;
+            // log2 of the duplicate divisor: the rounds sharing the bucket
+            const float lg = DUPB ? __log2f((float)(nh - (int)((dif[e / 2] >> (16 * (e % 2))) & 0xffffu))) : 0.f;
+            pr[e] = ok[e] ? fast_exp2(sacc[u][t] * krn2 - lv[t] - lg) : 0.f;
             gr[e] = pr[e] * (pacc[u][t] - dv[t]) * scale;
         }
     }
@@ -1061,7 +1112,7 @@ __device__ __forceinline__ void dkv_store(bf16 *dkr_part, bf16 *dv_part, size_t 
     store_row16<D>(dv_part + row, g, 1.f, dva);
 }
 
-template <int D, int NR, int MODE>
+template <int D, int NR, int MODE, bool DUPB>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_stream_kernel(
     int L, int nh, int T, int m, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const uint32_t *__restrict__ srec, const uint8_t *__restrict__ ktile,
@@ -1157,7 +1208,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         const float krn2 = reinterpret_cast<const float *>(kt)[ke];   // rn * scale * log2(e)
         const float rn = krn2 * inv_sl2;
         uint32_t skp[NR];   // the key's sorted index in the earlier rounds
-        if constexpr (kv_sk_in_regs<D, NR>()) {
+        if constexpr (kv_sk_regs<D, NR, DUPB>()) {
             // read for every rr < NR without a branch, so the reads go out
             // together (entries rr >= r are within the LDS tile and unused)
 #pragma unroll
@@ -1186,8 +1237,8 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const bool before = MODE != kBand ? qb + kBlk - 1 < (wk0 & -m) : qb + kBlk - 1 <= wk0;
             if (before || blk_lo > wk0 + 15)
                 return;
-            dkv_block<D, NR, MODE>(Qs[st], Gs[st], Ts[st], kt, recs + qb % kRecRing, kpos, ke, r, qb, sk, g, c, lane,
-                                   krn2, scale, skp, kop, vop, dka, dva);
+            dkv_block<D, NR, MODE, DUPB>(Qs[st], Gs[st], Ts[st], kt, recs + qb % kRecRing, kpos, ke, r, nh, qb, sk, g,
+                                         c, lane, krn2, scale, skp, kop, vop, dka, dva);
         };
         for (int b = 0; b < 4 && b < nb; ++b)
             work(b);
@@ -1239,15 +1290,19 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // blocks (and the next tile's query rows are loaded into registers) while
 // the tile's own four blocks are worked on.
 
-template <int D, bool BWD, int NR, int MODE>
+template <int D, bool BWD, int NR, int MODE, bool DUPB>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(
     int L, int nh, int T, float scale, const bf16 *__restrict__ q, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ Dvec,
     const uint32_t *__restrict__ meta, const uint32_t *__restrict__ srec, const uint32_t *__restrict__ wmeta,
-    const uint8_t *__restrict__ ktile, bf16 *__restrict__ out, float *__restrict__ lse_rounds)
+    const uint32_t *__restrict__ bmeta, const uint8_t *__restrict__ ktile, bf16 *__restrict__ out,
+    float *__restrict__ lse_rounds)
 {
     // the kind of set: kRange and kRangePos take the query's window from
-    // wmeta; kRangePos also compares positions
+    // wmeta; kRangePos also compares positions.  DUPB: duplicates weighed by
+    // the shared-bucket count instead of the first-owner mask; the records
+    // of the other nh - 1 rounds (round rr < r, then rr + 1) are then
+    // bucket-run starts (bmeta), and so are the key tiles' entries.
     constexpr bool NC = MODE != kBand;
     __shared__ __align__(16) uint16_t Ks[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
@@ -1270,6 +1325,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int lb = xcd_block(blockIdx.x, gridDim.x);
     const int seg = lb / rps, run = lb % rps;
     const int r = seg % nh, bh = seg / nh;
+    const int nrec = DUPB ? nh - 1 : r;   // other-round records in use
     const int t_begin = run * T, t_end = min(nt, t_begin + T);
     const uint32_t *sr = srec + (size_t)seg * L;
     const size_t tok0 = (size_t)bh * L;
@@ -1322,12 +1378,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         }
 #pragma unroll
         for (int rr = 0; rr < NR; ++rr)
-            if (rr < r)
-                R.qm[rr] = (NC ? wmeta : meta)[tok * nh + rr];
+            if (rr < nrec)
+                R.qm[rr] = DUPB ? bmeta[tok * nh + (rr < r ? rr : rr + 1)] : (NC ? wmeta : meta)[tok * nh + rr];
     };
     // the earlier-round test of a query record: key sorted index sk hits
-    // when (x - sk) mod 2^16 < n, as pairs of 16-bit halves
-    auto win_x = [](uint32_t qm) { return bcast16(NC ? rec_lo(qm) : rec_lo(qm) - 1u); };
+    // when (x - sk) mod 2^16 < n, as pairs of 16-bit halves (DUPB: x is the
+    // bucket-run start, compared for equality)
+    auto win_x = [](uint32_t qm) { return bcast16(DUPB || NC ? rec_lo(qm) : rec_lo(qm) - 1u); };
     auto win_n = [](uint32_t qm) { return bcast16(NC ? rec_hi(qm) + 1u : rec_hi(qm)); };
 
     // prologue: records [s0 - 128, s0 + 256), then the first tile's eight blocks and query rows
@@ -1378,7 +1435,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             if (g == 0) {
 #pragma unroll
                 for (int rr = 0; rr < NR; ++rr)
-                    if (rr < r)
+                    if (rr < nrec)
                         qmL[wave][rr][c] = cur.qm[rr];
             }
         }
@@ -1453,7 +1510,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             if constexpr (kEarlySk) {
 #pragma unroll
                 for (int rr = 0; rr < NR; ++rr)
-                    if (rr < r) {
+                    if (rr < nrec) {
 #pragma unroll
                         for (int kk = 0; kk < 2; ++kk)
                             kp[rr][kk] = read_sk(rr, kk);
@@ -1498,24 +1555,35 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                         ok[4 * kk + t] = ok[4 * kk + t] && rec_lo(pk[t]) < (uint32_t)cur.qpos;
                 }
             }
-            if (r > 0) {
-                uint32_t hit[4] = {0u, 0u, 0u, 0u};
+            float lg[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // log2 of the duplicate divisor (DUPB)
+            if (nrec > 0) {
+                uint32_t hit[4] = {0u, 0u, 0u, 0u};   // DUPB: rounds with a different bucket, per 16-bit half
 #pragma unroll
                 for (int rr = 0; rr < NR; ++rr)
-                    if (rr < r) {
+                    if (rr < nrec) {
 #pragma unroll
                         for (int kk = 0; kk < 2; ++kk) {
                             const uint2 k2 = kEarlySk ? kp[kEarlySk ? rr : 0][kk] : read_sk(rr, kk);
                             const uint32_t qmr = kKeepWin ? 0u : qmL[kKeepWin ? 0 : wave][kKeepWin ? 0 : rr][c];
                             const uint32_t s1 = kKeepWin ? si1p[kKeepWin ? rr : 0] : win_x(qmr);
-                            const uint32_t w1 = kKeepWin ? wp[kKeepWin ? rr : 0] : win_n(qmr);
-                            hit[2 * kk] |= win_hits2(s1, w1, k2.x);
-                            hit[2 * kk + 1] |= win_hits2(s1, w1, k2.y);
+                            if constexpr (DUPB) {
+                                hit[2 * kk] += ne16(s1, k2.x);
+                                hit[2 * kk + 1] += ne16(s1, k2.y);
+                            } else {
+                                const uint32_t w1 = kKeepWin ? wp[kKeepWin ? rr : 0] : win_n(qmr);
+                                hit[2 * kk] |= win_hits2(s1, w1, k2.x);
+                                hit[2 * kk + 1] |= win_hits2(s1, w1, k2.y);
+                            }
                         }
                     }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    ok[e] = ok[e] && ((hit[e / 2] >> (16 * (e % 2))) & 0xffffu) == 0u;
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t h = (hit[e / 2] >> (16 * (e % 2))) & 0xffffu;
+                    if constexpr (DUPB)
+                        lg[e] = __log2f((float)(nh - (int)h));
+                    else
+                        ok[e] = ok[e] && h == 0u;
+                }
             }
             if constexpr (!kEarlySk)
                 read_rn();
@@ -1527,10 +1595,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 for (int tt = 0; tt < 4; ++tt) {
                     const int e = 4 * kk + tt;
                     if constexpr (BWD) {
-                        const float pr = ok[e] ? fast_exp2(fmaf(sacc[kk][tt], rn[tt], -cur.lse2)) : 0.f;
+                        const float pr = ok[e] ? fast_exp2(fmaf(sacc[kk][tt], rn[tt], -cur.lse2) - lg[e]) : 0.f;
                         x[e] = pr * (pacc[kk][tt] - cur.Di) * (rn[tt] * kLn2);
                     } else {
-                        x[e] = ok[e] ? sacc[kk][tt] * rn[tt] : -INFINITY;
+                        x[e] = ok[e] ? sacc[kk][tt] * rn[tt] - lg[e] : -INFINITY;
                     }
                 }
             }
@@ -1717,18 +1785,18 @@ int max_window(const Dims &P) { return (2 * P.m + kBlk - 1) / kBlk * kBlk; }
 
 // The query-side stream kernel for the bound NR on the earlier rounds
 // (n_hashes - 1 rounded up to 1, 3, 7 or 13) and the kind of set.
-template <int D, bool BWD, int MODE>
+template <int D, bool BWD, int MODE, bool DUPB>
 void q_stream_nc(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-                 const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *ktile, void *out,
-                 float *lse_rounds, hipStream_t st)
+                 const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint32_t *bmeta,
+                 const uint8_t *ktile, void *out, float *lse_rounds, hipStream_t st)
 {
     const int nt = P.L / kRows, segs = P.BH() * P.nh;
     const int T = stream_run_tiles(nt, segs);
     const dim3 grid(segs * ((nt + T - 1) / T));
 #define LSH_QSTREAM(NR)                                                                                            \
-    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR, MODE>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T, P.scale,  \
-                       (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, wmeta, ktile,     \
-                       (bf16 *)out, lse_rounds)
+    hipLaunchKernelGGL((q_stream_kernel<D, BWD, NR, MODE, DUPB>), grid, dim3(kKvThreads), 0, st, P.L, P.nh, T,      \
+                       P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, wmeta,   \
+                       bmeta, ktile, (bf16 *)out, lse_rounds)
     if (P.nh <= 2)
         LSH_QSTREAM(1);
     else if (P.nh <= 4)
@@ -1742,26 +1810,36 @@ void q_stream_nc(const Dims &P, const void *q, const void *v, const void *dout, 
 
 template <int D, bool BWD>
 void q_stream_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-                 const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *ktile, void *out,
+                 const uint32_t *meta, const uint32_t *srec, const Extra &x, const uint8_t *ktile, void *out,
                  float *lse_rounds, hipStream_t st)
 {
-    if (P.kind() == kBand)
-        q_stream_nc<D, BWD, kBand>(P, q, v, dout, lse, Dv, meta, srec, nullptr, ktile, out, lse_rounds, st);
-    else if (P.kind() == kRange)
-        q_stream_nc<D, BWD, kRange>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, out, lse_rounds, st);
-    else
-        q_stream_nc<D, BWD, kRangePos>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, out, lse_rounds, st);
+    const uint32_t *wm = x.wmeta, *bm = x.bmeta;
+    if (P.dup_bucket) {
+        if (P.kind() == kBand)
+            q_stream_nc<D, BWD, kBand, true>(P, q, v, dout, lse, Dv, meta, srec, nullptr, bm, ktile, out, lse_rounds,
+                                             st);
+        else
+            q_stream_nc<D, BWD, kRange, true>(P, q, v, dout, lse, Dv, meta, srec, wm, bm, ktile, out, lse_rounds, st);
+    } else if (P.kind() == kBand) {
+        q_stream_nc<D, BWD, kBand, false>(P, q, v, dout, lse, Dv, meta, srec, nullptr, nullptr, ktile, out,
+                                          lse_rounds, st);
+    } else if (P.kind() == kRange) {
+        q_stream_nc<D, BWD, kRange, false>(P, q, v, dout, lse, Dv, meta, srec, wm, nullptr, ktile, out, lse_rounds,
+                                           st);
+    } else {
+        q_stream_nc<D, BWD, kRangePos, false>(P, q, v, dout, lse, Dv, meta, srec, wm, nullptr, ktile, out,
+                                              lse_rounds, st);
+    }
 }
 
 // (non-causal problems take the stream kernels only: mfma_path_ok)
 template <int D>
 hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *meta, const uint32_t *srec,
-                  const uint32_t *wmeta, const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
+                  const Extra &x, const uint8_t *ktile, void *o_rounds, float *lse_rounds, hipStream_t st)
 {
     ProfScope prof(LSH_KERNEL_FWD, st);
     if (kRows % P.m == 0) {
-        q_stream_go<D, false>(P, q, v, nullptr, nullptr, nullptr, meta, srec, wmeta, ktile, o_rounds, lse_rounds,
-                              st);
+        q_stream_go<D, false>(P, q, v, nullptr, nullptr, nullptr, meta, srec, x, ktile, o_rounds, lse_rounds, st);
     } else {
         hipLaunchKernelGGL((fwd_kernel<D>), dim3((P.L / kRows) * P.nh * P.BH()), dim3(kThreads), 0, st, P.L, P.nh,
                            max_window(P), P.scale * kLog2e, (const bf16 *)q, (const bf16 *)v, meta, srec, ktile,
@@ -1772,9 +1850,8 @@ hipError_t fwd_go(const Dims &P, const void *q, const void *v, const uint32_t *m
 
 template <int D>
 hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout, const float *lse, const float *Dv,
-                  const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta, const uint8_t *alone,
-                  const float *rnorm, const uint8_t *ktile, const uint8_t *qtile, void *part, void *dq, void *dv,
-                  hipStream_t st)
+                  const uint32_t *meta, const uint32_t *srec, const Extra &x, const float *rnorm,
+                  const uint8_t *ktile, const uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
 {
     // rows of one (token, round) are dq, dk rn, dv in turn (part_row)
     bf16 *dq_part = (bf16 *)part, *dkr_part = dq_part + D, *dv_part = dq_part + 2 * D;
@@ -1782,7 +1859,7 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     {
         ProfScope prof(LSH_KERNEL_BWD_DQ, st);
         if (kRows % P.m == 0) {
-            q_stream_go<D, true>(P, q, v, dout, lse, Dv, meta, srec, wmeta, ktile, dq_part, nullptr, st);
+            q_stream_go<D, true>(P, q, v, dout, lse, Dv, meta, srec, x, ktile, dq_part, nullptr, st);
         } else {
             hipLaunchKernelGGL((dq_kernel<D>), grid, dim3(kThreads), 0, st, P.L, P.nh, max_window(P), P.scale,
                                (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, lse, Dv, meta, srec, ktile,
@@ -1798,25 +1875,31 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
             const int nt = P.L / kRows, segs = P.BH() * P.nh;
             const int T = stream_run_tiles(nt, segs);
             const int runs = segs * ((nt + T - 1) / T);
-#define LSH_DKV(NR, NC)                                                                                        \
-    hipLaunchKernelGGL((dkv_stream_kernel<D, NR, NC>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T, P.m,     \
-                       P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile, dkr_part,  \
-                       dv_part)
-#define LSH_DKV_NR(NC)              \
+#define LSH_DKV(NR, MODE, DUPB)                                                                                \
+    hipLaunchKernelGGL((dkv_stream_kernel<D, NR, MODE, DUPB>), dim3(runs), dim3(kKvThreads), 0, st, P.L, P.nh, T,  \
+                       P.m, P.scale, (const bf16 *)q, (const bf16 *)v, (const bf16 *)dout, srec, ktile, qtile,       \
+                       dkr_part, dv_part)
+#define LSH_DKV_NR(MODE, DUPB)      \
     if (P.nh <= 2)                  \
-        LSH_DKV(1, NC);             \
+        LSH_DKV(1, MODE, DUPB);     \
     else if (P.nh <= 4)             \
-        LSH_DKV(3, NC);             \
+        LSH_DKV(3, MODE, DUPB);     \
     else if (P.nh <= 8)             \
-        LSH_DKV(7, NC);             \
+        LSH_DKV(7, MODE, DUPB);     \
     else                            \
-        LSH_DKV(13, NC)
-            if (P.kind() == kBand) {
-                LSH_DKV_NR(kBand);
+        LSH_DKV(13, MODE, DUPB)
+            if (P.dup_bucket) {
+                if (P.kind() == kBand) {
+                    LSH_DKV_NR(kBand, true);
+                } else {
+                    LSH_DKV_NR(kRange, true);
+                }
+            } else if (P.kind() == kBand) {
+                LSH_DKV_NR(kBand, false);
             } else if (P.kind() == kRange) {
-                LSH_DKV_NR(kRange);
+                LSH_DKV_NR(kRange, false);
             } else {
-                LSH_DKV_NR(kRangePos);
+                LSH_DKV_NR(kRangePos, false);
             }
 #undef LSH_DKV_NR
 #undef LSH_DKV
@@ -1832,8 +1915,8 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
     ProfScope prof(LSH_KERNEL_BWD_REDUCE, st);
 #define LSH_REDUCE(NH)                                                                                            \
     hipLaunchKernelGGL((reduce_kernel<D, NH>), dim3((ntok + TPB - 1) / TPB), dim3(kThreads), 0, st, P.L, P.nh, ntok, \
-                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, wmeta, alone, dq_part, dkr_part, dv_part,   \
-                       (bf16 *)dq, (bf16 *)dv)
+                       (const bf16 *)q, rnorm, (const bf16 *)dout, meta, x.wmeta, x.alone, dq_part, dkr_part,       \
+                       dv_part, (bf16 *)dq, (bf16 *)dv)
     if (P.nh <= 2)
         LSH_REDUCE(2);
     else if (P.nh <= 4)
@@ -1847,14 +1930,14 @@ hipError_t bwd_go(const Dims &P, const void *q, const void *v, const void *dout,
 }
 
 hipError_t tiles_go(const Dims &P, const uint32_t *srec, const uint32_t *meta, const uint32_t *wmeta,
-                    const float *rnorm, const float *lse, const float *Dv, uint8_t *ktile, uint8_t *qtile,
-                    hipStream_t st)
+                    const uint32_t *bmeta, const float *rnorm, const float *lse, const float *Dv, uint8_t *ktile,
+                    uint8_t *qtile, hipStream_t st)
 {
     const int ntiles = P.BH() * P.nh * (P.L / kBlk);
     const int per_block = kThreads / kWave;
     ProfScope prof(LSH_KERNEL_TILES, st);
     hipLaunchKernelGGL(tile_prep_kernel, dim3((ntiles + per_block - 1) / per_block), dim3(kThreads), 0, st, P.L, P.nh,
-                       ntiles, P.scale * kLog2e, srec, meta, wmeta, rnorm, lse, Dv, ktile, qtile);
+                       ntiles, P.scale * kLog2e, srec, meta, wmeta, bmeta, rnorm, lse, Dv, ktile, qtile);
     return hipGetLastError();
 }
 
@@ -1867,7 +1950,7 @@ bool mfma_path_ok(const Dims &P, int dtype)
     // rounds; sets other than the causal band run on the stream kernels only
     // (chunk lengths that divide 128)
     return dtype == LSH_BF16 && (P.d == 64 || P.d == 128) && P.L % kRows == 0 && P.nh <= kMaxEarlier + 1 &&
-           kRows + 2 * P.m + kBlk <= kRecCache && (P.kind() == kBand || kRows % P.m == 0);
+           kRows + 2 * P.m + kBlk <= kRecCache && ((P.kind() == kBand && !P.dup_bucket) || kRows % P.m == 0);
 }
 
 size_t mfma_ktile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / kBlk) * ktile_stride(P.nh); }
@@ -1875,34 +1958,29 @@ size_t mfma_qtile_bytes(const Dims &P) { return (size_t)P.BH() * P.nh * (P.L / k
 size_t bwd_mfma_part_bytes(const Dims &P) { return 3 * (size_t)P.BH() * P.nh * P.L * P.d * sizeof(uint16_t); }
 
 hipError_t launch_attn_fwd_mfma(const Dims &P, const void *q, const void *v, const uint32_t *meta,
-                                const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, uint8_t *ktile,
+                                const uint32_t *srec, const Extra &x, const float *rnorm, uint8_t *ktile,
                                 void *o_rounds, float *lse_rounds, hipStream_t st)
 {
-    if (P.kind() == kBand)
-        wmeta = nullptr;
-    hipError_t e = tiles_go(P, srec, meta, wmeta, rnorm, nullptr, nullptr, ktile, nullptr, st);
+    hipError_t e = tiles_go(P, srec, meta, x.wmeta, x.bmeta, rnorm, nullptr, nullptr, ktile, nullptr, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)
-        return fwd_go<128>(P, q, v, meta, srec, wmeta, ktile, o_rounds, lse_rounds, st);
-    return fwd_go<64>(P, q, v, meta, srec, wmeta, ktile, o_rounds, lse_rounds, st);
+        return fwd_go<128>(P, q, v, meta, srec, x, ktile, o_rounds, lse_rounds, st);
+    return fwd_go<64>(P, q, v, meta, srec, x, ktile, o_rounds, lse_rounds, st);
 }
 
 hipError_t launch_attn_bwd_mfma(const Dims &P, const void *q, const void *v, const void *dout, const float *lse,
-                                const float *Dv, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
-                                const uint8_t *alone, const float *rnorm, uint8_t *ktile, bool make_ktile,
-                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t st)
+                                const float *Dv, const uint32_t *meta, const uint32_t *srec, const Extra &x,
+                                const float *rnorm, uint8_t *ktile, bool make_ktile, uint8_t *qtile, void *part,
+                                void *dq, void *dv, hipStream_t st)
 {
-    if (P.kind() == kBand)
-        wmeta = nullptr;
-    if (P.kind() != kRangePos)
-        alone = nullptr;
-    hipError_t e = tiles_go(P, srec, meta, wmeta, rnorm, lse, Dv, make_ktile ? ktile : nullptr, qtile, st);
+    hipError_t e =
+        tiles_go(P, srec, meta, x.wmeta, x.bmeta, rnorm, lse, Dv, make_ktile ? ktile : nullptr, qtile, st);
     if (e != hipSuccess)
         return e;
     if (P.d == 128)
-        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, wmeta, alone, rnorm, ktile, qtile, part, dq, dv, st);
-    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, wmeta, alone, rnorm, ktile, qtile, part, dq, dv, st);
+        return bwd_go<128>(P, q, v, dout, lse, Dv, meta, srec, x, rnorm, ktile, qtile, part, dq, dv, st);
+    return bwd_go<64>(P, q, v, dout, lse, Dv, meta, srec, x, rnorm, ktile, qtile, part, dq, dv, st);
 }
 
 }  // namespace lsh

@@ -79,10 +79,12 @@ __device__ __forceinline__ bool in_span(uint32_t wrec, uint32_t sj)
 // bucket condition, the chunk window filtered by position (kRangePos).
 enum SetKind { kBand = 0, kRange = 1, kRangePos = 2 };
 
+// dup_bucket: duplicates counted over bucket membership (LSH_FLAG_DUP_BY_BUCKET)
+// instead of the first-owner rule.
 struct Dims {
     int B, H, L, d, nh, nb, m;
     float scale;
-    bool causal, bucket_mask;
+    bool causal, bucket_mask, dup_bucket;
     int BH() const { return B * H; }
     int kind() const { return causal ? (bucket_mask ? kBand : kRangePos) : kRange; }
 };
@@ -90,7 +92,19 @@ struct Dims {
 inline Dims dims_of(const lsh_problem_t *p)
 {
     return Dims{p->batch, p->heads, p->seq_len, p->head_dim, p->n_hashes, p->n_buckets, p->chunk_len,
-                p->scale, p->causal != 0, (p->flags & LSH_FLAG_NO_BUCKET_MASK) == 0};
+                p->scale, p->causal != 0, (p->flags & LSH_FLAG_NO_BUCKET_MASK) == 0,
+                (p->flags & LSH_FLAG_DUP_BY_BUCKET) != 0};
+}
+
+// Number of rounds in which two rows share a bucket, given each one's
+// per-round bucket-run starts (the sorted index where its bucket begins).
+__device__ __forceinline__ int shared_buckets(const uint32_t *__restrict__ bi, const uint32_t *__restrict__ bj,
+                                              int nh)
+{
+    int n = 0;
+    for (int r = 0; r < nh; ++r)
+        n += bi[r] == bj[r];
+    return n;
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -112,23 +126,31 @@ hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, 
 hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv,
                        int32_t *win_lo, void *ws, hipStream_t);
 size_t sort_ws_bytes(const Dims &);
-// Packed records, inverse norms, the window records of kRange / kRangePos
-// problems (wmeta, null for kBand), the per-(token, round) lone flags of
-// kRangePos problems (alone, with cmin as scratch of L/m words per
-// (b, h, round); both null otherwise) and (with out, dout) D = dO . O; with
-// meta null only D is written (the records are already in place).
+// Window-related records beyond meta and srec, each null where the problem
+// has no use for it: wmeta (kRange / kRangePos window ends), alone and cmin
+// (kRangePos lone flags and their per-chunk scratch), bmeta (dup_bucket: the
+// start of each row's bucket run per round, [B*H*L][nh]).
+struct Extra {
+    uint32_t *wmeta;
+    uint8_t *alone;
+    uint32_t *cmin, *bmeta;
+};
+
+// Packed records, inverse norms, the extra records and (with out, dout)
+// D = dO . O; with meta null only D is written (the records are already in
+// place).
 hipError_t launch_prep(const Dims &, int dtype, const void *q, const int32_t *perm, const int32_t *inv,
-                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, uint32_t *wmeta, uint8_t *alone,
-                       uint32_t *cmin, float *rnorm, const void *out, const void *dout, float *D, hipStream_t);
+                       const int32_t *win_lo, uint32_t *meta, uint32_t *srec, const Extra &x, float *rnorm,
+                       const void *out, const void *dout, float *D, hipStream_t);
 hipError_t launch_attn_fwd(const Dims &, int dtype, const void *q, const void *v, const uint32_t *meta,
-                           const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, void *o_rounds,
+                           const uint32_t *srec, const Extra &x, const float *rnorm, void *o_rounds,
                            float *lse_rounds, hipStream_t);
 hipError_t launch_combine(const Dims &, int dtype, const void *q, const void *v, const void *o_rounds,
                           const float *lse_rounds, void *out, float *lse, hipStream_t);
 hipError_t launch_attn_bwd(const Dims &, int dtype, const void *q, const void *v, const void *dout,
                            const float *lse, const float *D, const uint32_t *meta, const uint32_t *srec,
-                           const uint32_t *wmeta, const uint8_t *alone, const float *rnorm, float *dq_part,
-                           float *dk_part, float *dv_part, void *dq, void *dv, hipStream_t);
+                           const Extra &x, const float *rnorm, float *dq_part, float *dk_part, float *dv_part,
+                           void *dq, void *dv, hipStream_t);
 
 }  // namespace lsh
 
@@ -319,11 +341,11 @@ size_t mfma_qtile_bytes(const Dims &);
 // normalisation) and dv, [B*H*L][nh][3][d] (token-major), in one buffer of this size
 size_t bwd_mfma_part_bytes(const Dims &);
 hipError_t launch_attn_fwd_mfma(const Dims &, const void *q, const void *v, const uint32_t *meta,
-                                const uint32_t *srec, const uint32_t *wmeta, const float *rnorm, uint8_t *ktile,
+                                const uint32_t *srec, const Extra &x, const float *rnorm, uint8_t *ktile,
                                 void *o_rounds, float *lse_rounds, hipStream_t);
 hipError_t launch_attn_bwd_mfma(const Dims &, const void *q, const void *v, const void *dout, const float *lse,
-                                const float *D, const uint32_t *meta, const uint32_t *srec, const uint32_t *wmeta,
-                                const uint8_t *alone, const float *rnorm, uint8_t *ktile, bool make_ktile,
-                                uint8_t *qtile, void *part, void *dq, void *dv, hipStream_t);
+                                const float *D, const uint32_t *meta, const uint32_t *srec, const Extra &x,
+                                const float *rnorm, uint8_t *ktile, bool make_ktile, uint8_t *qtile, void *part,
+                                void *dq, void *dv, hipStream_t);
 
 }  // namespace lsh

@@ -46,7 +46,8 @@ int validate(const lsh_problem_t *p)
     if (p->batch < 0 || p->heads < 0 || p->seq_len < 0 || p->head_dim < 1 || p->n_hashes < 1 ||
         p->n_buckets < 2 || (p->n_buckets & 1) || p->chunk_len < 1 || p->seq_len % p->chunk_len ||
         !isfinite(p->scale) || (p->dtype != LSH_F32 && p->dtype != LSH_BF16) || (p->causal != 0 && p->causal != 1) ||
-        (p->flags & ~(int32_t)LSH_FLAG_NO_BUCKET_MASK))
+        (p->flags & ~(int32_t)(LSH_FLAG_NO_BUCKET_MASK | LSH_FLAG_DUP_BY_BUCKET)) ||
+        ((p->flags & LSH_FLAG_NO_BUCKET_MASK) && (p->flags & LSH_FLAG_DUP_BY_BUCKET)))
         return LSH_ERR_INVALID;
     if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128)
         return LSH_ERR_UNSUPPORTED;
@@ -65,20 +66,18 @@ bool empty(const lsh_problem_t *p) { return p->batch == 0 || p->heads == 0 || p-
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
-// Window records (wmeta) exist for kRange / kRangePos problems, lone flags
-// (alone) and per-chunk minimum positions (cmin, scratch) for kRangePos
-// only; they are null otherwise.
+// The extra records (see Extra) exist only where the problem uses them.
 struct FwdWs {
-    uint32_t *meta, *srec, *wmeta, *cmin;
-    uint8_t *alone;
+    uint32_t *meta, *srec;
+    Extra x;
     float *rnorm;
     uint8_t *ktile;
     size_t bytes;
 };
 
 struct BwdWs {
-    uint32_t *meta, *srec, *wmeta, *cmin;
-    uint8_t *alone;
+    uint32_t *meta, *srec;
+    Extra x;
     float *rnorm, *D, *dq_part, *dk_part, *dv_part;
     uint8_t *ktile, *qtile;
     size_t bytes;
@@ -96,11 +95,14 @@ size_t fwd_part(const Dims &P, uintptr_t b, W &w)
     w.rnorm = (float *)(b + o); o += align_up(tok * 4, 256);
     w.ktile = (uint8_t *)(b + o); o += align_up(mfma_ktile_bytes(P), 256);
     if (P.kind() != kBand) {
-        w.wmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+        w.x.wmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     }
     if (P.kind() == kRangePos) {
-        w.alone = (uint8_t *)(b + o); o += align_up(rnd, 256);
-        w.cmin = (uint32_t *)(b + o); o += align_up((size_t)P.BH() * P.nh * (P.L / P.m) * 4, 256);
+        w.x.alone = (uint8_t *)(b + o); o += align_up(rnd, 256);
+        w.x.cmin = (uint32_t *)(b + o); o += align_up((size_t)P.BH() * P.nh * (P.L / P.m) * 4, 256);
+    }
+    if (P.dup_bucket) {
+        w.x.bmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
     }
     return o;
 }
@@ -185,15 +187,15 @@ int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void
         return LSH_ERR_INVALID;
     const bool derive = perm != nullptr;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, derive ? w.meta : nullptr, w.srec, w.wmeta,
-                               w.alone, w.cmin, w.rnorm, out, dout, w.D, s);
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, derive ? w.meta : nullptr, w.srec, w.x,
+                               w.rnorm, out, dout, w.D, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype)) {
-            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.alone, w.rnorm, w.ktile,
-                                     derive, w.qtile, w.dq_part, dq, dv, s);
+            e = launch_attn_bwd_mfma(P, q, v, dout, lse, w.D, w.meta, w.srec, w.x, w.rnorm, w.ktile, derive, w.qtile,
+                                     w.dq_part, dq, dv, s);
         } else {
-            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.wmeta, w.alone, w.rnorm,
-                                w.dq_part, w.dk_part, w.dv_part, dq, dv, s);
+            e = launch_attn_bwd(P, prob->dtype, q, v, dout, lse, w.D, w.meta, w.srec, w.x, w.rnorm, w.dq_part,
+                                w.dk_part, w.dv_part, dq, dv, s);
         }
     }
     return hip_status(e);
@@ -214,7 +216,7 @@ const char *lsh_status_string(int status)
     }
 }
 
-int lsh_version(void) { return 400; }
+int lsh_version(void) { return 500; }
 
 const char *lsh_kernel_name(int kernel)
 {
@@ -285,13 +287,13 @@ int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const 
     if (ws_bytes < w.bytes)
         return LSH_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.wmeta, w.alone, w.cmin,
-                               w.rnorm, nullptr, nullptr, nullptr, s);
+    hipError_t e = launch_prep(P, prob->dtype, q, perm, inv, win_lo, w.meta, w.srec, w.x, w.rnorm, nullptr, nullptr,
+                               nullptr, s);
     if (e == hipSuccess) {
         if (mfma_path_ok(P, prob->dtype))
-            e = launch_attn_fwd_mfma(P, q, v, w.meta, w.srec, w.wmeta, w.rnorm, w.ktile, o_rounds, lse_rounds, s);
+            e = launch_attn_fwd_mfma(P, q, v, w.meta, w.srec, w.x, w.rnorm, w.ktile, o_rounds, lse_rounds, s);
         else
-            e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.wmeta, w.rnorm, o_rounds, lse_rounds, s);
+            e = launch_attn_fwd(P, prob->dtype, q, v, w.meta, w.srec, w.x, w.rnorm, o_rounds, lse_rounds, s);
     }
     return hip_status(e);
 }

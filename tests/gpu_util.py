@@ -33,7 +33,8 @@ def to_f64(t):
 def run_gpu(x, backward=True, rounds=False):
     cfg = x["cfg"]
     prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=cfg.causal, bucket_mask=cfg.bucket_mask)
+                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=cfg.causal, bucket_mask=cfg.bucket_mask,
+                       dup_by_bucket=cfg.dup_by_bucket)
     q = to_device(x["q"], cfg.dtype)
     v = to_device(x["v"], cfg.dtype)
     rot = to_device(x["rot"], cfg.dtype)

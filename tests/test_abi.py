@@ -97,10 +97,11 @@ def test_causal_flag_values():
 def test_flags_values():
     L = _lib.lib()
     dummy = ctypes.c_void_p(256)
-    p = _prob()
-    p.flags = 2                      # unknown bit
-    assert L.lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == 1
-    assert L.lsh_workspace_bytes(ctypes.byref(p), 1) == 0
+    for bad in (4, 3, -1):           # an unknown bit; both set flags together
+        p = _prob()
+        p.flags = bad
+        assert L.lsh_hash(ctypes.byref(p), dummy, dummy, dummy, None) == 1
+        assert L.lsh_workspace_bytes(ctypes.byref(p), 1) == 0
     c = _prob()
     rnd = c.batch * c.heads * c.seq_len * c.n_hashes
     a256 = lambda x: (x + 255) // 256 * 256
@@ -109,10 +110,13 @@ def test_flags_values():
     nbc = _prob(bucket_mask=False)
     extra = a256(rnd * 4) + a256(rnd) + a256(rnd // c.chunk_len * 4)
     nbn = _prob(bucket_mask=False, causal=False)
+    # duplicates counted over buckets: the bucket-run starts per token-round
+    dup = _prob(dup_by_bucket=True)
     for kind in (1, 2, 3):
         base = L.lsh_workspace_bytes(ctypes.byref(c), kind)
         assert L.lsh_workspace_bytes(ctypes.byref(nbc), kind) == base + extra
         assert L.lsh_workspace_bytes(ctypes.byref(nbn), kind) == base + a256(rnd * 4)
+        assert L.lsh_workspace_bytes(ctypes.byref(dup), kind) == base + a256(rnd * 4)
 
 
 def test_null_and_misaligned_pointers_rejected():

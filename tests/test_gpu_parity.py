@@ -349,6 +349,81 @@ def test_no_bucket_mask_backward_entry_points_agree(idx):
         assert torch.equal(bits(a), bits(b))
 
 
+# ----------------------------------------------------------------------------- duplicates by bucket
+# LSH_FLAG_DUP_BY_BUCKET: a member attended in k rounds weighs k / N, N =
+# rounds sharing the query's bucket.  Few buckets and short chunks (and the
+# clustered inputs) cut buckets by the window, where this differs from the
+# default count.
+
+# name, B, H, L, d, nb, nh, m, dtype, clustered, causal
+DB_SMALL = [
+    ("db-f32", 1, 2, 1024, 64, 8, 3, 16, "f32", False, True),
+    ("db-f32-noncausal", 1, 1, 512, 32, 4, 2, 8, "f32", False, False),
+    ("db-tiny-L", 1, 1, 8, 32, 4, 2, 2, "f32", False, True),
+    ("db-bf16", 2, 2, 1024, 64, 8, 3, 16, "bf16", False, True),
+    ("db-bf16-d128", 1, 2, 2048, 128, 16, 2, 32, "bf16", False, True),
+    ("db-bf16-d128-nh4", 1, 1, 2048, 128, 16, 4, 32, "bf16", False, True),
+    ("db-bf16-nh8", 1, 1, 1024, 64, 16, 8, 32, "bf16", False, True),
+    ("db-bf16-nh14-d128", 1, 1, 1024, 128, 16, 14, 64, "bf16", False, True),
+    ("db-bf16-noncausal", 1, 2, 2048, 64, 16, 3, 32, "bf16", False, False),
+    ("db-bf16-noncausal-d128-nh12", 1, 1, 1024, 128, 16, 12, 64, "bf16", False, False),
+    ("db-bf16-clustered", 1, 2, 2048, 64, 64, 4, 64, "bf16", True, True),
+    ("db-bf16-m96", 1, 2, 1536, 64, 8, 3, 96, "bf16", False, True),
+    ("db-bf16-one-round", 1, 2, 1024, 64, 8, 1, 32, "bf16", False, True),
+]
+
+
+def _db_cfg(case):
+    name, B, H, L, d, nb, nh, m, dt, cl, causal = case
+    return gen.Config(name, B, H, L, d, nb, nh, m, dt, cl, True, 700 + DB_SMALL.index(case), n_clusters=16,
+                      causal=causal, dup_by_bucket=True)
+
+
+@pytest.mark.parametrize("case", DB_SMALL, ids=[c[0] for c in DB_SMALL])
+def test_dup_by_bucket_small_shapes_match_oracle(case):
+    cfg = _db_cfg(case)
+    gu.say(f"[gpu] dup-by-bucket small case {cfg}")
+    x = gen.generate(cfg)
+    res = gu.run_gpu(x)
+    gu.compare_slices(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
+
+
+def test_dup_by_bucket_stress_workload_matches_oracle():
+    # the clustered 64K workload: buckets of ~256 rows overflow the window
+    x = dict(_full("stress"))
+    x["cfg"] = x["cfg"].with_(dup_by_bucket=True)
+    gu.say("[gpu] dup-by-bucket full-size stress: running the library")
+    res = gu.run_gpu(x)
+    gu.say("[gpu] dup-by-bucket full-size stress: oracle on slice (1, 2)")
+    gu.compare_slices(x, res, [(1, 2)])
+
+
+@pytest.mark.parametrize("idx", [0, 3, 5, 9, 10])
+def test_dup_by_bucket_backward_entry_points_agree(idx):
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    cfg = _db_cfg(DB_SMALL[idx])
+    gu.say(f"[gpu] dup-by-bucket backward entry points {cfg}")
+    x = gen.generate(cfg)
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=cfg.causal, dup_by_bucket=True)
+    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
+    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
+    mod = lsh.LshAttention(prob)
+    mod.forward(q, v, rot)
+    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
+    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
+    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
+    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
+    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
+    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
+    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for a, b in ((dq, dq_s), (dv, dv_s), (dq2, dq_s), (dv2, dv_s)):
+        assert torch.equal(bits(a), bits(b))
+
+
 def test_empty_problem_is_a_no_op():
     import lsh_sparse_attention_amd as lsh
     gu.say("[gpu] empty problem L=0")
