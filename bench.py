@@ -149,14 +149,16 @@ def rehash_variant(prob, mod, q, v, rot, do, steps, cfg) -> dict:
             "kept_between_passes": "out, lse (no buckets, sorted order or records)"}
 
 
-def set_variant(q, v, rot, do, steps, cfg, hip, causal, bucket_mask) -> dict:
+def set_variant(q, v, rot, do, steps, cfg, hip, causal, bucket_mask, dup_by_bucket=False) -> dict:
     """The same training step (forward and saved-records backward) on the same inputs with other
-    attended sets: non-causal (encoder) sets, or sets without the same-bucket condition."""
+    attended sets: non-causal (encoder) sets, sets without the same-bucket condition, or the
+    duplicate count over bucket membership."""
     import torch
     import lsh_sparse_attention_amd as lsh
     from lsh_sparse_attention_amd import _lib as L_
     prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=causal, bucket_mask=bucket_mask)
+                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=causal, bucket_mask=bucket_mask,
+                       dup_by_bucket=dup_by_bucket)
     mod = lsh.LshAttention(prob)
 
     def step():
@@ -184,7 +186,7 @@ def set_variant(q, v, rot, do, steps, cfg, hip, causal, bucket_mask) -> dict:
     ms = (time.perf_counter() - t0) * 1e3 / steps
     del mod
     return {"ms_per_step": ms, "value": cfg.batch * cfg.seq_len / (ms * 1e-3), "unit": "tokens/s",
-            "causal": causal, "bucket_mask": bucket_mask, "kernels_us": per_kernel}
+            "causal": causal, "bucket_mask": bucket_mask, "dup_by_bucket": dup_by_bucket, "kernels_us": per_kernel}
 
 
 def source_sha(kernel: str) -> str:
@@ -409,6 +411,7 @@ def main() -> int:
     if not args.no_variants:
         result["variants"]["non_causal"] = set_variant(q, v, rot, do, args.steps, cfg, hip, False, True)
         result["variants"]["no_bucket_mask"] = set_variant(q, v, rot, do, args.steps, cfg, hip, True, False)
+        result["variants"]["dup_by_bucket"] = set_variant(q, v, rot, do, args.steps, cfg, hip, True, True, True)
     torch.cuda.empty_cache()
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
