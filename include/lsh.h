@@ -251,6 +251,52 @@ int lsh_attn_bwd_saved(const lsh_problem_t *prob, const void *q, const void *v, 
                        size_t ws_bytes, void *stream);
 
 /*
+ * Chunked feed-forward layer ("Reformer" §3, Reversible Transformer: the
+ * feed-forward computation is independent across positions, so it is split
+ * into c chunks of positions, forward, recomputation and backward alike).
+ * The layer is the standard Transformer one, y = relu(x W1 + b1) W2 + b2,
+ * row by row; only one chunk's hidden activations (ceil(rows / c) x d_ff)
+ * are held at a time, in the workspace.  Hidden activations and their
+ * gradient are kept in bf16; products accumulate in fp32.
+ *   rows: n >= 0 positions (B * L); rows == 0 is a no-op returning LSH_OK.
+ *   d_model, d_ff: multiples of 8, at least 8.
+ *   chunks: c >= 1.
+ *   dtype: LSH_BF16 (x, w1, w2, y, dy, dx); LSH_F32 returns
+ *       LSH_ERR_UNSUPPORTED.
+ */
+typedef struct {
+    int32_t rows, d_model, d_ff, chunks;
+    int32_t dtype; /* lsh_dtype_t */
+} lsh_ff_t;
+
+/* Workspace bytes of lsh_ff_fwd (backward = 0) or lsh_ff_bwd (backward = 1);
+ * 0 if the description is invalid or empty.  Alignment: 256 bytes. */
+size_t lsh_ff_workspace_bytes(const lsh_ff_t *ff, int backward);
+
+/*
+ * lsh_ff_fwd -- y = relu(x W1 + b1) W2 + b2, chunk by chunk.
+ *   x  [n][d_model] bf16;  w1 [d_model][d_ff] bf16;  b1 [d_ff] fp32;
+ *   w2 [d_ff][d_model] bf16;  b2 [d_model] fp32;  y [n][d_model] bf16 out.
+ *   Device pointers, x, w1, w2, y 16-byte aligned; ws as returned by
+ *   lsh_ff_workspace_bytes(ff, 0).
+ */
+int lsh_ff_fwd(const lsh_ff_t *ff, const void *x, const void *w1, const float *b1, const void *w2, const float *b2,
+               void *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * lsh_ff_bwd -- gradients of sum(y * dy) for lsh_ff_fwd, chunk by chunk: the
+ * hidden activations of a chunk are recomputed from x (nothing is kept from
+ * the forward), then dH = (dy W2^T) * relu'(x W1 + b1), dx = dH W1^T, and the
+ * weight and bias gradients are summed over the chunks in fp32.
+ *   dy [n][d_model] bf16;  dx [n][d_model] bf16 out;
+ *   dw1 [d_model][d_ff], db1 [d_ff], dw2 [d_ff][d_model], db2 [d_model]
+ *   fp32 out (overwritten, not added to).
+ *   ws as returned by lsh_ff_workspace_bytes(ff, 1).
+ */
+int lsh_ff_bwd(const lsh_ff_t *ff, const void *x, const void *w1, const float *b1, const void *w2, const void *dy,
+               void *dx, float *dw1, float *db1, float *dw2, float *db2, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Instrumentation (not needed to compute anything).
  *
  * Kernels of the library, for lsh_profile_kernel and lsh_kernel_name.

@@ -18,11 +18,12 @@ import math
 
 import torch
 
-from ._lib import (LSH_BF16, LSH_F32, LSH_FLAG_DUP_BY_BUCKET, LSH_FLAG_NO_BUCKET_MASK, LSH_WS_BWD, LSH_WS_FWD,
+from ._lib import (FF, LSH_BF16, LSH_F32, LSH_FLAG_DUP_BY_BUCKET, LSH_FLAG_NO_BUCKET_MASK, LSH_WS_BWD, LSH_WS_FWD,
                    LSH_WS_REHASH, LSH_WS_SORT, LSH_WS_TRAIN, LshError, Problem, check, lib)
 
 __all__ = ["Problem", "LshError", "problem", "workspace_bytes", "lsh_hash", "lsh_sort", "lsh_attn_fwd",
-           "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash", "LshAttention"]
+           "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash", "LshAttention", "FF",
+           "ff_problem", "ff_workspace_bytes", "lsh_ff_fwd", "lsh_ff_bwd"]
 
 _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
 
@@ -213,3 +214,43 @@ class LshAttention:
         p = self.prob
         lsh_attn_bwd_saved(p, q, v, self.out, dout, self.lse, self.dq, self.dv, self.ws_fwd, stream)
         return self.dq, self.dv
+
+
+# ----------------------------------------------------------------------------- chunked feed-forward
+
+def ff_problem(rows, d_model, d_ff, chunks=1) -> FF:
+    """lsh_ff_t for bf16 activations."""
+    return FF(rows, d_model, d_ff, chunks, LSH_BF16)
+
+
+def ff_workspace_bytes(ff: FF, backward: bool) -> int:
+    return lib().lsh_ff_workspace_bytes(ctypes.byref(ff), 1 if backward else 0)
+
+
+def _ff_ws(ws, ff, backward):
+    need = ff_workspace_bytes(ff, backward)
+    if ws is None:
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+    return ws, need
+
+
+def lsh_ff_fwd(ff, x, w1, b1, w2, b2, y, ws=None, stream=None):
+    """y = relu(x w1 + b1) w2 + b2 in ff.chunks chunks of rows (lsh_ff_fwd)."""
+    ws, need = _ff_ws(ws, ff, False)
+    bf, f32 = torch.bfloat16, torch.float32
+    check("lsh_ff_fwd", lib().lsh_ff_fwd(ctypes.byref(ff), _ptr(x, "x", bf), _ptr(w1, "w1", bf), _ptr(b1, "b1", f32),
+                                         _ptr(w2, "w2", bf), _ptr(b2, "b2", f32), _ptr(y, "y", bf),
+                                         _ptr(ws, "ws"), ctypes.c_size_t(ws.numel()), _stream(stream)))
+    return y
+
+
+def lsh_ff_bwd(ff, x, w1, b1, w2, dy, dx, dw1, db1, dw2, db2, ws=None, stream=None):
+    """Gradients of sum(y * dy) (lsh_ff_bwd); the hidden activations are recomputed per chunk."""
+    ws, need = _ff_ws(ws, ff, True)
+    bf, f32 = torch.bfloat16, torch.float32
+    check("lsh_ff_bwd", lib().lsh_ff_bwd(ctypes.byref(ff), _ptr(x, "x", bf), _ptr(w1, "w1", bf), _ptr(b1, "b1", f32),
+                                         _ptr(w2, "w2", bf), _ptr(dy, "dy", bf), _ptr(dx, "dx", bf),
+                                         _ptr(dw1, "dw1", f32), _ptr(db1, "db1", f32), _ptr(dw2, "dw2", f32),
+                                         _ptr(db2, "db2", f32), _ptr(ws, "ws"), ctypes.c_size_t(ws.numel()),
+                                         _stream(stream)))
+    return dx, dw1, db1, dw2, db2

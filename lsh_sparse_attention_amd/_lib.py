@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "liblsh.so")
 # Exported symbols, in header order.
 SYMBOLS = ("lsh_status_string", "lsh_version", "lsh_workspace_bytes", "lsh_hash", "lsh_sort",
            "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash",
-           "lsh_kernel_name", "lsh_profile_kernel")
+           "lsh_kernel_name", "lsh_profile_kernel", "lsh_ff_workspace_bytes", "lsh_ff_fwd", "lsh_ff_bwd")
 
 KERNELS = ("hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq",
            "bwd_dkv", "bwd_reduce", "tiles")
@@ -30,6 +30,12 @@ class Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_hashes", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
                 ("chunk_len", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class FF(ctypes.Structure):
+    """Mirror of lsh_ff_t."""
+    _fields_ = [("rows", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("chunks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class LshError(RuntimeError):
@@ -62,8 +68,12 @@ def lib() -> ctypes.CDLL:
         L.lsh_attn_bwd_rehash.argtypes = [pp, vp, vp, vp, vp, vp, fp, vp, vp, vp, sz, vp]
         L.lsh_kernel_name.argtypes, L.lsh_kernel_name.restype = [ctypes.c_int], ctypes.c_char_p
         L.lsh_profile_kernel.argtypes = [ctypes.c_int, vp, vp]
+        fp_ = ctypes.POINTER(FF)
+        L.lsh_ff_workspace_bytes.argtypes, L.lsh_ff_workspace_bytes.restype = [fp_, ctypes.c_int], sz
+        L.lsh_ff_fwd.argtypes = [fp_, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lsh_ff_bwd.argtypes = [fp_, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("lsh_hash", "lsh_sort", "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved",
-                     "lsh_attn_bwd_rehash", "lsh_profile_kernel"):
+                     "lsh_attn_bwd_rehash", "lsh_profile_kernel", "lsh_ff_fwd", "lsh_ff_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

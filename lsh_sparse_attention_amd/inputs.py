@@ -221,3 +221,41 @@ def small_config(name="small", batch=1, heads=1, seq_len=256, head_dim=64, n_buc
     """A parity-test shape; any field can be overridden."""
     return Config(name, batch, heads, seq_len, head_dim, n_buckets, n_hashes, chunk_len, dtype,
                   clustered, True, seed, **kw)
+
+
+# ----------------------------------------------------------------------------- feed-forward layer
+# The ablation shape of the Reformer paper (§5 Experiments): d_model = 1024,
+# d_ff = 4096; rows are the B * L positions of a batch.
+FF_SHAPE = {"d_model": 1024, "d_ff": 4096}
+
+
+def generate_ff(n: int, d_model: int, d_ff: int, seed: int, grid: bool = True) -> dict:
+    """Seeded inputs of the feed-forward layer: x, w1, w2, dy as bf16 bit
+    patterns (uint16), b1, b2 as float32.
+
+    With ``grid`` every value lies on a coarse power-of-two grid (x, dy in
+    multiples of 1/4 up to 1, weights in multiples of 1/64 up to 1/8, biases
+    in multiples of 1/256), so every pre-activation x W1 + b1 and every
+    dy W2^T is a sum of exactly representable terms whose partial sums stay
+    exact in fp32 (at most 2^15 distinct steps): the ReLU decisions of an fp32
+    kernel and of an fp64 oracle then agree exactly (the role the argmax
+    margin rule plays for the hash).  Without ``grid`` (timing only) the
+    values are Gaussian, scaled as for a trained layer.
+    Draw order: x, w1, b1, w2, b2, dy.
+    """
+    rng = np.random.default_rng(seed)
+    if grid:
+        def g(shape, num, den):
+            return rng.integers(-num, num + 1, size=shape).astype(np.float64) / den
+        x, w1, b1 = g((n, d_model), 4, 4), g((d_model, d_ff), 8, 64), g(d_ff, 64, 256)
+        w2, b2, dy = g((d_ff, d_model), 8, 64), g(d_model, 64, 256), g((n, d_model), 4, 4)
+    else:
+        x = rng.standard_normal((n, d_model))
+        w1 = rng.standard_normal((d_model, d_ff)) / np.sqrt(d_model)
+        b1 = rng.standard_normal(d_ff) * 0.1
+        w2 = rng.standard_normal((d_ff, d_model)) / np.sqrt(d_ff)
+        b2 = rng.standard_normal(d_model) * 0.1
+        dy = rng.standard_normal((n, d_model))
+    bits = lambda a: f32_to_bf16_bits(f64_to_f32(a))
+    return {"x": bits(x), "w1": bits(w1), "b1": f64_to_f32(b1), "w2": bits(w2), "b2": f64_to_f32(b2),
+            "dy": bits(dy), "n": n, "d_model": d_model, "d_ff": d_ff, "grid": grid}

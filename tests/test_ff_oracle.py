@@ -60,3 +60,28 @@ def test_ff_closed_forms():
     g = ffo.backward(x, -w1, -b1, w2, b2, rng.standard_normal((n, dm)))
     for name in ("dx", "dw1", "db1", "dw2"):
         assert not np.any(g[name]), name
+
+
+def test_ff_row_and_column_restrictions_agree_with_full_backward():
+    x, w1, b1, w2, b2, dy = _problem(5, 40, 16, 24)
+    g = ffo.backward(x, w1, b1, w2, b2, dy)
+    rows, cols = [0, 7, 39], [1, 5, 23]
+    np.testing.assert_allclose(ffo.dx_rows(x, w1, b1, w2, dy, rows), g["dx"][rows], rtol=1e-13, atol=1e-13)
+    c = ffo.weight_grad_columns(x, w1, b1, w2, dy, cols)
+    np.testing.assert_allclose(c["dw1"], g["dw1"][:, cols], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(c["db1"], g["db1"][cols], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(c["dw2"], g["dw2"][cols], rtol=1e-13, atol=1e-13)
+
+
+def test_ff_abs_sums_bound_the_terms():
+    # the absolute-sum companions dominate the outputs and restrict like them
+    x, w1, b1, w2, b2, dy = _problem(6, 30, 12, 20)
+    g = ffo.backward(x, w1, b1, w2, b2, dy)
+    s = ffo.abs_sums(x, w1, b1, w2, dy)
+    assert np.all(s["y"] + np.abs(b2) >= np.abs(ffo.forward(x, w1, b1, w2, b2)) - 1e-12)
+    for k in ("dx", "dw1", "db1", "dw2", "db2"):
+        assert np.all(s[k] >= np.abs(g[k]) - 1e-12), k
+    r = ffo.abs_sums(x, w1, b1, w2, dy, rows=[2, 5], cols=[3, 19])
+    np.testing.assert_allclose(r["dx"], s["dx"][[2, 5]], rtol=1e-13)
+    np.testing.assert_allclose(r["dw1"], s["dw1"][:, [3, 19]], rtol=1e-13)
+    np.testing.assert_allclose(r["dw2"], s["dw2"][[3, 19]], rtol=1e-13)
