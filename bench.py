@@ -189,6 +189,46 @@ def set_variant(q, v, rot, do, steps, cfg, hip, causal, bucket_mask, dup_by_buck
             "causal": causal, "bucket_mask": bucket_mask, "dup_by_bucket": dup_by_bucket, "kernels_us": per_kernel}
 
 
+def ff_variant(steps, rows) -> dict:
+    """The chunked feed-forward layer of the Reformer block (the paper's ablation layer, d_model
+    1024, d_ff 4096) over the same number of positions, in 8 chunks: forward plus backward (which
+    recomputes the hidden activations), as one step; Gaussian inputs."""
+    import numpy as np
+    import torch
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import inputs as gen
+    dm, dff, chunks = gen.FF_SHAPE["d_model"], gen.FF_SHAPE["d_ff"], 8
+    d = gen.generate_ff(rows, dm, dff, seed=7, grid=False)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    x, w1, w2, dy = bf(d["x"]), bf(d["w1"]), bf(d["w2"]), bf(d["dy"])
+    b1, b2 = torch.from_numpy(d["b1"]).cuda(), torch.from_numpy(d["b2"]).cuda()
+    ff = lsh.ff_problem(rows, dm, dff, chunks)
+    wsf = torch.empty(lsh.ff_workspace_bytes(ff, False), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(lsh.ff_workspace_bytes(ff, True), dtype=torch.uint8, device="cuda")
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dw1 = torch.empty((dm, dff), dtype=torch.float32, device="cuda")
+    dw2 = torch.empty((dff, dm), dtype=torch.float32, device="cuda")
+    db1 = torch.empty(dff, dtype=torch.float32, device="cuda")
+    db2 = torch.empty(dm, dtype=torch.float32, device="cuda")
+
+    def step():
+        lsh.lsh_ff_fwd(ff, x, w1, b1, w2, b2, y, wsf)
+        lsh.lsh_ff_bwd(ff, x, w1, b1, w2, dy, dx, dw1, db1, dw2, db2, wsb)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 14.0 * rows * dm * dff     # forward 2 products, backward 5 (one recomputes h)
+    return {"ms_per_step": ms, "rows": rows, "d_model": dm, "d_ff": dff, "chunks": chunks,
+            "tflops": flops / (ms * 1e-3) / 1e12, "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"],
+            "value": rows / (ms * 1e-3), "unit": "tokens/s"}
+
+
 def source_sha(kernel: str) -> str:
     """Digest of the sources a kernel is compiled from (its file and the shared header)."""
     h = hashlib.sha256()
@@ -412,6 +452,8 @@ def main() -> int:
         result["variants"]["non_causal"] = set_variant(q, v, rot, do, args.steps, cfg, hip, False, True)
         result["variants"]["no_bucket_mask"] = set_variant(q, v, rot, do, args.steps, cfg, hip, True, False)
         result["variants"]["dup_by_bucket"] = set_variant(q, v, rot, do, args.steps, cfg, hip, True, True, True)
+        torch.cuda.empty_cache()
+        result["variants"]["chunked_ff"] = ff_variant(args.steps, cfg.batch * cfg.seq_len)
     torch.cuda.empty_cache()
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
