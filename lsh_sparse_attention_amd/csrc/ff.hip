@@ -154,7 +154,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(int M, int N, int
 // operand is read transposed: lane (column c, half h) gets the 8 k-values
 // 16 j + 4 h + {0..3} and 16 j + 8 + 4 h + {0..3} of its column (the same k
 // order for both operands, so their products pair up).
-constexpr int kTK = 32, kTPitch = 128 + 8;
+// LDS pitch 144 elements (288 bytes, 72 banks): the 4 rows a group of 16
+// lanes reads transposed start 8 banks apart and do not collide
+constexpr int kTK = 32, kTPitch = 128 + 16;
 __global__ __launch_bounds__(kGemmThreads) void gemm_tn_kernel(int M, int N, int K, int ksplit,
                                                                const bf16 *__restrict__ A, int lda,
                                                                const bf16 *__restrict__ B, int ldb,
