@@ -336,6 +336,9 @@ def main() -> int:
                          "step's launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 1 GiB (reference point for HBM byte counters)")
+    ap.add_argument("--ff-only", action="store_true",
+                    help="instead of the bench line: only the chunked feed-forward step (variants.chunked_ff) "
+                         "over the workload's B * L rows")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -346,6 +349,11 @@ def main() -> int:
     if args.sweep:
         return sweep(args.sweep, args.steps, args.warmup)
     import torch
+    if args.ff_only:
+        from lsh_sparse_attention_amd import inputs as gen_
+        c = gen_.CONFIGS[args.config]
+        print(json.dumps({"chunked_ff": ff_variant(args.steps, c.batch * c.seq_len)}), flush=True)
+        return 0
     if args.copy_calibration:
         n = 1 << 28                                   # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
         src = torch.ones(n, dtype=torch.float32, device="cuda")
