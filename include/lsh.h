@@ -77,7 +77,8 @@ typedef enum {
  *       B >= 0, H >= 0, 0 <= L <= 65536.  A problem with B, H or L equal to 0
  *       is empty: every call on it returns LSH_OK at once, without reading
  *       its pointers or launching anything.
- *   n_hashes: nh >= 1 hash rounds (<= 16).
+ *   n_hashes: nh >= 1 hash rounds (<= 16); B * H * nh <= 65535 and
+ *       B * H * nh * L < 2^31 (else LSH_ERR_UNSUPPORTED).
  *   n_buckets: nb, even, 2 <= nb <= 4096; nb = 2 * columns of the rotation.
  *   chunk_len: m, 1 <= m, L % m == 0 (m == L gives one chunk).
  *   causal: 1 = causal sets ("Reformer" §2: a query attends to no position

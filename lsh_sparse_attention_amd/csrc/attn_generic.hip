@@ -156,26 +156,59 @@ __global__ __launch_bounds__(kThreads) void window_kernel(int L, int nh, int m, 
 // exactly when its window length w is 0 (its window start is then itself:
 // the bucket begins there; a row inside a run has a window start before
 // it), so the run start of sorted row s is the last s' <= s with w(s') = 0,
-// a prefix maximum.  One workgroup per (b, h, round); each thread takes a
-// contiguous stretch of rows.  Writes bmeta[tok nh + r].
+// a prefix maximum.  Two passes over tiles of 1024 sorted rows (one thread a
+// row): the last run start of every tile (tmax), then each tile's prefix
+// maximum seeded with the maximum of the tiles before it.  Writes
+// bmeta[tok nh + r].
 constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ int block_max(int x, int *red)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x = max(x, __shfl_xor(x, o, kWave));
+    if (lane == 0)
+        red[wave] = x;
+    __syncthreads();
+    x = lane < kScanThreads / kWave ? red[lane] : -1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x = max(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void run_tile_kernel(int L, const uint32_t *__restrict__ srec,
+                                                                uint32_t *__restrict__ tmax)
+{
+    __shared__ int red[kScanThreads / kWave];
+    const size_t seg = blockIdx.y;
+    const int s = blockIdx.x * kScanThreads + threadIdx.x;
+    const int v = (s < L && rec_hi(srec[seg * L + s]) == 0u) ? s : -1;
+    const int m = block_max(v, red);
+    if (threadIdx.x == 0)
+        tmax[seg * gridDim.x + blockIdx.x] = (uint32_t)m;
+}
+
 __global__ __launch_bounds__(kScanThreads) void bucket_start_kernel(int L, int nh, const uint32_t *__restrict__ srec,
+                                                                    const uint32_t *__restrict__ tmax,
                                                                     uint32_t *__restrict__ bmeta)
 {
+    __shared__ int red[kScanThreads / kWave];
     __shared__ int wave_max[kScanThreads / kWave];
-    const size_t seg = blockIdx.x;
+    const size_t seg = blockIdx.y;
     const int r = (int)(seg % nh);
     const size_t bh = seg / nh;
-    const uint32_t *sr = srec + seg * L;
-    const int per = (L + kScanThreads - 1) / kScanThreads;
-    const int s0 = min(L, (int)threadIdx.x * per), s1 = min(L, s0 + per);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    int mx = -1;
-    for (int s = s0; s < s1; ++s)
-        if (rec_hi(sr[s]) == 0u)
-            mx = s;
-    // inclusive prefix maximum over the threads
-    int x = mx;
+    // the tiles before this one (at most 64 of them)
+    int seed = -1;
+    for (int t = threadIdx.x; t < (int)blockIdx.x; t += kScanThreads)
+        seed = max(seed, (int)tmax[seg * gridDim.x + t]);
+    seed = block_max(seed, red);
+    const int s = blockIdx.x * kScanThreads + threadIdx.x;
+    const uint32_t rec = s < L ? srec[seg * L + s] : 0u;
+    int x = (s < L && rec_hi(rec) == 0u) ? s : -1;
+    // inclusive prefix maximum over the block
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
         const int y = __shfl_up(x, o, kWave);
@@ -185,17 +218,11 @@ __global__ __launch_bounds__(kScanThreads) void bucket_start_kernel(int L, int n
     if (lane == kWave - 1)
         wave_max[wave] = x;
     __syncthreads();
-    int carry = __shfl_up(x, 1, kWave);
-    if (lane == 0)
-        carry = -1;
     for (int w = 0; w < wave; ++w)
-        carry = max(carry, wave_max[w]);
-    for (int s = s0; s < s1; ++s) {
-        const uint32_t rec = sr[s];
-        if (rec_hi(rec) == 0u)
-            carry = s;
-        bmeta[(bh * L + rec_lo(rec)) * nh + r] = (uint32_t)carry;
-    }
+        x = max(x, wave_max[w]);
+    x = max(x, seed);
+    if (s < L)
+        bmeta[(bh * L + rec_lo(rec)) * nh + r] = (uint32_t)x;
 }
 
 // Dot of a per-lane row (global) with a wave-distributed vector whose
@@ -697,9 +724,11 @@ hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32
         hipLaunchKernelGGL(window_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                            st, P.L, P.nh, P.m, chunk_only, total, srec, wmeta, cmin, alone);
     }
-    if (meta && x.bmeta)
-        hipLaunchKernelGGL(bucket_start_kernel, dim3((unsigned)(P.BH() * P.nh)), dim3(kScanThreads), 0, st, P.L, P.nh,
-                           srec, x.bmeta);
+    if (meta && x.bmeta) {
+        const dim3 grid((P.L + kScanThreads - 1) / kScanThreads, (unsigned)(P.BH() * P.nh));
+        hipLaunchKernelGGL(run_tile_kernel, grid, dim3(kScanThreads), 0, st, P.L, srec, x.bscr);
+        hipLaunchKernelGGL(bucket_start_kernel, grid, dim3(kScanThreads), 0, st, P.L, P.nh, srec, x.bscr, x.bmeta);
+    }
     return hipGetLastError();
 }
 

@@ -128,12 +128,13 @@ hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int3
 size_t sort_ws_bytes(const Dims &);
 // Window-related records beyond meta and srec, each null where the problem
 // has no use for it: wmeta (kRange / kRangePos window ends), alone and cmin
-// (kRangePos lone flags and their per-chunk scratch), bmeta (dup_bucket: the
-// start of each row's bucket run per round, [B*H*L][nh]).
+// (kRangePos lone flags and their per-chunk scratch), bmeta and bscr
+// (dup_bucket: the start of each row's bucket run per round, [B*H*L][nh],
+// and its scratch of one word per 1024 sorted rows).
 struct Extra {
     uint32_t *wmeta;
     uint8_t *alone;
-    uint32_t *cmin, *bmeta;
+    uint32_t *cmin, *bmeta, *bscr;
 };
 
 // Packed records, inverse norms, the extra records and (with out, dout)

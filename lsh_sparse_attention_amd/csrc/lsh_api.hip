@@ -53,9 +53,10 @@ int validate(const lsh_problem_t *p)
         return LSH_ERR_UNSUPPORTED;
     if (p->seq_len > kMaxLen || p->n_hashes > kMaxHashes || p->n_buckets > kMaxBucketsAbi)
         return LSH_ERR_UNSUPPORTED;
-    // every element index must fit in size_t arithmetic and every segment count in int
+    // every element index must fit in size_t arithmetic and every segment count in int;
+    // the (b, h, round) segments index a grid dimension of at most 65535
     const double tok_rounds = (double)p->batch * p->heads * p->n_hashes * p->seq_len;
-    if (tok_rounds > 2147483647.0)
+    if (tok_rounds > 2147483647.0 || (double)p->batch * p->heads * p->n_hashes > 65535.0)
         return LSH_ERR_UNSUPPORTED;
     return LSH_OK;
 }
@@ -103,6 +104,7 @@ size_t fwd_part(const Dims &P, uintptr_t b, W &w)
     }
     if (P.dup_bucket) {
         w.x.bmeta = (uint32_t *)(b + o); o += align_up(rnd * 4, 256);
+        w.x.bscr = (uint32_t *)(b + o); o += align_up((size_t)P.BH() * P.nh * ((P.L + 1023) / 1024) * 4, 256);
     }
     return o;
 }

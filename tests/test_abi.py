@@ -45,6 +45,7 @@ def _prob(**kw):
     (dict(n_buckets=15), 1), (dict(n_buckets=0), 1), (dict(chunk_len=48), 1), (dict(seq_len=-256), 1),
     (dict(batch=-1), 1), (dict(chunk_len=0), 1),
     (dict(head_dim=48), 2), (dict(seq_len=65536 * 2, chunk_len=64), 2), (dict(n_hashes=17), 2),
+    (dict(batch=4096, heads=8, n_hashes=2, seq_len=64), 2),
     (dict(n_buckets=8192), 2),
 ])
 def test_invalid_problems_rejected_before_launch(kw, status):
@@ -111,12 +112,15 @@ def test_flags_values():
     extra = a256(rnd * 4) + a256(rnd) + a256(rnd // c.chunk_len * 4)
     nbn = _prob(bucket_mask=False, causal=False)
     # duplicates counted over buckets: the bucket-run starts per token-round
+    # and one scratch word per 1024 sorted rows of each (b, h, round)
     dup = _prob(dup_by_bucket=True)
+    segs = c.batch * c.heads * c.n_hashes
     for kind in (1, 2, 3):
         base = L.lsh_workspace_bytes(ctypes.byref(c), kind)
         assert L.lsh_workspace_bytes(ctypes.byref(nbc), kind) == base + extra
         assert L.lsh_workspace_bytes(ctypes.byref(nbn), kind) == base + a256(rnd * 4)
-        assert L.lsh_workspace_bytes(ctypes.byref(dup), kind) == base + a256(rnd * 4)
+        assert L.lsh_workspace_bytes(ctypes.byref(dup), kind) == (
+            base + a256(rnd * 4) + a256(segs * ((c.seq_len + 1023) // 1024) * 4))
 
 
 def test_null_and_misaligned_pointers_rejected():
