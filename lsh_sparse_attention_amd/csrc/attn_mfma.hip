@@ -15,16 +15,19 @@
 // r' < r (the first round that holds a member counts it).  The band needs
 // no chunk arithmetic: win_lo carries it.
 //
-// Dataflow, common to the three attention kernels: a workgroup (4 waves)
-// owns 128 consecutive sorted rows of one (batch, head, round); the other
-// operand streams through LDS in blocks of 32 sorted rows.  Rows are fetched
-// by position straight into LDS with global_load_lds_dwordx4 (no staging
-// registers) into a ring of LDS stages, several blocks ahead of the block in
-// use, so that enough bytes are in flight per CU to cover the loaded memory
-// latency (the query-owned kernels run two workgroups per CU, the key-owned
-// one a single workgroup with a deeper ring); each
-// wave waits on its own outstanding loads with s_waitcnt vmcnt and a
-// workgroup barrier publishes the block.  Tiles are stored unpadded with the
+// Dataflow: a workgroup owns 128 consecutive sorted rows of one (batch, head,
+// round); the other operand streams through LDS in blocks of 32 sorted rows.
+// Rows are fetched by position straight into LDS with global_load_lds_dwordx4
+// (no staging registers) into a ring of LDS stages, several blocks ahead of
+// the block in use, so that enough bytes are in flight per CU to cover the
+// loaded memory latency; each wave waits on its own outstanding loads with
+// s_waitcnt vmcnt and a workgroup barrier publishes the block.  Two kernel
+// families: for chunk lengths that divide 128 (every workload), persistent
+// 8-wave workgroups (one per CU) walk runs of consecutive 128-row tiles with
+// an 8-stage ring shared between neighbouring tiles (q_stream_kernel,
+// dkv_stream_kernel, below); for other chunk lengths, one 4-wave workgroup per
+// tile (fwd_kernel, dq_kernel with a 4-stage ring and two workgroups per CU;
+// dkv_kernel).  Tiles are stored unpadded with the
 // 16-byte chunks of row r XOR-swizzled by r, so that both the row reads
 // (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16) spread over
 // the LDS banks.  Per-block metadata (inverse key norms, the keys' sorted
@@ -493,7 +496,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int r = W.r, bh = W.bh, s0 = W.s0;
     const uint32_t *sr = srec + ((size_t)bh * nh + r) * L;
     const size_t tok0 = (size_t)bh * L;
-    const float scale_log2 = scale * kLog2e;
 
     // Prologue in two dependent memory round trips, as in the forward.
     const int c0 = s0 - min(s0, maxw);
@@ -1332,7 +1334,6 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const size_t part0 = (size_t)seg * L;
     const int kts = ktile_stride(nh);
     const uint8_t *ktb = ktile + (size_t)seg * nblk * kts;
-    const float scale_log2 = scale * kLog2e;
 
     auto issue_block = [&](int a) __attribute__((always_inline)) {
         const int st = a % kStreamStages;
@@ -1713,7 +1714,6 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
     const int tok = blockIdx.x * TPB + grp;
     if (tok >= ntok)
         return;
-    const int bh = tok / L, t = tok % L;
     float aq[8] = {}, ak[8] = {}, av[8] = {};
     bool alone = true;
     // every round's rows requested before any is summed (nh <= NH)
