@@ -229,6 +229,26 @@ def ff_variant(steps, rows) -> dict:
             "value": rows / (ms * 1e-3), "unit": "tokens/s"}
 
 
+def copy_bandwidth_gbs() -> float:
+    """HBM bandwidth of a plain device-to-device copy of 1 GiB (bytes read + written per second),
+    the practical ceiling a bandwidth-bound kernel is compared with beside the 8 TB/s spec."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    gbs = 2 * 4 * n * 5 / (time.perf_counter() - t0) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def source_sha(kernel: str) -> str:
     """Digest of the sources a kernel is compiled from (its file and the shared header)."""
     h = hashlib.sha256()
@@ -439,6 +459,10 @@ def main() -> int:
     roof["kernel"] = dominant
     roof["kernel_us"] = kern_ms * 1e3
     roof["algorithmic"] = {"flops": flops, "bytes": nbytes}
+    if roof["bound"] == "hbm":
+        # the measured denominator beside the spec one: a plain 1 GiB device copy
+        roof["copy_gbs"] = copy_bandwidth_gbs()
+        roof["frac_of_copy"] = roof["achieved"] / roof["copy_gbs"]
 
     result = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
