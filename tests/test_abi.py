@@ -199,3 +199,29 @@ def test_kernel_names_and_profile_hook():
     assert L.lsh_kernel_name(len(_lib.KERNELS)) is None
     assert L.lsh_profile_kernel(len(_lib.KERNELS), None, None) == 1
     assert L.lsh_profile_kernel(0, None, None) == 0      # clearing needs no GPU
+
+
+def test_ff_descriptions_validated_without_launching():
+    L = _lib.lib()
+    dummy = ctypes.c_void_p(256)
+    ok = lsh.ff_problem(100, 64, 256, 2)
+    assert L.lsh_ff_workspace_bytes(ctypes.byref(ok), 0) > 0
+    assert L.lsh_ff_workspace_bytes(ctypes.byref(ok), 1) > L.lsh_ff_workspace_bytes(ctypes.byref(ok), 0)
+    for bad, status in ((lsh.ff_problem(100, 60, 256, 2), 1), (lsh.ff_problem(100, 64, 250, 2), 1),
+                        (lsh.ff_problem(100, 64, 256, 0), 1), (lsh.ff_problem(-1, 64, 256, 1), 1)):
+        assert L.lsh_ff_workspace_bytes(ctypes.byref(bad), 0) == 0
+        assert L.lsh_ff_fwd(ctypes.byref(bad), dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                            ctypes.c_size_t(1 << 30), None) == status
+    f32 = lsh.ff_problem(100, 64, 256, 2)
+    f32.dtype = 0
+    assert L.lsh_ff_fwd(ctypes.byref(f32), dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                        ctypes.c_size_t(1 << 30), None) == 2
+    # null pointers and a short workspace are rejected before anything runs
+    assert L.lsh_ff_fwd(ctypes.byref(ok), None, dummy, dummy, dummy, dummy, dummy, dummy,
+                        ctypes.c_size_t(1 << 30), None) == 1
+    assert L.lsh_ff_fwd(ctypes.byref(ok), dummy, dummy, dummy, dummy, dummy, dummy, dummy, ctypes.c_size_t(16),
+                        None) == 1
+    empty = lsh.ff_problem(0, 64, 256, 2)
+    assert L.lsh_ff_workspace_bytes(ctypes.byref(empty), 1) == 0
+    assert L.lsh_ff_bwd(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, None, None,
+                        ctypes.c_size_t(0), None) == 0

@@ -67,7 +67,7 @@ def _np(t):
 # n, d_model, d_ff, chunks: tiles of 128 with ragged row, column and K tails,
 # one chunk and many, a chunk count that does not divide n
 SMALL = [(1000, 64, 256, 3), (257, 128, 512, 1), (130, 64, 192, 7), (2048, 256, 1024, 4), (1, 8, 8, 1),
-         (96, 1024, 4096, 2)]
+         (96, 1024, 4096, 2), (5, 16, 24, 9), (1100, 40, 136, 2)]
 
 
 @pytest.mark.parametrize("n,dm,dff,c", SMALL)

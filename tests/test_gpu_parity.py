@@ -283,6 +283,7 @@ NB_SMALL = [
     ("nb-f32-d128-m1", 1, 1, 256, 128, 8, 2, 1, "f32", False, True),
     ("nb-f32-one-chunk", 1, 1, 256, 64, 8, 2, 256, "f32", False, True),
     ("nb-tiny-L", 1, 1, 8, 32, 4, 2, 2, "f32", False, True),
+    ("nb-single-token", 1, 1, 1, 32, 2, 1, 1, "f32", False, True),
     ("nb-bf16-causal", 2, 2, 1024, 64, 16, 3, 32, "bf16", False, True),
     ("nb-bf16-causal-d128", 1, 2, 2048, 128, 32, 2, 64, "bf16", False, True),
     ("nb-bf16-causal-m128", 1, 2, 4096, 64, 64, 1, 128, "bf16", False, True),
@@ -360,6 +361,7 @@ DB_SMALL = [
     ("db-f32", 1, 2, 1024, 64, 8, 3, 16, "f32", False, True),
     ("db-f32-noncausal", 1, 1, 512, 32, 4, 2, 8, "f32", False, False),
     ("db-tiny-L", 1, 1, 8, 32, 4, 2, 2, "f32", False, True),
+    ("db-single-token", 1, 1, 1, 32, 2, 2, 1, "f32", False, True),
     ("db-bf16", 2, 2, 1024, 64, 8, 3, 16, "bf16", False, True),
     ("db-bf16-d128", 1, 2, 2048, 128, 16, 2, 32, "bf16", False, True),
     ("db-bf16-d128-nh4", 1, 1, 2048, 128, 16, 4, 32, "bf16", False, True),
