@@ -229,6 +229,43 @@ def ff_variant(steps, rows) -> dict:
             "value": rows / (ms * 1e-3), "unit": "tokens/s"}
 
 
+def gemm_tflops(n: int = 8192) -> float:
+    """Rate of a plain n^3 bf16 matrix product through torch.matmul (the vendor GEMM library), the
+    practical matrix-core ceiling a compute-bound kernel is compared with beside the datasheet peak."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    reps = 10
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    tf = 2.0 * n ** 3 * reps / (time.perf_counter() - t0) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return tf
+
+
+def kernel_rooflines(per_kernel: dict, cfg, gemm_tf: float) -> dict:
+    """Per kernel: one launch's duration and its algorithmic bytes and flops as rates, each
+    against the HBM and matrix-core peaks (and the measured GEMM rate for the products)."""
+    out = {}
+    for k, us in per_kernel.items():
+        flops, nbytes = algorithmic_work(k, cfg)
+        t = us * 1e-6
+        row = {"us": round(us, 2), "gbs": round(nbytes / t / 1e9, 1),
+               "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 3)}
+        if flops:
+            tf = flops / t / 1e12
+            row.update({"tflops": round(tf, 1), "frac_mfma": round(tf / MFMA_PEAK_TFLOPS[cfg.dtype], 3),
+                        "frac_of_gemm": round(tf / gemm_tf, 3)})
+        out[k] = row
+    return out
+
+
 def copy_bandwidth_gbs() -> float:
     """HBM bandwidth of a plain device-to-device copy of 1 GiB (bytes read + written per second),
     the practical ceiling a bandwidth-bound kernel is compared with beside the 8 TB/s spec."""
@@ -476,6 +513,10 @@ def main() -> int:
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "variants": None,
     }
+    if cfg.dtype == "bf16":
+        gtf = gemm_tflops()
+        result["gemm_tflops"] = gtf
+        result["kernels"] = kernel_rooflines(per_kernel, cfg, gtf)
     if not args.no_variants:
         result["variants"] = {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)}
     del mod
@@ -486,6 +527,9 @@ def main() -> int:
         result["variants"]["dup_by_bucket"] = set_variant(q, v, rot, do, args.steps, cfg, hip, True, True, True)
         torch.cuda.empty_cache()
         result["variants"]["chunked_ff"] = ff_variant(args.steps, cfg.batch * cfg.seq_len)
+        if "gemm_tflops" in result:
+            ff = result["variants"]["chunked_ff"]
+            ff["frac_of_gemm"] = ff["tflops"] / result["gemm_tflops"]
     torch.cuda.empty_cache()
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
