@@ -12,9 +12,9 @@
 // C = A B^T with both operands stored K-major ([M][K] and [N][K]; W1 and W2
 // are transposed once per call where needed).  A workgroup of 4 waves
 // computes a 128 x 128 tile of C, each wave a 64 x 64 quarter as 2 x 2 MFMA
-// tiles, with the K loop staged through double-buffered LDS in steps of 64;
-// the next step's operands are fetched into registers while the current one
-// is multiplied.  The epilogue adds the bias and applies the ReLU, or masks
+// tiles, with the K loop staged through one LDS stage in steps of 64; the
+// next step's operands are fetched into registers while the current one is
+// multiplied.  The epilogue adds the bias and applies the ReLU, or masks
 // by ReLU' (the backward's dH = dY W2^T where the hidden value is positive).
 // The weight gradients (x^T dh, h^T dy) sum over the chunk's rows, which are
 // the leading dimension of both operands: a second kernel stages k-rows of
@@ -43,8 +43,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(int M, int N, int
                                                                const bf16 *__restrict__ mask, int ldm,
                                                                bf16 *__restrict__ C, int ldc)
 {
-    __shared__ __align__(16) uint16_t As[2][kBM * kPitch];
-    __shared__ __align__(16) uint16_t Bs[2][kBN * kPitch];
+    // one LDS stage (36 KB): three workgroups share a CU (the register count
+    // allows three waves per SIMD) and hide each other's load latency, which
+    // measured faster than two double-buffered workgroups
+    __shared__ __align__(16) uint16_t As[kBM * kPitch];
+    __shared__ __align__(16) uint16_t Bs[kBN * kPitch];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / 2, wn = wave % 2;
     const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
@@ -61,12 +64,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(int M, int N, int
             rb[i] = (n0 + row < N && k < K) ? ld16(B + (size_t)(n0 + row) * ldb + k) : z;
         }
     };
-    auto stash = [&](int buf) __attribute__((always_inline)) {
+    auto stash = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = tid + kGemmThreads * i, row = q / 8, kc = q % 8;
-            st16(&As[buf][row * kPitch + 8 * kc], ra[i]);
-            st16(&Bs[buf][row * kPitch + 8 * kc], rb[i]);
+            st16(&As[row * kPitch + 8 * kc], ra[i]);
+            st16(&Bs[row * kPitch + 8 * kc], rb[i]);
         }
     };
 
@@ -78,10 +81,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(int M, int N, int
             acc[i][j] = f32x16_t{};
     const int nk = (K + kBK - 1) / kBK;
     fetch(0);
-    stash(0);
+    stash();
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
+        // the next K step's operands are loaded into registers while this one
+        // is multiplied out of LDS
         if (kt + 1 < nk)
             fetch((kt + 1) * kBK);
 #pragma unroll
@@ -90,10 +94,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(int M, int N, int
             bf16x8_t a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = as_bf16x8(ld16(&As[buf][(wm * 64 + 32 * i + c) * kPitch + 16 * ks + 8 * h]));
+                a[i] = as_bf16x8(ld16(&As[(wm * 64 + 32 * i + c) * kPitch + 16 * ks + 8 * h]));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                b[j] = as_bf16x8(ld16(&Bs[buf][(wn * 64 + 32 * j + c) * kPitch + 16 * ks + 8 * h]));
+                b[j] = as_bf16x8(ld16(&Bs[(wn * 64 + 32 * j + c) * kPitch + 16 * ks + 8 * h]));
             // B as the instruction's first operand: the tile comes out transposed,
             // so a lane holds 4 consecutive columns of one row of C
 #pragma unroll
@@ -102,8 +106,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_kernel(int M, int N, int
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
         }
-        if (kt + 1 < nk)
-            stash(buf ^ 1);
+        if (kt + 1 < nk) {
+            __syncthreads();   // every wave is done reading the stage
+            stash();
+        }
         __syncthreads();
     }
 
