@@ -114,9 +114,14 @@ class Hip:
             raise RuntimeError("hipEventCreate failed")
         return ev
 
-    def elapsed_ms(self, a, b) -> float:
+    def elapsed_ms(self, a, b, missing_ok: bool = False):
+        """Milliseconds between two recorded events.  With missing_ok, None when
+        they were never recorded (a kernel the problem does not launch)."""
         ms = ctypes.c_float()
         if self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            self.h.hipGetLastError()   # clear the runtime's last-error state
+            if missing_ok:
+                return None
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
 
@@ -174,7 +179,9 @@ def set_variant(q, v, rot, do, steps, cfg, hip, causal, bucket_mask, dup_by_buck
     torch.cuda.synchronize()
     per_kernel = {}
     for k, (a, b) in enumerate(evs):
-        per_kernel[L_.KERNELS[k]] = round(hip.elapsed_ms(a, b) * 1e3, 2)
+        ms = hip.elapsed_ms(a, b, missing_ok=True)
+        if ms is not None:
+            per_kernel[L_.KERNELS[k]] = round(ms * 1e3, 2)
         L.lsh_profile_kernel(k, None, None)
         hip.destroy(a)
         hip.destroy(b)
@@ -249,7 +256,7 @@ def gemm_tflops(n: int = 8192) -> float:
     return tf
 
 
-def kernel_rooflines(per_kernel: dict, cfg, gemm_tf: float) -> dict:
+def kernel_rooflines(per_kernel: dict, cfg, gemm_tf) -> dict:
     """Per kernel: one launch's duration and its algorithmic bytes and flops as rates, each
     against the HBM and matrix-core peaks (and the measured GEMM rate for the products)."""
     out = {}
@@ -260,8 +267,9 @@ def kernel_rooflines(per_kernel: dict, cfg, gemm_tf: float) -> dict:
                "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 3)}
         if flops:
             tf = flops / t / 1e12
-            row.update({"tflops": round(tf, 1), "frac_mfma": round(tf / MFMA_PEAK_TFLOPS[cfg.dtype], 3),
-                        "frac_of_gemm": round(tf / gemm_tf, 3)})
+            row.update({"tflops": round(tf, 1), "frac_mfma": round(tf / MFMA_PEAK_TFLOPS[cfg.dtype], 3)})
+            if gemm_tf:
+                row["frac_of_gemm"] = round(tf / gemm_tf, 3)
         out[k] = row
     return out
 
@@ -460,7 +468,9 @@ def main() -> int:
     torch.cuda.synchronize()
     per_kernel = {}
     for k, (a, b) in enumerate(evs):
-        per_kernel[_lib.KERNELS[k]] = hip.elapsed_ms(a, b) * 1e3
+        ms = hip.elapsed_ms(a, b, missing_ok=True)   # kernels the problem does not launch are left out
+        if ms is not None:
+            per_kernel[_lib.KERNELS[k]] = ms * 1e3
         L.lsh_profile_kernel(k, None, None)
     dominant = max(per_kernel, key=per_kernel.get)
     dk = _lib.KERNELS.index(dominant)
@@ -513,10 +523,11 @@ def main() -> int:
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "variants": None,
     }
-    if cfg.dtype == "bf16":
+    gtf = None
+    if cfg.dtype == "bf16":   # the GEMM reference rate is a bf16 one
         gtf = gemm_tflops()
         result["gemm_tflops"] = gtf
-        result["kernels"] = kernel_rooflines(per_kernel, cfg, gtf)
+    result["kernels"] = kernel_rooflines(per_kernel, cfg, gtf)
     if not args.no_variants:
         result["variants"] = {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)}
     del mod
