@@ -124,9 +124,12 @@ __device__ __forceinline__ void tile_argmax(const f32x16_t (&acc)[2], int j0, in
 }
 
 // The same update for a full tile with fewer vector instructions: the
-// tile's largest key by three-input maxima, then the first slot holding it
-// (a compare and a select per score, last slot first).  Only tracker 0 of
-// each column tile is used.
+// tile's largest key by three-input maxima (over each half of the slots and
+// then both), then the first slot holding it, searched in two independent
+// chains (a compare and a select per score, last slot first).  The search
+// is written so that its result is always used; otherwise the compiler
+// turns it into a branch, which splits the code it can schedule together
+// with the next tile's products.  Only tracker 0 of each column tile is used.
 __device__ __forceinline__ void tile_argmax_full(const f32x16_t (&acc)[2], int j0, uint32_t (&bk)[2][2],
                                                  int (&bi)[2][2])
 {
@@ -138,15 +141,21 @@ __device__ __forceinline__ void tile_argmax_full(const f32x16_t (&acc)[2], int j
             const uint32_t u = __float_as_uint(acc[ct][e]);
             k[e] = __builtin_amdgcn_alignbit(u, u, 31);
         }
-        const uint32_t m0 = max(max(k[0], k[1]), k[2]), m1 = max(max(k[3], k[4]), k[5]);
-        const uint32_t m2 = max(max(k[6], k[7]), k[8]), m3 = max(max(k[9], k[10]), k[11]);
-        const uint32_t m4 = max(max(k[12], k[13]), k[14]);
-        const uint32_t tm = max(max(max(m0, m1), m2), max(max(m3, m4), k[15]));
-        int ts = 0;
+        const uint32_t lo = max(max(max(max(k[0], k[1]), k[2]), max(max(k[3], k[4]), k[5])), max(k[6], k[7]));
+        const uint32_t hi = max(max(max(max(k[8], k[9]), k[10]), max(max(k[11], k[12]), k[13])), max(k[14], k[15]));
+        const uint32_t tm = max(lo, hi);
+        // the key searched for: the tile maximum if it beats the tracked one,
+        // else all ones (a NaN pattern, never the key of a finite score), so
+        // the search runs unconditionally and leaves the tracked column
+        const uint32_t want = tm > bk[ct][0] ? tm : 0xffffffffu;
+        const int keep = bi[ct][0] - j0;
+        int ta = keep, tb = keep;
 #pragma unroll
-        for (int e = 15; e >= 0; --e)
-            ts = k[e] == tm ? 8 * (e / 4) + (e % 4) : ts;
-        bi[ct][0] = tm > bk[ct][0] ? j0 + ts : bi[ct][0];
+        for (int e = 7; e >= 0; --e) {
+            ta = k[e] == want ? 8 * (e / 4) + (e % 4) : ta;
+            tb = k[e + 8] == want ? 8 * ((e + 8) / 4) + (e % 4) : tb;
+        }
+        bi[ct][0] = j0 + (lo == want ? ta : tb);
         bk[ct][0] = max(bk[ct][0], tm);
     }
 }
@@ -291,9 +300,10 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
 
 // The same computation when every staged block holds 64 full columns
 // (half % 64 == 0), software-pipelined within the wave: the matrix-core
-// products of a tile are issued interleaved with the argmax of the tile
-// before it (its accumulators are a second register set), so the vector ALU
-// work runs while the matrix core is busy instead of after it.  The argmax
+// products of a tile and the argmax of the tile before it (its accumulators
+// are a second register set) are independent code in one scheduling region,
+// which the compiler interleaves so that vector work can issue while the
+// matrix core is busy (explicit interleaving hints measured slower).  The argmax
 // of a block's last tile runs under the next block's first tile; a round is
 // stored once its last tile's argmax is done.  The staged blocks alternate
 // between two LDS buffers, so one barrier per block suffices: block b + 1
@@ -344,14 +354,6 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int
             st16(&buf[(i / CPR) * P + 8 * (i % CPR)], pre[it]);
         }
     };
-    // one product, then a share of the other tile's argmax, sixteen times
-    auto interleave = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 2 * (D / 16); ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-        }
-    };
     auto products = [&](const uint16_t *buf, int jt, f32x16_t (&acc)[2]) __attribute__((always_inline)) {
         bf16x8_t aop[D / 16];
         read_rot<D, P>(buf, jt, grp, m, aop);
@@ -388,12 +390,10 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int
         for (int jt = 0; jt < NT; jt += 2) {
             products(buf, jt, acc0);
             tile_argmax_full(acc1, jt == 0 ? prev_j : jb + 32 * (jt - 1), bk, bi);
-            interleave();
             if (jt == 0 && prev_last)
                 round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
             products(buf, jt + 1, acc1);
             tile_argmax_full(acc0, jb + 32 * jt, bk, bi);
-            interleave();
         }
         prev_j = jb + COLS - 32;
         prev_r = r;
