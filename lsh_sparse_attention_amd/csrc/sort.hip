@@ -109,7 +109,11 @@ __global__ __launch_bounds__(kScatterThreads) void sort_scatter(int L, int nb, i
                                                                 int32_t *__restrict__ win_lo)
 {
     extern __shared__ int32_t wcnt[];  // [4][nb]
-    const int tile = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x;
+    // all tiles of a segment on one XCD: their scattered 4-byte writes into
+    // the segment's sorted order then meet in one L2, which merges them into
+    // whole lines before they go to memory
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int tile = lb % ntiles, seg = lb / ntiles, tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
     const int nwaves = kScatterThreads / kWave;
     for (int k = tid; k < nwaves * nb; k += kScatterThreads)
@@ -213,7 +217,7 @@ hipError_t launch_sort(const Dims &P, const int32_t *buckets, int32_t *perm, int
         return e;
     const size_t lds_scatter = (size_t)(kScatterThreads / kWave) * P.nb * sizeof(int32_t);
     ProfScope prof(LSH_KERNEL_SORT_SCATTER, st);
-    hipLaunchKernelGGL(sort_scatter, dim3(nt, S), dim3(kScatterThreads), lds_scatter, st, P.L, P.nb, nbits, P.m,
+    hipLaunchKernelGGL(sort_scatter, dim3(nt * S), dim3(kScatterThreads), lds_scatter, st, P.L, P.nb, nbits, P.m,
                        nt, buckets, (const int32_t *)cnt, (const int32_t *)bstart, perm, inv, win_lo);
     return hipGetLastError();
 }
