@@ -41,8 +41,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, int m, in
     // D/8 lanes per token, each on 8 consecutive elements
     constexpr int CPT = D / 8, TPB = kThreads / CPT;
     const int grp = threadIdx.x / CPT, ch = threadIdx.x % CPT;
-    const int t = blockIdx.x * TPB + grp;
-    const int bh = blockIdx.y;
+    // the blocks of one (b, h) on one XCD: the records written into its
+    // rounds' sorted orders land at scattered places, and one L2 then
+    // merges them into whole lines before they go to memory
+    const int nbx = (L + TPB - 1) / TPB;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int t = (lb % nbx) * TPB + grp;
+    const int bh = lb / nbx;
     const bool valid = t < L;
     const size_t tok = (size_t)bh * L + (valid ? t : 0);
     float x[8], y[8];
@@ -709,7 +714,7 @@ hipError_t prep_go(const Dims &P, const void *q, const int32_t *inv, const int32
     uint32_t *wmeta = x.wmeta, *cmin = x.cmin;
     uint8_t *alone = x.alone;
     constexpr int TPB = kThreads / (D / 8);
-    dim3 grid((P.L + TPB - 1) / TPB, P.BH());
+    dim3 grid((unsigned)(((P.L + TPB - 1) / TPB) * P.BH()));
     ProfScope prof(LSH_KERNEL_PREP, st);
     const int chunk_only = P.bucket_mask ? 0 : 1;
     hipLaunchKernelGGL((prep_kernel<T, D>), grid, dim3(kThreads), 0, st, P.L, P.nh, P.m, chunk_only, (const T *)q,
