@@ -232,7 +232,9 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
                                                              uint8_t *__restrict__ ktile, uint8_t *__restrict__ qtile)
 {
     const int lane = threadIdx.x % kWave;
-    const int tile = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+    // the tiles of one (b, h) on one XCD: their gathers of that head's
+    // records, norms, lse and D then share one L2
+    const int tile = xcd_block(blockIdx.x, gridDim.x) * (kThreads / kWave) + threadIdx.x / kWave;
     if (tile >= ntiles)
         return;
     const int per = L / kBlk;
