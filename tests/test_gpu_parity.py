@@ -98,6 +98,17 @@ def test_workload_shapes_match_oracle(name):
     assert np.array_equal(res["out"][:, :, 0], gen.to_f64(x["v"][:, :, 0], cfg.dtype))
 
 
+def test_maximum_segment_count():
+    """B*H*n_hashes = 65528 (segments are capped at 65535): the grids that index segments or heads
+    run at their largest; every segment's sort is checked and three heads against the oracle."""
+    cfg = gen.Config("max-segments", 1, 8191, 128, 64, 8, 8, 32, "bf16", False, True, 901, n_clusters=16)
+    gu.say(f"[gpu] maximum segment count: {cfg}")
+    x = gen.generate(cfg, with_grad=True)
+    res = gu.run_gpu(x)
+    gu.check_sort_properties(res, cfg)
+    gu.compare_slices(x, res, [(0, 0), (0, 4095), (0, 8190)])
+
+
 def test_rounds_combine_to_output():
     cfg = _small_cfg(SMALL[1])
     gu.say(f"[gpu] combine identity {cfg}")
