@@ -3,9 +3,10 @@
 Hash buckets, permutations, inverse permutations and window bounds must match
 bit for bit; outputs, lse and gradients within atol = rtol = 1e-4 (fp32
 problems) or 2e-2 (bf16 problems), elementwise, against the fp64 oracle.
-Small shapes are compared whole; the five workload shapes at full size are
-compared on sampled (batch, head) slices, with the sort checked for every
-slice through properties that hold at any size.
+Small shapes are compared whole; the five workload shapes at full size have
+the hash and sort of every (batch, head) slice compared with the oracle's bit
+for bit, and outputs and gradients compared on sampled slices.  Each of the
+three backward entry points is compared with the oracle on its own.
 """
 import numpy as np
 import pytest
@@ -96,6 +97,9 @@ def test_workload_shapes_match_oracle(name):
     gu.compare_slices(x, res, SAMPLES[name])
     # the first token of every slice attends only to itself
     assert np.array_equal(res["out"][:, :, 0], gen.to_f64(x["v"][:, :, 0], cfg.dtype))
+    # buckets, perm, inv and win_lo of every (b, h) slice against the oracle's hash and sort
+    gu.say(f"[gpu] full-size {name}: oracle hash and sort on all {cfg.batch * cfg.heads} slices")
+    gu.compare_hash_sort_all_slices(x, res)
 
 
 def test_maximum_segment_count():
@@ -138,57 +142,31 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("idx", [1, 0, 2, 17, 19])
-def test_standalone_backward_matches_saved(idx):
-    # lsh_attn_bwd (records derived again from perm, inv, win_lo) against the
-    # saved-records backward that LshAttention runs: same kernels, same bits
-    import lsh_sparse_attention_amd as lsh
-    from lsh_sparse_attention_amd import _lib
+@pytest.mark.parametrize("idx", [1, 0, 2, 17, 19, 13, 21])
+def test_backward_entry_points_match_oracle(idx):
+    # lsh_attn_bwd_saved, lsh_attn_bwd (records derived again from perm, inv,
+    # win_lo) and lsh_attn_bwd_rehash (buckets, order and windows recomputed
+    # from q and rot): each one's dq and dv against the oracle, and the three
+    # bit for bit against one another
     cfg = _small_cfg(SMALL[idx])
-    gu.say(f"[gpu] standalone vs saved backward {cfg}")
+    gu.say(f"[gpu] backward entry points {cfg}")
     x = gen.generate(cfg)
-    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype)
-    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
-    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
-    mod = lsh.LshAttention(prob)
-    mod.forward(q, v, rot)
-    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
-    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
-    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
-    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
-    torch.cuda.synchronize()
-    assert torch.equal(dq.view(torch.int16) if dq.dtype == torch.bfloat16 else dq,
-                       dq_s.view(torch.int16) if dq_s.dtype == torch.bfloat16 else dq_s)
-    assert torch.equal(dv.view(torch.int16) if dv.dtype == torch.bfloat16 else dv,
-                       dv_s.view(torch.int16) if dv_s.dtype == torch.bfloat16 else dv_s)
+    res = gu.run_gpu_backward_entries(x)
+    gu.compare_backward_entries(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
 
 
-@pytest.mark.parametrize("idx", [1, 0, 2, 17, 19])
-def test_rehash_backward_matches_stored_order(idx):
-    # lsh_attn_bwd_rehash recomputes buckets, order and windows from q and
-    # rot; hashing and sorting are deterministic, so the gradient equals
-    # lsh_attn_bwd's on the forward's stored order bit for bit
-    import lsh_sparse_attention_amd as lsh
-    from lsh_sparse_attention_amd import _lib
-    cfg = _small_cfg(SMALL[idx])
-    gu.say(f"[gpu] rehash vs stored-order backward {cfg}")
-    x = gen.generate(cfg)
-    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype)
-    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
-    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
-    mod = lsh.LshAttention(prob, backward=False)
-    mod.forward(q, v, rot)
-    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
-    dq, dv = torch.empty_like(q), torch.empty_like(v)
-    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
-    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
-    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
-    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
-    torch.cuda.synchronize()
-    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
-    assert torch.equal(bits(dq), bits(dq2)) and torch.equal(bits(dv), bits(dv2))
+BWD_FULL = {"text": [(0, 5)], "stress": [(2, 6)]}
+
+
+@pytest.mark.parametrize("name", list(BWD_FULL))
+def test_backward_entry_points_at_workload_size(name):
+    # the standalone and rehash backwards at full size (the rehash path hashes
+    # and sorts every (b, h, round) segment inside the call), against the oracle
+    x = _full(name)
+    gu.say(f"[gpu] backward entry points, full-size {name}: running the library")
+    res = gu.run_gpu_backward_entries(x)
+    gu.say(f"[gpu] backward entry points, full-size {name}: oracle on slices {BWD_FULL[name]}")
+    gu.compare_backward_entries(x, res, BWD_FULL[name])
 
 
 # ----------------------------------------------------------------------------- non-causal
@@ -257,30 +235,12 @@ def test_noncausal_workload_shapes_match_oracle(name):
 
 
 @pytest.mark.parametrize("idx", [0, 8, 9, 15, 19])
-def test_noncausal_saved_standalone_and_rehash_backwards_agree(idx):
-    # the three backward entry points give the same bits on non-causal problems
-    import lsh_sparse_attention_amd as lsh
-    from lsh_sparse_attention_amd import _lib
+def test_noncausal_backward_entry_points_match_oracle(idx):
     cfg = _nc_cfg(NC_SMALL[idx])
     gu.say(f"[gpu] non-causal backward entry points {cfg}")
     x = gen.generate(cfg)
-    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=False)
-    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
-    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
-    mod = lsh.LshAttention(prob)
-    mod.forward(q, v, rot)
-    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
-    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
-    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
-    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
-    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
-    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
-    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
-    torch.cuda.synchronize()
-    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
-    for a, b in ((dq, dq_s), (dv, dv_s), (dq2, dq_s), (dv2, dv_s)):
-        assert torch.equal(bits(a), bits(b))
+    res = gu.run_gpu_backward_entries(x)
+    gu.compare_backward_entries(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
 
 
 # ----------------------------------------------------------------------------- no bucket mask
@@ -336,29 +296,12 @@ def test_no_bucket_mask_workload_shapes_match_oracle(name, causal, sl):
 
 
 @pytest.mark.parametrize("idx", [0, 5, 7, 11, 14])
-def test_no_bucket_mask_backward_entry_points_agree(idx):
-    import lsh_sparse_attention_amd as lsh
-    from lsh_sparse_attention_amd import _lib
+def test_no_bucket_mask_backward_entry_points_match_oracle(idx):
     cfg = _nb_cfg(NB_SMALL[idx])
     gu.say(f"[gpu] no-bucket-mask backward entry points {cfg}")
     x = gen.generate(cfg)
-    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=cfg.causal, bucket_mask=False)
-    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
-    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
-    mod = lsh.LshAttention(prob)
-    mod.forward(q, v, rot)
-    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
-    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
-    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
-    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
-    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
-    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
-    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
-    torch.cuda.synchronize()
-    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
-    for a, b in ((dq, dq_s), (dv, dv_s), (dq2, dq_s), (dv2, dv_s)):
-        assert torch.equal(bits(a), bits(b))
+    res = gu.run_gpu_backward_entries(x)
+    gu.compare_backward_entries(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
 
 
 # ----------------------------------------------------------------------------- duplicates by bucket
@@ -412,29 +355,12 @@ def test_dup_by_bucket_stress_workload_matches_oracle():
 
 
 @pytest.mark.parametrize("idx", [0, 3, 5, 9, 10])
-def test_dup_by_bucket_backward_entry_points_agree(idx):
-    import lsh_sparse_attention_amd as lsh
-    from lsh_sparse_attention_amd import _lib
+def test_dup_by_bucket_backward_entry_points_match_oracle(idx):
     cfg = _db_cfg(DB_SMALL[idx])
     gu.say(f"[gpu] dup-by-bucket backward entry points {cfg}")
     x = gen.generate(cfg)
-    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype, causal=cfg.causal, dup_by_bucket=True)
-    q, v = gu.to_device(x["q"], cfg.dtype), gu.to_device(x["v"], cfg.dtype)
-    rot, do = gu.to_device(x["rot"], cfg.dtype), gu.to_device(x["dout"], cfg.dtype)
-    mod = lsh.LshAttention(prob)
-    mod.forward(q, v, rot)
-    dq_s, dv_s = (t.clone() for t in mod.backward(q, v, do))
-    ws = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_BWD), dtype=torch.uint8, device="cuda")
-    dq, dv = torch.empty_like(dq_s), torch.empty_like(dv_s)
-    lsh.lsh_attn_bwd(prob, q, v, mod.out, do, mod.lse, mod.perm, mod.inv, mod.win_lo, dq, dv, ws)
-    wr = torch.empty(lsh.workspace_bytes(prob, _lib.LSH_WS_REHASH), dtype=torch.uint8, device="cuda")
-    dq2, dv2 = torch.empty_like(q), torch.empty_like(v)
-    lsh.lsh_attn_bwd_rehash(prob, q, v, rot, mod.out, do, mod.lse, dq2, dv2, wr)
-    torch.cuda.synchronize()
-    bits = (lambda t: t.view(torch.int16)) if cfg.dtype == "bf16" else (lambda t: t.view(torch.int32))
-    for a, b in ((dq, dq_s), (dv, dv_s), (dq2, dq_s), (dv2, dv_s)):
-        assert torch.equal(bits(a), bits(b))
+    res = gu.run_gpu_backward_entries(x)
+    gu.compare_backward_entries(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
 
 
 def test_empty_problem_is_a_no_op():
