@@ -40,7 +40,7 @@ WORKLOAD_NAMES = {
 # source file of each kernel on the bf16 matrix-core path, for matching stored
 # counter measurements to the code they were taken on
 KERNEL_SOURCE = {
-    "hash": "hash.hip", "sort_hist": "sort.hip", "sort_scan": "sort.hip", "sort_scatter": "sort.hip",
+    "hash": "hash.hip", "sort_count": "sort.hip", "sort_scatter": "sort.hip",
     "prep": "attn_generic.hip", "tiles": "attn_mfma.hip", "attn_fwd": "attn_mfma.hip",
     "combine": "attn_generic.hip", "bwd_dq": "attn_mfma.hip", "bwd_dkv": "attn_mfma.hip",
     "bwd_reduce": "attn_mfma.hip",
@@ -64,17 +64,16 @@ def algorithmic_work(name: str, cfg, backward_prep: bool = True) -> tuple[float,
     T = B * H * L
     Tr = T * nh
     S = B * H * nh
-    ntiles = -(-L // 2048)
+    ntiles = -(-L // 4096)                          # sort tiles per segment
+    cnt_bytes = S * ntiles * nb * 2                 # 16-bit per-tile bucket counts
     pairs = (2.0 * m * L - m * m) * B * H * nh      # query-key pairs of the dense chunk tiles
     meta = 4 * nh                                   # one packed record per round
     if name == "hash":
         return 2.0 * T * nh * (nb // 2) * d, T * d * s + nh * d * (nb // 2) * s + Tr * 4
-    if name == "sort_hist":
-        return 0.0, Tr * 4 + S * ntiles * nb * 4
-    if name == "sort_scan":
-        return 0.0, 4 * S * ntiles * nb * 4 + S * nb * 4
-    if name == "sort_scatter":
-        return 0.0, Tr * 4 + S * ntiles * nb * 4 + Tr * 12
+    if name == "sort_count":     # bucket ids in, per-tile counts out
+        return 0.0, Tr * 4 + cnt_bytes
+    if name == "sort_scatter":   # bucket ids in (again), the segment's counts, perm / inv / win_lo out
+        return 0.0, Tr * 4 + cnt_bytes + Tr * 12
     qtile_row = ((320 + 128 * (nh - 1) + 255) & ~255) // 32   # stored query-tile bytes per sorted row
     ktile_row = ((128 + 64 * (nh - 1) + 255) & ~255) // 32    # stored key-tile bytes per sorted row
     if name == "prep":
@@ -303,8 +302,9 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+def stored_traffic(kernel: str, workload: str, key: str = "bytes_per_launch"):
+    """Bytes per launch from committed rocprofv3 counter runs (key "bytes_per_launch": calibrated
+    FETCH_SIZE/WRITE_SIZE; "dram_bytes_per_launch": DRAM read and write requests), if they were
     taken on the current source of the kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -314,7 +314,19 @@ def stored_traffic(kernel: str, workload: str):
     rec = table.get(f"{kernel}@{workload}")
     if not rec or rec.get("source_sha") != source_sha(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(key)
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(x, heads: int):
@@ -327,7 +339,7 @@ def cpu_baseline(x, heads: int):
     dt = time.perf_counter() - t0
     tokens = cfg.seq_len * heads / cfg.heads      # the work of all heads of that many tokens
     return {
-        "value": tokens / dt, "unit": "tokens/s", "cores": ora.threads(), "kind": "oracle",
+        "value": tokens / dt, "unit": "tokens/s", "cores": ora.threads(), "cpu_model": cpu_model(), "kind": "oracle",
         "sample": (f"batch 0, heads 0..{heads - 1} of {cfg.heads} at full L={cfg.seq_len}: hash, sort, "
                    f"forward and backward in fp64; {dt:.1f} s; tokens counted as L*{heads}/{cfg.heads}"),
     }
@@ -401,6 +413,9 @@ def main() -> int:
                          "step's launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three device copies of 1 GiB (reference point for HBM byte counters)")
+    ap.add_argument("--workloads", default="tiny,mid,image,stress",
+                    help="other workloads measured after the main one, each with its own line under "
+                         "'workloads' (empty: none)")
     ap.add_argument("--ff-only", action="store_true",
                     help="instead of the bench line: only the chunked feed-forward step (variants.chunked_ff) "
                          "over the workload's B * L rows")
@@ -437,97 +452,27 @@ def main() -> int:
     t0 = time.perf_counter()
     x = gen.generate(cfg, with_grad=True)
     print(f"[bench] generated {cfg.name} inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-
-    def dev(a):
-        import numpy as np
-        a = np.ascontiguousarray(a)
-        if cfg.dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    q, v, rot, do = dev(x["q"]), dev(x["v"]), dev(x["rot"]), dev(x["dout"])
-    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
-                       cfg.chunk_len, cfg.scale, cfg.dtype)
-    mod = lsh.LshAttention(prob)
-    L = _lib.lib()
     hip = Hip()
-    nk = len(_lib.KERNELS)
-
-    def step():
-        mod.forward(q, v, rot)
-        mod.backward(q, v, do)
-
-    for _ in range(max(0, args.warmup - 1)):
-        step()
-    torch.cuda.synchronize()
-    # last warmup step: every kernel bracketed, to find the dominant one
-    evs = [(hip.event(), hip.event()) for _ in range(nk)]
-    for k, (a, b) in enumerate(evs):
-        L.lsh_profile_kernel(k, a, b)
-    step()
-    torch.cuda.synchronize()
-    per_kernel = {}
-    for k, (a, b) in enumerate(evs):
-        ms = hip.elapsed_ms(a, b, missing_ok=True)   # kernels the problem does not launch are left out
-        if ms is not None:
-            per_kernel[_lib.KERNELS[k]] = ms * 1e3
-        L.lsh_profile_kernel(k, None, None)
-    dominant = max(per_kernel, key=per_kernel.get)
-    dk = _lib.KERNELS.index(dominant)
-
-    # timed region: K steps, the dominant kernel bracketed by HIP events on
-    # the stream it is launched on (the current torch stream)
-    pairs = [(hip.event(), hip.event()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in pairs:
-        L.lsh_profile_kernel(dk, a, b)
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    L.lsh_profile_kernel(dk, None, None)
-    kern_ms = sum(hip.elapsed_ms(a, b) for a, b in pairs) / len(pairs)
-    for a, b in pairs + evs:
-        hip.destroy(a)
-        hip.destroy(b)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = cfg.batch * cfg.seq_len * args.steps / elapsed
-    flops, nbytes = algorithmic_work(dominant, cfg)
-    t_mfma = flops / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
-    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    if t_mfma > t_hbm:
-        roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[cfg.dtype],
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(dominant, cfg.name)
-    roof["kernel"] = dominant
-    roof["kernel_us"] = kern_ms * 1e3
-    roof["algorithmic"] = {"flops": flops, "bytes": nbytes}
-    if roof["bound"] == "hbm":
-        # the measured denominator beside the spec one: a plain 1 GiB device copy
-        roof["copy_gbs"] = copy_bandwidth_gbs()
-        roof["frac_of_copy"] = roof["achieved"] / roof["copy_gbs"]
-
+    gtf = gemm_tflops() if cfg.dtype == "bf16" else None   # the GEMM reference rate is a bf16 one
+    main_run = measure_workload(x, args.steps, args.warmup, hip, gtf, keep=True)
+    mod, (q, v, rot, do) = main_run.pop("_mod"), main_run.pop("_tensors")
+    prob = mod.prob
     result = {
-        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": main_run["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_run["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES.get(cfg.name, cfg.name), "name": cfg.name, "batch": cfg.batch,
-                   "heads": cfg.heads, "seq_len": cfg.seq_len, "head_dim": cfg.head_dim,
-                   "n_buckets": cfg.n_buckets, "n_hashes": cfg.n_hashes, "chunk_len": cfg.chunk_len,
-                   "causal": True, "clustered_inputs": cfg.clustered},
-        "roofline": roof,
-        "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "config": main_run["config"],
+        "roofline": main_run["roofline"],
+        "kernels_us": main_run["kernels_us"],
         "variants": None,
     }
-    gtf = None
-    if cfg.dtype == "bf16":   # the GEMM reference rate is a bf16 one
-        gtf = gemm_tflops()
+    if gtf is not None:
         result["gemm_tflops"] = gtf
-    result["kernels"] = kernel_rooflines(per_kernel, cfg, gtf)
+    result["kernels"] = main_run["kernels"]
+    if result["roofline"]["bound"] == "hbm":
+        # the measured denominator beside the spec one: a plain 1 GiB device copy
+        result["roofline"]["copy_gbs"] = copy_bandwidth_gbs()
+        result["roofline"]["frac_of_copy"] = result["roofline"]["achieved"] / result["roofline"]["copy_gbs"]
     if not args.no_variants:
         result["variants"] = {"rehash_backward": rehash_variant(prob, mod, q, v, rot, do, args.steps, cfg)}
     del mod
@@ -541,14 +486,138 @@ def main() -> int:
         if "gemm_tflops" in result:
             ff = result["variants"]["chunked_ff"]
             ff["frac_of_gemm"] = ff["tflops"] / result["gemm_tflops"]
+    del q, v, rot, do
     torch.cuda.empty_cache()
     if args.cpu_heads > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(x, args.cpu_heads)
     else:
         result["cpu_baseline"] = None
+    del x
+    # the other workloads, each its own full training step on its own inputs (parity cases of the
+    # tests; reported here for their throughput and the roofline of their dominant kernel)
+    others = [w for w in (args.workloads.split(",") if args.workloads else []) if w and w != cfg.name]
+    if others:
+        result["workloads"] = {}
+    for name in others:
+        t0 = time.perf_counter()
+        xw = gen.generate(gen.CONFIGS[name], with_grad=True)
+        print(f"[bench] workload {name}: inputs in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+        wr = measure_workload(xw, args.steps, args.warmup, hip, gtf)
+        result["workloads"][name] = {k: wr[k] for k in ("config", "ms_per_step", "value", "unit", "roofline",
+                                                        "kernels")}
+        del xw
+        torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
     return 0
+
+
+def measure_workload(x, steps: int, warmup: int, hip, gtf, keep: bool = False) -> dict:
+    """One workload's training step (forward + saved-records backward) on its seeded inputs.
+
+    1. warmup - 1 untimed steps;
+    2. a profiled pass of min(steps, 10) steps with every kernel bracketed by HIP events in every
+       step: the per-kernel table (average launch duration over those steps; prep and tiles
+       launch twice per step and their bracket holds the backward's launch);
+    3. the timed region: `steps` steps, wall clock around them (synchronised on both sides), with
+       only the dominant kernel bracketed by HIP events on the stream it is launched on (the
+       current torch stream); its average launch duration over the timed steps gives the roofline.
+    """
+    import numpy as np
+    import torch
+    import lsh_sparse_attention_amd as lsh
+    from lsh_sparse_attention_amd import _lib
+    cfg = x["cfg"]
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, v, rot, do = dev(x["q"]), dev(x["v"]), dev(x["rot"]), dev(x["dout"])
+    prob = lsh.problem(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.n_hashes, cfg.n_buckets,
+                       cfg.chunk_len, cfg.scale, cfg.dtype)
+    mod = lsh.LshAttention(prob)
+    L = _lib.lib()
+    nk = len(_lib.KERNELS)
+
+    def step():
+        mod.forward(q, v, rot)
+        mod.backward(q, v, do)
+
+    for _ in range(max(1, warmup - 1)):
+        step()
+    torch.cuda.synchronize()
+    # profiled pass: every kernel bracketed in every step
+    nprof = max(1, min(steps, 10))
+    sums, counts = [0.0] * nk, [0] * nk
+    for _ in range(nprof):
+        evs = [(hip.event(), hip.event()) for _ in range(nk)]
+        for k, (a, b) in enumerate(evs):
+            L.lsh_profile_kernel(k, a, b)
+        step()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(evs):
+            ms = hip.elapsed_ms(a, b, missing_ok=True)   # kernels the problem does not launch are left out
+            if ms is not None:
+                sums[k] += ms * 1e3
+                counts[k] += 1
+            L.lsh_profile_kernel(k, None, None)
+            hip.destroy(a)
+            hip.destroy(b)
+    per_kernel = {_lib.KERNELS[k]: sums[k] / counts[k] for k in range(nk) if counts[k]}
+    dominant = max(per_kernel, key=per_kernel.get)
+    dk = _lib.KERNELS.index(dominant)
+
+    # timed region: K steps, the dominant kernel bracketed on the current torch stream
+    pairs = [(hip.event(), hip.event()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        L.lsh_profile_kernel(dk, a, b)
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    L.lsh_profile_kernel(dk, None, None)
+    kern_ms = sum(hip.elapsed_ms(a, b) for a, b in pairs) / len(pairs)
+    for a, b in pairs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    flops, nbytes = algorithmic_work(dominant, cfg)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma > t_hbm:
+        roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": MFMA_PEAK_TFLOPS[cfg.dtype],
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(dominant, cfg.name)
+    roof["dram_traffic"] = stored_traffic(dominant, cfg.name, key="dram_bytes_per_launch")
+    roof["kernel"] = dominant
+    roof["kernel_us"] = kern_ms * 1e3                     # timed region, this kernel's events
+    roof["kernel_us_profiled_pass"] = per_kernel[dominant]  # the per-kernel table's figure
+    roof["algorithmic"] = {"flops": flops, "bytes": nbytes}
+    if flops:
+        roof["mfma_frac_nominal"] = flops / (kern_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[cfg.dtype]
+    out = {
+        "config": {"workload": WORKLOAD_NAMES.get(cfg.name, cfg.name), "name": cfg.name, "batch": cfg.batch,
+                   "heads": cfg.heads, "seq_len": cfg.seq_len, "head_dim": cfg.head_dim,
+                   "n_buckets": cfg.n_buckets, "n_hashes": cfg.n_hashes, "chunk_len": cfg.chunk_len,
+                   "causal": True, "clustered_inputs": cfg.clustered, "dtype": cfg.dtype},
+        "ms_per_step": elapsed * 1e3 / steps,
+        "value": cfg.batch * cfg.seq_len * steps / elapsed, "unit": "tokens/s",
+        "roofline": roof,
+        "kernels_us": {k: round(u, 2) for k, u in per_kernel.items()},
+        "kernels": kernel_rooflines(per_kernel, cfg, gtf),
+    }
+    if keep:
+        out["_mod"], out["_tensors"] = mod, (q, v, rot, do)
+    else:
+        del mod, q, v, rot, do
+    return out
 
 
 if __name__ == "__main__":

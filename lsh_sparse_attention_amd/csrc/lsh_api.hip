@@ -12,8 +12,8 @@ hipEvent_t g_prof_start[LSH_KERNEL_COUNT];
 hipEvent_t g_prof_stop[LSH_KERNEL_COUNT];
 
 const char *const kKernelNames[LSH_KERNEL_COUNT] = {
-    "hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq", "bwd_dkv",
-    "bwd_reduce", "tiles"};
+    "hash", "sort_count", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq", "bwd_dkv", "bwd_reduce",
+    "tiles"};
 
 }  // namespace
 
@@ -116,7 +116,7 @@ FwdWs fwd_layout(const Dims &P, void *base)
     return w;
 }
 
-BwdWs bwd_layout(const Dims &P, void *base)
+BwdWs bwd_layout(const Dims &P, int dtype, void *base)
 {
     const size_t tok = (size_t)P.BH() * P.L, rnd = tok * P.nh, part = rnd * P.d * sizeof(float);
     const uintptr_t b = (uintptr_t)base;
@@ -125,10 +125,17 @@ BwdWs bwd_layout(const Dims &P, void *base)
     // up to here the same offsets as the forward's workspace, so that a
     // backward can take over the forward's records
     w.D = (float *)(b + o); o += align_up(tok * 4, 256);
-    w.dq_part = (float *)(b + o); o += align_up(part, 256);
-    w.dk_part = (float *)(b + o); o += align_up(part, 256);
-    w.dv_part = (float *)(b + o); o += align_up(part, 256);
-    w.qtile = (uint8_t *)(b + o); o += align_up(mfma_qtile_bytes(P), 256);
+    w.dq_part = (float *)(b + o);
+    if (mfma_path_ok(P, dtype)) {
+        // bf16 partials, the three rows of a (token, round) side by side, and the query tiles
+        o += align_up(bwd_mfma_part_bytes(P), 256);
+        w.qtile = (uint8_t *)(b + o); o += align_up(mfma_qtile_bytes(P), 256);
+    } else {
+        // fp32 partials of the per-query kernels
+        o += align_up(part, 256);
+        w.dk_part = (float *)(b + o); o += align_up(part, 256);
+        w.dv_part = (float *)(b + o); o += align_up(part, 256);
+    }
     w.bytes = o;
     return w;
 }
@@ -144,14 +151,14 @@ struct RehashWs {
     size_t bytes;
 };
 
-RehashWs rehash_layout(const Dims &P, void *base)
+RehashWs rehash_layout(const Dims &P, int dtype, void *base)
 {
     const size_t rnd = (size_t)P.BH() * P.nh * P.L;
     const uintptr_t b = (uintptr_t)base;
     RehashWs w{};
     size_t o = 0;
     w.bwd = (void *)(b + o);
-    w.bwd_bytes = bwd_layout(P, nullptr).bytes;
+    w.bwd_bytes = bwd_layout(P, dtype, nullptr).bytes;
     o += align_up(w.bwd_bytes, 256);
     w.buckets = (int32_t *)(b + o); o += align_up(rnd * 4, 256);
     w.perm = (int32_t *)(b + o); o += align_up(rnd * 4, 256);
@@ -184,7 +191,7 @@ int attn_bwd(const lsh_problem_t *prob, const void *q, const void *v, const void
     const Dims P = dims_of(prob);
     if (!bwd_args_ok(q, v, out, dout, lse, dq, dv) || !ws || ((uintptr_t)ws & 255u))
         return LSH_ERR_INVALID;
-    const BwdWs w = bwd_layout(P, ws);
+    const BwdWs w = bwd_layout(P, prob->dtype, ws);
     if (ws_bytes < w.bytes)
         return LSH_ERR_INVALID;
     const bool derive = perm != nullptr;
@@ -218,7 +225,7 @@ const char *lsh_status_string(int status)
     }
 }
 
-int lsh_version(void) { return 500; }
+int lsh_version(void) { return 600; }
 
 const char *lsh_kernel_name(int kernel)
 {
@@ -247,8 +254,8 @@ size_t lsh_workspace_bytes(const lsh_problem_t *prob, int kind)
     case LSH_WS_SORT: return sort_ws_bytes(P);
     case LSH_WS_FWD: return fwd_layout(P, nullptr).bytes;
     case LSH_WS_BWD:
-    case LSH_WS_TRAIN: return bwd_layout(P, nullptr).bytes;
-    case LSH_WS_REHASH: return rehash_layout(P, nullptr).bytes;
+    case LSH_WS_TRAIN: return bwd_layout(P, prob->dtype, nullptr).bytes;
+    case LSH_WS_REHASH: return rehash_layout(P, prob->dtype, nullptr).bytes;
     default: return 0;
     }
 }
@@ -336,7 +343,7 @@ int lsh_attn_bwd_rehash(const lsh_problem_t *prob, const void *q, const void *v,
     // every argument is checked before the hash and sort are launched
     if (!rot || !aligned16(rot) || !bwd_args_ok(q, v, out, dout, lse, dq, dv) || !ws || ((uintptr_t)ws & 255u))
         return LSH_ERR_INVALID;
-    const RehashWs w = rehash_layout(P, ws);
+    const RehashWs w = rehash_layout(P, prob->dtype, ws);
     if (ws_bytes < w.bytes)
         return LSH_ERR_INVALID;
     hipStream_t s = (hipStream_t)stream;
