@@ -12,7 +12,10 @@
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers to contiguous row-major arrays,
  *     owned by the caller, at least 16-byte aligned.  The library allocates
- *     nothing, frees nothing and keeps no state between calls.
+ *     nothing and frees nothing; the results of a call depend on its
+ *     arguments only.  The one process-wide setting is the instrumentation
+ *     bracket of lsh_profile_kernel (HIP events recorded around launches; it
+ *     changes no result).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and nothing synchronises with the host.  Outputs are valid once the
  *     stream reaches that point.
@@ -153,8 +156,9 @@ int lsh_hash(const lsh_problem_t *prob, const void *q, const void *rot, int32_t 
  *           with LSH_FLAG_NO_BUCKET_MASK, whose sets the attention calls
  *           take from the chunks alone).
  *   ws      workspace of lsh_workspace_bytes(prob, LSH_WS_SORT) bytes.
- * Bucket values outside [0, nb) are undefined behaviour (not checked on the
- * device).
+ * Bucket values outside [0, nb) are not reported: the kernels clamp them into
+ * [0, nb), so the outputs are then meaningless but every write stays inside
+ * perm, inv, win_lo and the workspace.
  */
 int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, int32_t *inv,
              int32_t *win_lo, void *ws, size_t ws_bytes, void *stream);
@@ -304,21 +308,22 @@ int lsh_ff_bwd(const lsh_ff_t *ff, const void *x, const void *w1, const float *b
  */
 typedef enum {
     LSH_KERNEL_HASH = 0,        /* lsh_hash: rotation + argmax                      */
-    LSH_KERNEL_SORT_HIST = 1,   /* lsh_sort: per-tile bucket counts                 */
-    LSH_KERNEL_SORT_SCAN = 2,   /* lsh_sort: offsets of (tile, bucket) runs         */
-    LSH_KERNEL_SORT_SCATTER = 3,/* lsh_sort: stable ranks, perm / inv / win_lo      */
-    LSH_KERNEL_PREP = 4,        /* lsh_attn_fwd / lsh_attn_bwd: packed records,
+    LSH_KERNEL_SORT_COUNT = 1,  /* lsh_sort: per-tile bucket counts                 */
+    LSH_KERNEL_SORT_SCATTER = 2,/* lsh_sort: bucket starts and earlier-tile counts
+                                   from the count matrix, stable ranks,
+                                   perm / inv / win_lo                            */
+    LSH_KERNEL_PREP = 3,        /* lsh_attn_fwd / lsh_attn_bwd: packed records,
                                    inverse norms, non-causal window ends (and
                                    dO . O in the backward; only that in
                                    lsh_attn_bwd_saved)                             */
-    LSH_KERNEL_FWD = 5,         /* lsh_attn_fwd: per-round chunk attention          */
-    LSH_KERNEL_COMBINE = 6,     /* lsh_combine                                      */
-    LSH_KERNEL_BWD_DQ = 7,      /* lsh_attn_bwd: query-side gradient per round      */
-    LSH_KERNEL_BWD_DKV = 8,     /* lsh_attn_bwd: key-side gradients per round       */
-    LSH_KERNEL_BWD_REDUCE = 9,  /* lsh_attn_bwd: sum over rounds, key normalisation */
-    LSH_KERNEL_TILES = 10,      /* lsh_attn_fwd / lsh_attn_bwd (bf16 matrix-core
+    LSH_KERNEL_FWD = 4,         /* lsh_attn_fwd: per-round chunk attention          */
+    LSH_KERNEL_COMBINE = 5,     /* lsh_combine                                      */
+    LSH_KERNEL_BWD_DQ = 6,      /* lsh_attn_bwd: query-side gradient per round      */
+    LSH_KERNEL_BWD_DKV = 7,     /* lsh_attn_bwd: key-side gradients per round       */
+    LSH_KERNEL_BWD_REDUCE = 8,  /* lsh_attn_bwd: sum over rounds, key normalisation */
+    LSH_KERNEL_TILES = 9,       /* lsh_attn_fwd / lsh_attn_bwd (bf16 matrix-core
                                    path): per-32-row metadata tiles             */
-    LSH_KERNEL_COUNT = 11
+    LSH_KERNEL_COUNT = 10
 } lsh_kernel_t;
 
 /* Name of a kernel id (static storage), or NULL for an unknown id. */

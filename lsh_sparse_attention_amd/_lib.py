@@ -15,8 +15,8 @@ SYMBOLS = ("lsh_status_string", "lsh_version", "lsh_workspace_bytes", "lsh_hash"
            "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash",
            "lsh_kernel_name", "lsh_profile_kernel", "lsh_ff_workspace_bytes", "lsh_ff_fwd", "lsh_ff_bwd")
 
-KERNELS = ("hash", "sort_hist", "sort_scan", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq",
-           "bwd_dkv", "bwd_reduce", "tiles")
+KERNELS = ("hash", "sort_count", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq", "bwd_dkv",
+           "bwd_reduce", "tiles")
 
 LSH_OK, LSH_ERR_INVALID, LSH_ERR_UNSUPPORTED, LSH_ERR_HIP = 0, 1, 2, 3
 LSH_F32, LSH_BF16 = 0, 1

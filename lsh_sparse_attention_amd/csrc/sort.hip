@@ -2,177 +2,206 @@
 // "Reformer: The Efficient Transformer", §2: sorting by bucket (positions
 // carried along) clusters same-bucket pairs; ties keep position order.
 //
-// Three launches over S = B*H*nh segments of L positions, tiles of kTile:
-//   sort_hist    per (tile, segment): bucket counts of the tile   -> cnt[S][T][nb]
-//   sort_scan    per segment: cnt becomes the first sorted index of each
-//                (tile, bucket) run; bstart = first sorted index of each bucket
-//   sort_scatter per (tile, segment): stable rank inside the tile, then
-//                perm / inv / win_lo.
+// Two launches over S = B*H*nh segments of L positions, in tiles of kTile
+// positions (one workgroup per (segment, tile)):
+//   sort_count    the tile's bucket counts, as 16-bit values -> cnt[S][T][nb]
+//   sort_scatter  reads its segment's whole count matrix (a few tens of KB,
+//                 from L2: all tiles of a segment run on one XCD) and forms
+//                 from it both the bucket totals (their exclusive scan gives
+//                 each bucket's first sorted index) and the counts of the
+//                 earlier tiles; then ranks its positions stably and writes
+//                 perm / inv / win_lo.
+// No pass is serial over a segment, nothing needs zeroing between calls, and
+// each segment's count matrix is re-read by its T tiles instead of being
+// scanned once by a single workgroup.
 #include "common.hpp"
 
 namespace lsh {
 namespace {
 
-constexpr int kTile = 2048;
-constexpr int kScatterThreads = 256;                      // 4 waves
-constexpr int kWavePositions = kTile / (kScatterThreads / kWave);  // 512 per wave
-constexpr int kScanThreads = 1024;
+constexpr int kTile = 4096;                                 // positions per workgroup
+constexpr int kThreads = 256;                               // 4 waves
+constexpr int kWaves = kThreads / kWave;
+constexpr int kWavePositions = kTile / kWaves;              // 1024 per wave
+constexpr int kGroups = kWavePositions / kWave;             // 16 groups of 64 per wave
 constexpr int kMaxBuckets = 4096;
+static_assert(kTile <= 65535, "tile counts are stored in 16 bits");
 
-__global__ __launch_bounds__(kScatterThreads) void sort_hist(int L, int nb, int ntiles,
-                                                             const int32_t *__restrict__ buckets,
-                                                             int32_t *__restrict__ cnt)
+// The tile's positions as the waves walk them: wave w owns the w-th quarter,
+// group g of it the 64 positions from g * 64.
+__device__ __forceinline__ int tile_pos(int tile, int wave, int g, int lane)
 {
-    extern __shared__ int32_t h[];
-    const int tile = blockIdx.x, seg = blockIdx.y, tid = threadIdx.x;
-    for (int b = tid; b < nb; b += kScatterThreads)
-        h[b] = 0;
-    __syncthreads();
-    const int32_t *bk = buckets + (size_t)seg * L;
-    const int base = tile * kTile;
-    for (int k = tid; k < kTile; k += kScatterThreads) {
-        int t = base + k;
-        if (t < L)
-            atomicAdd(&h[bk[t]], 1);
-    }
-    __syncthreads();
-    int32_t *out = cnt + ((size_t)seg * ntiles + tile) * nb;
-    for (int b = tid; b < nb; b += kScatterThreads)
-        out[b] = h[b];
+    return tile * kTile + wave * kWavePositions + g * kWave + lane;
 }
 
-// Exclusive scan of the nb bucket totals inside one block (nb <= 4 * 1024).
-__device__ void block_exclusive_scan(int32_t *vals, int nb, int32_t *tmp)
+// A bucket id as both kernels use it: clamped into [0, nb), so that ids
+// outside the range (undefined behaviour by the contract) still give in-range
+// sorted indices, consistently in both kernels.
+__device__ __forceinline__ int clamp_bucket(int32_t b, int nb) { return b < 0 ? 0 : (b >= nb ? nb - 1 : b); }
+
+__global__ __launch_bounds__(kThreads) void sort_count(int L, int nb, int ntiles, const int32_t *__restrict__ buckets,
+                                                       uint32_t *__restrict__ cnt)
 {
-    const int tid = threadIdx.x;
-    constexpr int per = kMaxBuckets / kScanThreads;  // 4
-    int32_t loc[per];
-    int32_t sum = 0;
+    extern __shared__ uint32_t h[];   // [nb]
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int tile = lb % ntiles, seg = lb / ntiles, tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int32_t *bk = buckets + (size_t)seg * L;
+    int32_t x[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        const int t = tile_pos(tile, wave, g, lane);
+        x[g] = t < L ? clamp_bucket(bk[t], nb) : -1;
+    }
+    for (int b = tid; b < nb; b += kThreads)
+        h[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+        if (x[g] >= 0)
+            atomicAdd(&h[x[g]], 1u);
+    __syncthreads();
+    // two 16-bit counts per word (nb is even)
+    uint32_t *out = cnt + ((size_t)seg * ntiles + tile) * (nb / 2);
+    for (int p = tid; p < nb / 2; p += kThreads)
+        out[p] = h[2 * p] | (h[2 * p + 1] << 16);
+}
+
+// Exclusive scan of v[0 .. n) in LDS (n <= kMaxBuckets), in place; ends with
+// a workgroup barrier.
+__device__ void block_exclusive_scan(uint32_t *v, int n, uint32_t *wsum)
+{
+    constexpr int per = kMaxBuckets / kThreads;   // 16 consecutive entries per thread
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    uint32_t loc[per];
+    uint32_t sum = 0;
 #pragma unroll
     for (int k = 0; k < per; ++k) {
-        int b = tid * per + k;
-        loc[k] = b < nb ? vals[b] : 0;
+        const int i = tid * per + k;
+        loc[k] = i < n ? v[i] : 0u;
         sum += loc[k];
     }
-    tmp[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        int32_t add = tid >= off ? tmp[tid - off] : 0;
-        __syncthreads();
-        tmp[tid] += add;
-        __syncthreads();
+    // inclusive scan of the thread sums within the wave, then across the waves
+    uint32_t inc = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o, kWave);
+        if (lane >= o)
+            inc += y;
     }
-    int32_t run = tmp[tid] - sum;  // exclusive prefix of this thread's group
+    if (lane == kWave - 1)
+        wsum[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum;
+    for (int w = 0; w < wave; ++w)
+        run += wsum[w];
 #pragma unroll
     for (int k = 0; k < per; ++k) {
-        int b = tid * per + k;
-        if (b < nb)
-            vals[b] = run;
+        const int i = tid * per + k;
+        if (i < n)
+            v[i] = run;
         run += loc[k];
     }
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kScanThreads) void sort_scan(int nb, int ntiles, int32_t *__restrict__ cnt,
-                                                          int32_t *__restrict__ bstart)
+__global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbits, int m, int ntiles,
+                                                         const int32_t *__restrict__ buckets,
+                                                         const uint32_t *__restrict__ cnt,
+                                                         int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                                                         int32_t *__restrict__ win_lo)
 {
-    __shared__ int32_t tot[kMaxBuckets];
-    __shared__ int32_t tmp[kScanThreads];
-    const int seg = blockIdx.x, tid = threadIdx.x;
-    int32_t *c = cnt + (size_t)seg * ntiles * nb;
-    // per bucket: exclusive prefix over tiles, and the bucket total
-    for (int b = tid; b < nb; b += kScanThreads) {
-        int32_t run = 0;
-        for (int t = 0; t < ntiles; ++t) {
-            int32_t x = c[(size_t)t * nb + b];
-            c[(size_t)t * nb + b] = run;
-            run += x;
-        }
-        tot[b] = run;
-    }
-    __syncthreads();
-    block_exclusive_scan(tot, nb, tmp);
-    for (int b = tid; b < nb; b += kScanThreads) {
-        int32_t s = tot[b];
-        bstart[(size_t)seg * nb + b] = s;
-        for (int t = 0; t < ntiles; ++t)
-            c[(size_t)t * nb + b] += s;
-    }
-}
-
-__global__ __launch_bounds__(kScatterThreads) void sort_scatter(int L, int nb, int nbits, int m, int ntiles,
-                                                                const int32_t *__restrict__ buckets,
-                                                                const int32_t *__restrict__ off,
-                                                                const int32_t *__restrict__ bstart,
-                                                                int32_t *__restrict__ perm,
-                                                                int32_t *__restrict__ inv,
-                                                                int32_t *__restrict__ win_lo)
-{
-    extern __shared__ int32_t wcnt[];  // [4][nb]
+    // LDS: bstart[nb] (bucket totals, then the first sorted index of each
+    // bucket), pre[nb] (counts of the earlier tiles), wcnt[kWaves][nb]
+    // (per-wave counts, then each wave's next sorted index per bucket)
+    extern __shared__ uint32_t lds[];
+    __shared__ uint32_t wsum[kWaves];
+    uint32_t *bstart = lds, *pre = lds + nb, *wcnt = lds + 2 * nb;
     // all tiles of a segment on one XCD: their scattered 4-byte writes into
     // the segment's sorted order then meet in one L2, which merges them into
-    // whole lines before they go to memory
+    // whole lines before they go to memory, and the segment's count matrix
+    // is read from that L2 by all of them
     const int lb = xcd_block(blockIdx.x, gridDim.x);
     const int tile = lb % ntiles, seg = lb / ntiles, tid = threadIdx.x;
     const int wave = tid / kWave, lane = tid % kWave;
-    const int nwaves = kScatterThreads / kWave;
-    for (int k = tid; k < nwaves * nb; k += kScatterThreads)
-        wcnt[k] = 0;
-    __syncthreads();
     const int32_t *bk = buckets + (size_t)seg * L;
-    const int wbase = tile * kTile + wave * kWavePositions;
-    int32_t *mine = wcnt + wave * nb;
-    // 1. counts of each wave's sub-range
-    for (int g = 0; g < kWavePositions; g += kWave) {
-        int t = wbase + g + lane;
-        if (t < L)
-            atomicAdd(&mine[bk[t]], 1);
+    int32_t x[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        const int t = tile_pos(tile, wave, g, lane);
+        x[g] = t < L ? clamp_bucket(bk[t], nb) : -1;
+    }
+    for (int k = tid; k < kWaves * nb; k += kThreads)
+        wcnt[k] = 0u;
+    // 1. the segment's bucket totals, and the counts of the tiles before this one
+    const uint32_t *cs = cnt + (size_t)seg * ntiles * (nb / 2);
+    for (int p = tid; p < nb / 2; p += kThreads) {
+        uint32_t tot_lo = 0u, tot_hi = 0u, pre_lo = 0u, pre_hi = 0u;
+        for (int t = 0; t < ntiles; ++t) {
+            if (t == tile) {
+                pre_lo = tot_lo;
+                pre_hi = tot_hi;
+            }
+            const uint32_t c = cs[(size_t)t * (nb / 2) + p];
+            tot_lo += c & 0xffffu;
+            tot_hi += c >> 16;
+        }
+        bstart[2 * p] = tot_lo;
+        bstart[2 * p + 1] = tot_hi;
+        pre[2 * p] = pre_lo;
+        pre[2 * p + 1] = pre_hi;
     }
     __syncthreads();
-    // 2. first sorted index of each (wave, bucket) run: tile offset plus the
-    //    counts of the earlier waves of this tile
-    const int32_t *toff = off + ((size_t)seg * ntiles + tile) * nb;
-    for (int b = tid; b < nb; b += kScatterThreads) {
-        int32_t run = toff[b];
-        for (int w = 0; w < nwaves; ++w) {
-            int32_t x = wcnt[w * nb + b];
+    // 2. each wave's counts of its quarter of the tile
+    uint32_t *mine = wcnt + wave * nb;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+        if (x[g] >= 0)
+            atomicAdd(&mine[x[g]], 1u);
+    // 3. first sorted index of each bucket (the barrier at its end also
+    //    completes the counts above)
+    block_exclusive_scan(bstart, nb, wsum);
+    // 4. first sorted index of each (wave, bucket) run of this tile
+    for (int b = tid; b < nb; b += kThreads) {
+        uint32_t run = bstart[b] + pre[b];
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t c = wcnt[w * nb + b];
             wcnt[w * nb + b] = run;
-            run += x;
+            run += c;
         }
     }
     __syncthreads();
-    // 3. each wave walks its sub-range in order, 64 positions at a time;
-    //    lanes holding the same bucket are ranked by lane index.
+    // 5. each wave walks its quarter in order, 64 positions at a time; lanes
+    //    holding the same bucket are ranked by lane index (ballots over the
+    //    bucket's bits)
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int32_t *bs = bstart + (size_t)seg * nb;
     int32_t *pr = perm + (size_t)seg * L, *iv = inv + (size_t)seg * L, *wl = win_lo + (size_t)seg * L;
-    for (int g = 0; g < kWavePositions; g += kWave) {
-        const int t = wbase + g + lane;
-        const bool valid = t < L;
-        const int b = valid ? bk[t] : 0;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+        const int t = tile_pos(tile, wave, g, lane);
+        const bool valid = x[g] >= 0;
+        const int b = valid ? x[g] : 0;
         uint64_t peers = __ballot(valid);
+        if (peers == 0ull)
+            break;   // the rest of the wave's quarter is past L
         for (int bit = 0; bit < nbits; ++bit) {
             const bool on = (b >> bit) & 1;
             const uint64_t set = __ballot(valid && on);
             peers &= on ? set : ~set;
         }
         const int rank = __popcll(peers & lt_mask);
-        int32_t s = 0;
+        uint32_t s = 0u;
         if (valid)
-            s = mine[b] + rank;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            s = mine[b] + (uint32_t)rank;
+        wave_lds_sync();
         if (valid && rank == 0)
-            mine[b] = s + __popcll(peers);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            mine[b] = s + (uint32_t)__popcll(peers);
+        wave_lds_sync();
         if (valid) {
             pr[s] = t;
-            iv[t] = s;
-            const int lo_chunk = (s / m - 1) * m;
-            const int lo_bucket = bs[b];
+            iv[t] = (int32_t)s;
+            const int lo_chunk = ((int)s / m - 1) * m;
+            const int lo_bucket = (int)bstart[b];
             wl[t] = lo_bucket > lo_chunk ? lo_bucket : lo_chunk;
         }
     }
@@ -184,41 +213,33 @@ int ntiles_of(const Dims &P) { return (P.L + kTile - 1) / kTile; }
 
 size_t sort_ws_bytes(const Dims &P)
 {
-    size_t S = (size_t)P.BH() * P.nh;
-    return align_up(S * ntiles_of(P) * P.nb * sizeof(int32_t), 256) + align_up(S * P.nb * sizeof(int32_t), 256);
+    const size_t S = (size_t)P.BH() * P.nh;
+    return align_up(S * ntiles_of(P) * (P.nb / 2) * sizeof(uint32_t), 256);
 }
 
 hipError_t launch_sort(const Dims &P, const int32_t *buckets, int32_t *perm, int32_t *inv, int32_t *win_lo,
                        void *ws, hipStream_t st)
 {
-    if (P.nb > kMaxBuckets)
+    if (P.nb > kMaxBuckets || (P.nb & 1) || P.L > 65536)
         return hipErrorInvalidValue;
     const int S = P.BH() * P.nh;
     const int nt = ntiles_of(P);
-    int32_t *cnt = (int32_t *)ws;
-    int32_t *bstart = (int32_t *)((char *)ws + align_up((size_t)S * nt * P.nb * sizeof(int32_t), 256));
+    uint32_t *cnt = (uint32_t *)ws;
     int nbits = 0;
     while ((1 << nbits) < P.nb)
         ++nbits;
-    const size_t lds_hist = (size_t)P.nb * sizeof(int32_t);
+    const unsigned grid = (unsigned)S * (unsigned)nt;
     {
-        ProfScope prof(LSH_KERNEL_SORT_HIST, st);
-        hipLaunchKernelGGL(sort_hist, dim3(nt, S), dim3(kScatterThreads), lds_hist, st, P.L, P.nb, nt, buckets,
-                           cnt);
+        ProfScope prof(LSH_KERNEL_SORT_COUNT, st);
+        hipLaunchKernelGGL(sort_count, dim3(grid), dim3(kThreads), (size_t)P.nb * sizeof(uint32_t), st, P.L, P.nb,
+                           nt, buckets, cnt);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    {
-        ProfScope prof(LSH_KERNEL_SORT_SCAN, st);
-        hipLaunchKernelGGL(sort_scan, dim3(S), dim3(kScanThreads), 0, st, P.nb, nt, cnt, bstart);
-    }
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    const size_t lds_scatter = (size_t)(kScatterThreads / kWave) * P.nb * sizeof(int32_t);
     ProfScope prof(LSH_KERNEL_SORT_SCATTER, st);
-    hipLaunchKernelGGL(sort_scatter, dim3(nt * S), dim3(kScatterThreads), lds_scatter, st, P.L, P.nb, nbits, P.m,
-                       nt, buckets, (const int32_t *)cnt, (const int32_t *)bstart, perm, inv, win_lo);
+    hipLaunchKernelGGL(sort_scatter, dim3(grid), dim3(kThreads), (size_t)(2 + kWaves) * P.nb * sizeof(uint32_t), st,
+                       P.L, P.nb, nbits, P.m, nt, buckets, (const uint32_t *)cnt, perm, inv, win_lo);
     return hipGetLastError();
 }
 
