@@ -190,6 +190,75 @@ __device__ __forceinline__ void round_store(uint32_t (&bk)[2][2], int (&bi)[2][2
     }
 }
 
+// Deferred slot search (full tiles).  Per row (column tile ct) the round's
+// best entry so far is kept as a key and the lane's 16 scores y' = -y of the
+// tile that holds it; the slot inside that tile is searched for once, when
+// the round ends.  Per tile the lane takes the largest +y entry (max of -y')
+// and the largest -y entry (max of y') with three-input maxima; the larger
+// one wins, +y on equal magnitude (it has the lower index).  Its key is
+// (bits of the magnitude << 1) | (1 for +y): keys order entries like
+// [y ; -y] does except for the index, and a strictly larger key replaces the
+// tracked one, so an earlier tile (lower index) wins ties.  Every real key is
+// at least 1 (a -y winner has nonzero magnitude), so the initial 0 is
+// replaced by the first tile.
+__device__ __forceinline__ void tile_track(const f32x16_t (&acc)[2], int j0, uint32_t (&bk)[2], int (&bj)[2],
+                                           f32x16_t (&sv)[2])
+{
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const f32x16_t &a = acc[ct];
+        const float mp = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(-a[0], -a[1]), -a[2]), fmaxf(fmaxf(-a[3], -a[4]), -a[5])),
+                                     fmaxf(fmaxf(fmaxf(-a[6], -a[7]), -a[8]), fmaxf(fmaxf(-a[9], -a[10]), -a[11]))),
+                               fmaxf(fmaxf(fmaxf(-a[12], -a[13]), -a[14]), -a[15]));
+        const float mn = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(a[0], a[1]), a[2]), fmaxf(fmaxf(a[3], a[4]), a[5])),
+                                     fmaxf(fmaxf(fmaxf(a[6], a[7]), a[8]), fmaxf(fmaxf(a[9], a[10]), a[11]))),
+                               fmaxf(fmaxf(fmaxf(a[12], a[13]), a[14]), a[15]));
+        const bool plus = mp >= mn;
+        const uint32_t key = (__float_as_uint(plus ? mp : mn) << 1) | (plus ? 1u : 0u);
+        const bool better = key > bk[ct];
+        bk[ct] = better ? key : bk[ct];
+        bj[ct] = better ? j0 : bj[ct];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            sv[ct][e] = better ? a[e] : sv[ct][e];
+    }
+}
+
+// End of a round under the deferred search: the first slot of the kept tile
+// whose score is the tracked entry (y' = -magnitude for +y, +magnitude for
+// -y; floating equality, so a zero matches either sign), then the merge with
+// the other half of the row (larger key, else smaller column), the store and
+// the reset.
+__device__ __forceinline__ void round_store_tracked(uint32_t (&bk)[2], int (&bj)[2], const f32x16_t (&sv)[2], int h,
+                                                    int c, int row0, int L, int half, int32_t *__restrict__ out)
+{
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const uint32_t k0 = bk[ct];
+        const float mag = __uint_as_float(k0 >> 1);
+        const float want = (k0 & 1u) ? -mag : mag;
+        int slot = 0;
+#pragma unroll
+        for (int e = 15; e >= 0; --e)
+            slot = sv[ct][e] == want ? 8 * (e / 4) + (e % 4) : slot;
+        int i0 = bj[ct] + slot + 4 * h;
+        uint32_t kk = k0;
+        const auto pk = __builtin_amdgcn_permlane32_swap(kk, kk, false, false);
+        const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i0, (uint32_t)i0, false, false);
+        const uint32_t ok = h ? pk[0] : pk[1];
+        const int oi = (int)(h ? pi[0] : pi[1]);
+        if (ok > kk || (ok == kk && oi < i0)) {
+            kk = ok;
+            i0 = oi;
+        }
+        const int row = row0 + 32 * ct + c;
+        if (h == 0 && row < L)
+            out[row] = (kk & 1u) ? i0 : half + i0;
+        bk[ct] = 0u;
+        bj[ct] = 0;
+    }
+}
+
 // A operand of tile jt of a staged block: lane (column 32 jt + c, half h)
 // gets d = 16 ks + 8 h + 0..7, read transposed from the row-major block.
 template <int D, int P>
@@ -366,9 +435,11 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int
                 acc[ct] = mfma32(aop[ks], qop[ct][ks], acc[ct]);
     };
 
-    uint32_t bk[2][2] = {{0u, 0u}, {0u, 0u}};
-    int bi[2][2] = {{0, 0}, {0, 0}};
-    // accumulators of the previous block's last tile; zero keys change nothing
+    uint32_t bk[2] = {0u, 0u};
+    int bj[2] = {0, 0};
+    f32x16_t sv[2] = {f32x16_t{}, f32x16_t{}};
+    // accumulators of the previous block's last tile (none before the first
+    // block: their tracking is skipped there)
     f32x16_t acc0[2], acc1[2] = {f32x16_t{}, f32x16_t{}};
     int prev_j = 0, prev_r = 0;   // first column and round of that tile
     bool prev_last = false;       // it ended its round
@@ -389,18 +460,19 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_pipe_kernel(int L, int
 #pragma unroll
         for (int jt = 0; jt < NT; jt += 2) {
             products(buf, jt, acc0);
-            tile_argmax_full(acc1, jt == 0 ? prev_j : jb + 32 * (jt - 1), bk, bi);
+            if (jt > 0 || blk > 0)
+                tile_track(acc1, jt == 0 ? prev_j : jb + 32 * (jt - 1), bk, bj, sv);
             if (jt == 0 && prev_last)
-                round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
+                round_store_tracked(bk, bj, sv, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
             products(buf, jt + 1, acc1);
-            tile_argmax_full(acc0, jb + 32 * jt, bk, bi);
+            tile_track(acc0, jb + 32 * jt, bk, bj, sv);
         }
         prev_j = jb + COLS - 32;
         prev_r = r;
         prev_last = jb + COLS == half;
     }
-    tile_argmax_full(acc1, prev_j, bk, bi);
-    round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
+    tile_track(acc1, prev_j, bk, bj, sv);
+    round_store_tracked(bk, bj, sv, h, c, row0, L, half, buckets + ((size_t)bh * nh + prev_r) * L);
 }
 
 template <int D>
