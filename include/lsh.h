@@ -164,6 +164,27 @@ int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, i
              int32_t *win_lo, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * lsh_sort_noalloc -- lsh_sort for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments as lsh_sort without
+ * ws / ws_bytes and the same results bit for bit; the per-tile count matrix
+ * (lsh_workspace_bytes(prob, LSH_WS_SORT) bytes) lives instead in a static
+ * device array of the library, LSH_SORT_NOALLOC_MAX_BYTES on every GPU it
+ * runs on, held until the process ends.  The call allocates nothing; its
+ * first call on a GPU looks up that GPU's copy of the array (the GPU of
+ * `stream`, or the current one for the null stream).
+ *   Problems whose count matrix is larger than LSH_SORT_NOALLOC_MAX_BYTES:
+ *   LSH_ERR_UNSUPPORTED, before anything is launched.
+ *   Calls on one GPU share its array, which keeps the last call's counts
+ *   (each call writes every count it reads, so nothing has to start at
+ *   zero): calls that may overlap on one GPU (streams not ordered with each
+ *   other) race and must not be issued.
+ */
+#define LSH_SORT_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+int lsh_sort_noalloc(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, int32_t *inv,
+                     int32_t *win_lo, void *stream);
+
+/*
  * lsh_attn_fwd -- per-round chunked attention ("Reformer" §2 and App. A):
  * in round r, query t attends to the members of its attended set (causal or
  * not, see lsh_problem_t) other than itself, with logits

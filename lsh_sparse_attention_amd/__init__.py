@@ -21,7 +21,8 @@ import torch
 from ._lib import (FF, LSH_BF16, LSH_F32, LSH_FLAG_DUP_BY_BUCKET, LSH_FLAG_NO_BUCKET_MASK, LSH_WS_BWD, LSH_WS_FWD,
                    LSH_WS_REHASH, LSH_WS_SORT, LSH_WS_TRAIN, LshError, Problem, check, lib)
 
-__all__ = ["Problem", "LshError", "problem", "workspace_bytes", "lsh_hash", "lsh_sort", "lsh_attn_fwd",
+__all__ = ["Problem", "LshError", "problem", "workspace_bytes", "lsh_hash", "lsh_sort", "lsh_sort_noalloc",
+           "lsh_attn_fwd",
            "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash", "LshAttention", "FF",
            "ff_problem", "ff_workspace_bytes", "lsh_ff_fwd", "lsh_ff_bwd"]
 
@@ -101,6 +102,16 @@ def lsh_sort(prob, buckets, perm, inv, win_lo, ws, stream=None):
     check("lsh_sort", lib().lsh_sort(ctypes.byref(prob), _ptr(buckets, "buckets", torch.int32),
                                      _ptr(perm, "perm", torch.int32), _ptr(inv, "inv", torch.int32),
                                      _ptr(win_lo, "win_lo", torch.int32), wp, wn, _stream(stream)))
+
+
+def lsh_sort_noalloc(prob, buckets, perm, inv, win_lo, stream=None):
+    """lsh_sort with the library's static scratch instead of a workspace (allocates nothing)."""
+    n = _tok(prob) * prob.n_hashes
+    for t, nm in ((buckets, "buckets"), (perm, "perm"), (inv, "inv"), (win_lo, "win_lo")):
+        _numel_check(t, n, nm)
+    check("lsh_sort_noalloc", lib().lsh_sort_noalloc(
+        ctypes.byref(prob), _ptr(buckets, "buckets", torch.int32), _ptr(perm, "perm", torch.int32),
+        _ptr(inv, "inv", torch.int32), _ptr(win_lo, "win_lo", torch.int32), _stream(stream)))
 
 
 def lsh_attn_fwd(prob, q, v, perm, inv, win_lo, o_rounds, lse_rounds, ws, stream=None):

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "liblsh.so")
 
 # Exported symbols, in header order.
 SYMBOLS = ("lsh_status_string", "lsh_version", "lsh_workspace_bytes", "lsh_hash", "lsh_sort",
-           "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash",
+           "lsh_sort_noalloc", "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved", "lsh_attn_bwd_rehash",
            "lsh_kernel_name", "lsh_profile_kernel", "lsh_ff_workspace_bytes", "lsh_ff_fwd", "lsh_ff_bwd")
 
 KERNELS = ("hash", "sort_count", "sort_scatter", "prep", "attn_fwd", "combine", "bwd_dq", "bwd_dkv",
@@ -22,6 +22,7 @@ LSH_OK, LSH_ERR_INVALID, LSH_ERR_UNSUPPORTED, LSH_ERR_HIP = 0, 1, 2, 3
 LSH_F32, LSH_BF16 = 0, 1
 LSH_WS_SORT, LSH_WS_FWD, LSH_WS_BWD, LSH_WS_TRAIN, LSH_WS_REHASH = 0, 1, 2, 3, 4
 LSH_FLAG_NO_BUCKET_MASK, LSH_FLAG_DUP_BY_BUCKET = 1, 2
+LSH_SORT_NOALLOC_MAX_BYTES = 16 << 20
 
 
 class Problem(ctypes.Structure):
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.lsh_workspace_bytes.argtypes, L.lsh_workspace_bytes.restype = [pp, ctypes.c_int], sz
         L.lsh_hash.argtypes = [pp, vp, vp, i32p, vp]
         L.lsh_sort.argtypes = [pp, i32p, i32p, i32p, i32p, vp, sz, vp]
+        L.lsh_sort_noalloc.argtypes = [pp, i32p, i32p, i32p, i32p, vp]
         L.lsh_attn_fwd.argtypes = [pp, vp, vp, i32p, i32p, i32p, vp, fp, vp, sz, vp]
         L.lsh_combine.argtypes = [pp, vp, vp, vp, fp, vp, fp, vp]
         L.lsh_attn_bwd.argtypes = [pp, vp, vp, vp, vp, fp, i32p, i32p, i32p, vp, vp, vp, sz, vp]
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.lsh_ff_workspace_bytes.argtypes, L.lsh_ff_workspace_bytes.restype = [fp_, ctypes.c_int], sz
         L.lsh_ff_fwd.argtypes = [fp_, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lsh_ff_bwd.argtypes = [fp_, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for name in ("lsh_hash", "lsh_sort", "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved",
+        for name in ("lsh_hash", "lsh_sort", "lsh_sort_noalloc", "lsh_attn_fwd", "lsh_combine", "lsh_attn_bwd", "lsh_attn_bwd_saved",
                      "lsh_attn_bwd_rehash", "lsh_profile_kernel", "lsh_ff_fwd", "lsh_ff_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L

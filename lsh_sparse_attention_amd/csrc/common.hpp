@@ -126,6 +126,12 @@ hipError_t launch_hash(const Dims &, int dtype, const void *q, const void *rot, 
 hipError_t launch_sort(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv,
                        int32_t *win_lo, void *ws, hipStream_t);
 size_t sort_ws_bytes(const Dims &);
+// lsh_sort with its count matrix in the library's static device array (no
+// workspace argument): fails with hipErrorInvalidValue if sort_ws_bytes
+// exceeds sort_noalloc_max_bytes().
+hipError_t launch_sort_noalloc(const Dims &, const int32_t *buckets, int32_t *perm, int32_t *inv, int32_t *win_lo,
+                               hipStream_t);
+size_t sort_noalloc_max_bytes();
 // Window-related records beyond meta and srec, each null where the problem
 // has no use for it: wmeta (kRange / kRangePos window ends), alone and cmin
 // (kRangePos lone flags and their per-chunk scratch), bmeta and bscr

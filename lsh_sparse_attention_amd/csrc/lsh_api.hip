@@ -282,6 +282,21 @@ int lsh_sort(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, i
     return hip_status(launch_sort(P, buckets, perm, inv, win_lo, ws, (hipStream_t)stream));
 }
 
+int lsh_sort_noalloc(const lsh_problem_t *prob, const int32_t *buckets, int32_t *perm, int32_t *inv, int32_t *win_lo,
+                     void *stream)
+{
+    static_assert(LSH_SORT_NOALLOC_MAX_BYTES == (size_t)16 << 20, "header and library agree on the scratch size");
+    int st = validate(prob);
+    if (st != LSH_OK || empty(prob))
+        return st;
+    const Dims P = dims_of(prob);
+    if (!buckets || !perm || !inv || !win_lo)
+        return LSH_ERR_INVALID;
+    if (sort_ws_bytes(P) > sort_noalloc_max_bytes())
+        return LSH_ERR_UNSUPPORTED;
+    return hip_status(launch_sort_noalloc(P, buckets, perm, inv, win_lo, (hipStream_t)stream));
+}
+
 int lsh_attn_fwd(const lsh_problem_t *prob, const void *q, const void *v, const int32_t *perm, const int32_t *inv,
                  const int32_t *win_lo, void *o_rounds, float *lse_rounds, void *ws, size_t ws_bytes, void *stream)
 {

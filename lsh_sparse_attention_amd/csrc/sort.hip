@@ -14,6 +14,8 @@
 // No pass is serial over a segment, nothing needs zeroing between calls, and
 // each segment's count matrix is re-read by its T tiles instead of being
 // scanned once by a single workgroup.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace lsh {
@@ -210,6 +212,70 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
 int ntiles_of(const Dims &P) { return (P.L + kTile - 1) / kTile; }
 
 }  // namespace
+
+// Scratch of lsh_sort_noalloc: the count matrix in a static device array
+// instead of a caller's workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` only names the
+// symbol; its device address, per GPU, comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the GPU that `stream` belongs to (the
+// current GPU for the null stream), looked up once per GPU with that GPU
+// current, then kept.
+hipError_t scratch_address(hipStream_t stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = r;
+        }
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t sort_noalloc_max_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t launch_sort_noalloc(const Dims &P, const int32_t *buckets, int32_t *perm, int32_t *inv, int32_t *win_lo,
+                               hipStream_t st)
+{
+    if (sort_ws_bytes(P) > kNoAllocScratchBytes)
+        return hipErrorInvalidValue;
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(st, &ws);
+    if (e != hipSuccess)
+        return e;
+    return launch_sort(P, buckets, perm, inv, win_lo, ws, st);
+}
 
 size_t sort_ws_bytes(const Dims &P)
 {

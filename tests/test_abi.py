@@ -225,3 +225,23 @@ def test_ff_descriptions_validated_without_launching():
     assert L.lsh_ff_workspace_bytes(ctypes.byref(empty), 1) == 0
     assert L.lsh_ff_bwd(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, None, None,
                         ctypes.c_size_t(0), None) == 0
+
+
+def test_sort_noalloc_arguments_and_limit():
+    # lsh_sort_noalloc validates like lsh_sort and rejects problems whose count
+    # matrix exceeds the static scratch, all before anything is launched
+    L = _lib.lib()
+    ok = ctypes.c_void_p(1 << 20)
+    p = _prob()
+    assert L.lsh_sort_noalloc(ctypes.byref(p), None, ok, ok, ok, None) == _lib.LSH_ERR_INVALID
+    assert L.lsh_sort_noalloc(ctypes.byref(p), ok, ok, None, ok, None) == _lib.LSH_ERR_INVALID
+    assert L.lsh_sort_noalloc(None, ok, ok, ok, ok, None) == _lib.LSH_ERR_INVALID
+    empty = lsh.problem(1, 2, 0, 64, 2, 16, 32, dtype="bf16")
+    assert L.lsh_sort_noalloc(ctypes.byref(empty), None, None, None, None, None) == _lib.LSH_OK
+    # 8 x 16 x 8 segments of 16 tiles x 4096 buckets x 2 bytes = 128 MiB of counts
+    big = lsh.problem(8, 16, 65536, 64, 8, 4096, 128, dtype="bf16")
+    assert L.lsh_workspace_bytes(ctypes.byref(big), _lib.LSH_WS_SORT) > _lib.LSH_SORT_NOALLOC_MAX_BYTES
+    assert L.lsh_sort_noalloc(ctypes.byref(big), ok, ok, ok, ok, None) == _lib.LSH_ERR_UNSUPPORTED
+    # the text-shaped problem fits
+    text = lsh.problem(1, 8, 65536, 128, 4, 1024, 128, dtype="bf16")
+    assert 0 < L.lsh_workspace_bytes(ctypes.byref(text), _lib.LSH_WS_SORT) <= _lib.LSH_SORT_NOALLOC_MAX_BYTES
