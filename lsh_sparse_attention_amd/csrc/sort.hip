@@ -27,6 +27,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kWavePositions = kTile / kWaves;              // 1024 per wave
 constexpr int kGroups = kWavePositions / kWave;             // 16 groups of 64 per wave
 constexpr int kMaxBuckets = 4096;
+constexpr int kMaxTiles = 65536 / kTile;                    // L <= 65536
 static_assert(kTile <= 65535, "tile counts are stored in 16 bits");
 
 // The tile's positions as the waves walk them: wave w owns the w-th quarter,
@@ -107,7 +108,7 @@ __device__ void block_exclusive_scan(uint32_t *v, int n, uint32_t *wsum)
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbits, int m, int ntiles,
+__global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbits, int m, uint64_t mmagic, int ntiles,
                                                          const int32_t *__restrict__ buckets,
                                                          const uint32_t *__restrict__ cnt,
                                                          int32_t *__restrict__ perm, int32_t *__restrict__ inv,
@@ -139,14 +140,19 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
     const uint32_t *cs = cnt + (size_t)seg * ntiles * (nb / 2);
     for (int p = tid; p < nb / 2; p += kThreads) {
         uint32_t tot_lo = 0u, tot_hi = 0u, pre_lo = 0u, pre_hi = 0u;
-        for (int t = 0; t < ntiles; ++t) {
+        // every tile's word requested before any is added (at most kMaxTiles tiles)
+        uint32_t cw[kMaxTiles];
+#pragma unroll
+        for (int t = 0; t < kMaxTiles; ++t)
+            cw[t] = t < ntiles ? cs[(size_t)t * (nb / 2) + p] : 0u;
+#pragma unroll
+        for (int t = 0; t < kMaxTiles; ++t) {
             if (t == tile) {
                 pre_lo = tot_lo;
                 pre_hi = tot_hi;
             }
-            const uint32_t c = cs[(size_t)t * (nb / 2) + p];
-            tot_lo += c & 0xffffu;
-            tot_hi += c >> 16;
+            tot_lo += cw[t] & 0xffffu;
+            tot_hi += cw[t] >> 16;
         }
         bstart[2 * p] = tot_lo;
         bstart[2 * p + 1] = tot_hi;
@@ -202,7 +208,9 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
         if (valid) {
             pr[s] = t;
             iv[t] = (int32_t)s;
-            const int lo_chunk = ((int)s / m - 1) * m;
+            // s / m as a multiply: floor(s * (floor(2^32 / m) + 1) / 2^32) is
+            // exact for s < 2^16 and m <= 2^16
+            const int lo_chunk = ((int)(((uint64_t)s * mmagic) >> 32) - 1) * m;
             const int lo_bucket = (int)bstart[b];
             wl[t] = lo_bucket > lo_chunk ? lo_bucket : lo_chunk;
         }
@@ -305,7 +313,8 @@ hipError_t launch_sort(const Dims &P, const int32_t *buckets, int32_t *perm, int
         return e;
     ProfScope prof(LSH_KERNEL_SORT_SCATTER, st);
     hipLaunchKernelGGL(sort_scatter, dim3(grid), dim3(kThreads), (size_t)(2 + kWaves) * P.nb * sizeof(uint32_t), st,
-                       P.L, P.nb, nbits, P.m, nt, buckets, (const uint32_t *)cnt, perm, inv, win_lo);
+                       P.L, P.nb, nbits, P.m, (uint64_t)(0xffffffffull / (uint64_t)P.m) + 1u, nt, buckets,
+                       (const uint32_t *)cnt, perm, inv, win_lo);
     return hipGetLastError();
 }
 
