@@ -154,6 +154,60 @@ def margin_ok(q64: np.ndarray, rot64: np.ndarray, block_elems: int = 1 << 25) ->
     return ok
 
 
+def generate_tied_rotation(seed: int, rows: int, d: int, n_buckets: int, n_hashes: int, n_base: int = 6,
+                           dtype: str = "bf16") -> dict:
+    """Inputs with exact ties in [qR ; -qR], for the hash's first-index rule.
+
+    Each round's rotation is built from ``n_base`` random base columns: column j
+    is base column c_j times a sign s_j (both drawn), so the entries of
+    [qR ; -qR] take only the values +-(q . B_c) and every value occurs several
+    times, in one 32-column tile and across tiles.  Half of the base columns
+    keep one sign over all their copies, so their largest entries lie in the
+    -y half for half of the rows; the others occur with both signs.  A negated
+    copy of a column gives the exactly negated products and sums, so these
+    ties are exact in any precision.  Rows are drawn, and redrawn in order,
+    until in every round the largest |q . B_c| beats the second largest base
+    column by the margin rule's gap (computed as in ``margin_ok``, over the
+    base columns): the winning value is then decided far from any rounding,
+    and which of its equal copies wins only by the tie rule.
+    Returns q [rows, d] and rot [nh, d, nb/2] in storage form, the rotation's
+    and the base columns' fp64 values, and each column's base index and sign.
+    """
+    import torch
+    rng = np.random.default_rng(seed)
+    half = n_buckets // 2
+    base = to_storage(rng.standard_normal((n_hashes, d, n_base)), dtype)
+    base64 = to_f64(base, dtype)
+    cls = rng.integers(0, n_base, size=(n_hashes, half))
+    # the first half of the base columns keep one sign over all their copies (so
+    # their largest entries can lie in the -y half only), the others mix signs
+    fixed = rng.choice(np.array([-1.0, 1.0]), size=(n_hashes, n_base))
+    mixed = rng.choice(np.array([-1.0, 1.0]), size=(n_hashes, half))
+    sign = np.where(cls < n_base // 2, np.take_along_axis(fixed, cls, axis=1), mixed)
+    rot64 = np.stack([base64[r][:, cls[r]] * sign[r] for r in range(n_hashes)])
+    rot = to_storage(rot64, dtype)
+    assert np.array_equal(to_f64(rot, dtype), rot64)
+    q = to_storage(rng.standard_normal((rows, d)), dtype)
+    bt = torch.from_numpy(np.ascontiguousarray(base64.transpose(1, 0, 2).reshape(d, -1))).float()
+    col_norm = float(np.sqrt((base64 ** 2).sum(axis=1)).max())
+    gamma = (d + 2) * 2.0 ** -24
+
+    def ok(qs):
+        q64 = to_f64(qs, dtype)
+        v = (torch.from_numpy(q64).float() @ bt).view(-1, n_hashes, n_base).abs()
+        top = v.topk(2, dim=-1).values
+        gap = (top[..., 0] - top[..., 1]).double()
+        norm = torch.from_numpy(np.sqrt(np.einsum("ij,ij->i", q64, q64)))[:, None]
+        err = 2.0 * gamma * norm * col_norm
+        return ((gap >= MARGIN * norm + err) & (gap >= 2.0 * err) & (norm > 0)).all(dim=-1).numpy()
+
+    bad = np.nonzero(~ok(q))[0]
+    while bad.size:
+        q[bad] = to_storage(rng.standard_normal((bad.size, d)), dtype)
+        bad = bad[~ok(q[bad])]
+    return {"q": q, "rot": rot, "rot64": rot64, "base64": base64, "classes": cls, "signs": sign}
+
+
 # ----------------------------------------------------------------------------
 # generation
 

@@ -84,3 +84,16 @@ def test_every_library_kernel_has_a_model():
     for k in _lib.KERNELS:
         flops, nbytes = bench.algorithmic_work(k, cfg())
         assert nbytes > 0 and flops >= 0
+
+
+def test_sort_bytes_match_definition():
+    # the sort reads every bucket id once per launch and writes perm, inv and win_lo once (12 bytes
+    # per token-round, the scope table's unit), plus one 16-bit count per (segment, 4096-position
+    # tile, bucket), written by the first launch and read by the second
+    c = cfg(seq_len=10000)
+    S = c.batch * c.heads * c.n_hashes
+    Tr = S * c.seq_len
+    tiles = -(-c.seq_len // 4096)
+    cnt = S * tiles * c.n_buckets * 2
+    assert bench.algorithmic_work("sort_count", c) == (0.0, Tr * 4 + cnt)
+    assert bench.algorithmic_work("sort_scatter", c) == (0.0, Tr * 4 + cnt + Tr * 12)

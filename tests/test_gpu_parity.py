@@ -14,6 +14,7 @@ import torch
 
 from lsh_sparse_attention_amd import inputs as gen
 import gpu_util as gu
+from oracle import oracle as ora
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +64,31 @@ def test_small_shapes_match_oracle(case):
     res = gu.run_gpu(x)
     gu.check_sort_properties(res, cfg)
     gu.compare_slices(x, res, [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)])
+
+
+# head dim, buckets: nb/2 a multiple of 64 runs the pipelined hash kernel (slot search deferred to
+# the end of each round), the others the per-tile search
+TIES = [(128, 1024), (64, 1024), (32, 128), (64, 192), (128, 96), (64, 4096)]
+
+
+@pytest.mark.parametrize("d,nb", TIES, ids=[f"d{d}-nb{nb}" for d, nb in TIES])
+def test_hash_first_index_on_exact_ties(d, nb):
+    # rotations made of a few base columns repeated with signs: many entries of
+    # [qR ; -qR] are exactly equal, inside a 32-column tile, across tiles and
+    # in both halves; the first index must win, as in the oracle
+    import lsh_sparse_attention_amd as lsh
+    L, nh = 1000, 3
+    x = gen.generate_tied_rotation(21 + d + nb, L, d, nb, nh)
+    gu.say(f"[gpu] hash on exact ties d={d} nb={nb} L={L} nh={nh}")
+    prob = lsh.problem(1, 1, L, d, nh, nb, 8, dtype="bf16")
+    q = gu.to_device(x["q"], "bf16").view(1, 1, L, d)
+    rot = gu.to_device(x["rot"], "bf16")
+    bk = torch.full((1, 1, nh, L), -1, dtype=torch.int32, device="cuda")
+    lsh.lsh_hash(prob, q, rot, bk)
+    torch.cuda.synchronize()
+    want = ora.hash_(gen.to_f64(x["q"], "bf16"), x["rot64"], nb)
+    got = bk.cpu().numpy()[0, 0]
+    assert np.array_equal(got, want), f"{int((got != want).sum())} of {got.size} buckets differ"
 
 
 _CACHE = {}

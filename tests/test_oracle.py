@@ -88,6 +88,28 @@ def test_hash_sign_order_matters():
 
 # ----------------------------------------------------------------------------- sort
 
+@pytest.mark.parametrize("d,nb", [(128, 1024), (64, 192), (32, 16)])
+def test_hash_first_index_on_exact_ties(d, nb):
+    # Rotations built from a few base columns repeated with signs make many
+    # entries of [qR ; -qR] exactly equal (Reformer §2 defines the bucket as
+    # the argmax; the first index wins ties).  z is assembled from the base
+    # columns' values by index, so its ties are exact by construction, and
+    # numpy's argmax returns the first maximum.
+    from lsh_sparse_attention_amd import inputs as gen
+    x = gen.generate_tied_rotation(11, 512, d, nb, 2, n_base=4)
+    q64 = gen.to_f64(x["q"], "bf16")
+    bk = ora.hash_(q64, x["rot64"], nb)
+    half = nb // 2
+    for r in range(2):
+        y = (q64 @ x["base64"][r])[:, x["classes"][r]] * x["signs"][r]   # exact copies of the base values
+        z = np.concatenate([y, -y], axis=1)
+        want = np.argmax(z, axis=1)
+        assert np.array_equal(bk[r], want)
+        # the rule is exercised: several copies of the maximum, winners in both halves
+        assert ((z == z.max(axis=1, keepdims=True)).sum(axis=1) > 1).mean() > 0.5
+        assert 0 < (want >= half).mean() < 1
+
+
 def test_sort_golden():
     g = _golden()["attention"]
     bk = np.array(g["buckets"], np.int32)
