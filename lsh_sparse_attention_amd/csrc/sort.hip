@@ -22,19 +22,19 @@ namespace lsh {
 namespace {
 
 constexpr int kTile = 4096;                                 // positions per workgroup
-constexpr int kThreads = 256;                               // 4 waves
-constexpr int kWaves = kThreads / kWave;
-constexpr int kWavePositions = kTile / kWaves;              // 1024 per wave
-constexpr int kGroups = kWavePositions / kWave;             // 16 groups of 64 per wave
 constexpr int kMaxBuckets = 4096;
 constexpr int kMaxTiles = 65536 / kTile;                    // L <= 65536
 static_assert(kTile <= 65535, "tile counts are stored in 16 bits");
+// Workgroups of W waves: 8 while the per-wave counters fit LDS beside the
+// bucket starts (nb <= 2048), else 4.
+constexpr int kWideBuckets = 2048;
 
-// The tile's positions as the waves walk them: wave w owns the w-th quarter,
-// group g of it the 64 positions from g * 64.
+// The tile's positions as the waves walk them: wave w owns the w-th part of
+// kTile / W positions, group g of it the 64 positions from g * 64.
+template <int W>
 __device__ __forceinline__ int tile_pos(int tile, int wave, int g, int lane)
 {
-    return tile * kTile + wave * kWavePositions + g * kWave + lane;
+    return tile * kTile + wave * (kTile / W) + g * kWave + lane;
 }
 
 // A bucket id as both kernels use it: clamped into [0, nb), so that ids
@@ -42,9 +42,11 @@ __device__ __forceinline__ int tile_pos(int tile, int wave, int g, int lane)
 // sorted indices, consistently in both kernels.
 __device__ __forceinline__ int clamp_bucket(int32_t b, int nb) { return b < 0 ? 0 : (b >= nb ? nb - 1 : b); }
 
-__global__ __launch_bounds__(kThreads) void sort_count(int L, int nb, int ntiles, const int32_t *__restrict__ buckets,
-                                                       uint32_t *__restrict__ cnt)
+template <int W>
+__global__ __launch_bounds__(W * kWave) void sort_count(int L, int nb, int ntiles, const int32_t *__restrict__ buckets,
+                                                        uint32_t *__restrict__ cnt)
 {
+    constexpr int kThreads = W * kWave, kGroups = kTile / kThreads;
     extern __shared__ uint32_t h[];   // [nb]
     const int lb = xcd_block(blockIdx.x, gridDim.x);
     const int tile = lb % ntiles, seg = lb / ntiles, tid = threadIdx.x;
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void sort_count(int L, int nb, int ntiles
     int32_t x[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-        const int t = tile_pos(tile, wave, g, lane);
+        const int t = tile_pos<W>(tile, wave, g, lane);
         x[g] = t < L ? clamp_bucket(bk[t], nb) : -1;
     }
     for (int b = tid; b < nb; b += kThreads)
@@ -70,11 +72,13 @@ __global__ __launch_bounds__(kThreads) void sort_count(int L, int nb, int ntiles
         out[p] = h[2 * p] | (h[2 * p + 1] << 16);
 }
 
-// Exclusive scan of v[0 .. n) in LDS (n <= kMaxBuckets), in place; ends with
-// a workgroup barrier.
+// Exclusive scan of v[0 .. n) in LDS (n <= kMaxBuckets) by a workgroup of W
+// waves, in place; ends with a workgroup barrier.
+template <int W>
 __device__ void block_exclusive_scan(uint32_t *v, int n, uint32_t *wsum)
 {
-    constexpr int per = kMaxBuckets / kThreads;   // 16 consecutive entries per thread
+    constexpr int kThreads = W * kWave;
+    constexpr int per = kMaxBuckets / kThreads;   // consecutive entries per thread
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     uint32_t loc[per];
     uint32_t sum = 0;
@@ -108,7 +112,8 @@ __device__ void block_exclusive_scan(uint32_t *v, int n, uint32_t *wsum)
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbits, int m, uint64_t mmagic, int ntiles,
+template <int W>
+__global__ __launch_bounds__(W * kWave) void sort_scatter(int L, int nb, int nbits, int m, uint64_t mmagic, int ntiles,
                                                          const int32_t *__restrict__ buckets,
                                                          const uint32_t *__restrict__ cnt,
                                                          int32_t *__restrict__ perm, int32_t *__restrict__ inv,
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
     // LDS: bstart[nb] (bucket totals, then the first sorted index of each
     // bucket), pre[nb] (counts of the earlier tiles), wcnt[kWaves][nb]
     // (per-wave counts, then each wave's next sorted index per bucket)
+    constexpr int kThreads = W * kWave, kWaves = W, kGroups = kTile / kThreads;
     extern __shared__ uint32_t lds[];
     __shared__ uint32_t wsum[kWaves];
     uint32_t *bstart = lds, *pre = lds + nb, *wcnt = lds + 2 * nb;
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
     int32_t x[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-        const int t = tile_pos(tile, wave, g, lane);
+        const int t = tile_pos<W>(tile, wave, g, lane);
         x[g] = t < L ? clamp_bucket(bk[t], nb) : -1;
     }
     for (int k = tid; k < kWaves * nb; k += kThreads)
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
             atomicAdd(&mine[x[g]], 1u);
     // 3. first sorted index of each bucket (the barrier at its end also
     //    completes the counts above)
-    block_exclusive_scan(bstart, nb, wsum);
+    block_exclusive_scan<W>(bstart, nb, wsum);
     // 4. first sorted index of each (wave, bucket) run of this tile
     for (int b = tid; b < nb; b += kThreads) {
         uint32_t run = bstart[b] + pre[b];
@@ -179,33 +185,36 @@ __global__ __launch_bounds__(kThreads) void sort_scatter(int L, int nb, int nbit
         }
     }
     __syncthreads();
-    // 5. each wave walks its quarter in order, 64 positions at a time; lanes
+    // 5. each wave walks its part in order, 64 positions at a time.  Lanes
     //    holding the same bucket are ranked by lane index (ballots over the
-    //    bucket's bits)
+    //    bucket's bits); the group's lowest such lane takes the bucket's next
+    //    sorted indices from the wave's counter with one fetch-and-add, whose
+    //    result the others read from it.  A wave's LDS operations complete in
+    //    program order, so earlier groups get lower indices, and no group waits
+    //    for the one before it.
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int32_t *pr = perm + (size_t)seg * L, *iv = inv + (size_t)seg * L, *wl = win_lo + (size_t)seg * L;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-        const int t = tile_pos(tile, wave, g, lane);
+        const int t = tile_pos<W>(tile, wave, g, lane);
         const bool valid = x[g] >= 0;
         const int b = valid ? x[g] : 0;
         uint64_t peers = __ballot(valid);
         if (peers == 0ull)
-            break;   // the rest of the wave's quarter is past L
+            break;   // the rest of the wave's part is past L
         for (int bit = 0; bit < nbits; ++bit) {
             const bool on = (b >> bit) & 1;
             const uint64_t set = __ballot(valid && on);
             peers &= on ? set : ~set;
         }
         const int rank = __popcll(peers & lt_mask);
-        uint32_t s = 0u;
-        if (valid)
-            s = mine[b] + (uint32_t)rank;
-        wave_lds_sync();
+        uint32_t base = 0u;
         if (valid && rank == 0)
-            mine[b] = s + (uint32_t)__popcll(peers);
-        wave_lds_sync();
+            base = atomicAdd(&mine[b], (uint32_t)__popcll(peers));
+        // the lowest peer (a lane without peers, past L, reads lane 63 and ignores it)
+        base = (uint32_t)__shfl((int)base, (__ffsll((long long)peers) - 1) & (kWave - 1), kWave);
         if (valid) {
+            const uint32_t s = base + (uint32_t)rank;
             pr[s] = t;
             iv[t] = (int32_t)s;
             // s / m as a multiply: floor(s * (floor(2^32 / m) + 1) / 2^32) is
@@ -303,18 +312,27 @@ hipError_t launch_sort(const Dims &P, const int32_t *buckets, int32_t *perm, int
     while ((1 << nbits) < P.nb)
         ++nbits;
     const unsigned grid = (unsigned)S * (unsigned)nt;
+    const bool wide = P.nb <= kWideBuckets;
     {
         ProfScope prof(LSH_KERNEL_SORT_COUNT, st);
-        hipLaunchKernelGGL(sort_count, dim3(grid), dim3(kThreads), (size_t)P.nb * sizeof(uint32_t), st, P.L, P.nb,
-                           nt, buckets, cnt);
+        if (wide)
+            hipLaunchKernelGGL(sort_count<8>, dim3(grid), dim3(8 * kWave), (size_t)P.nb * sizeof(uint32_t), st, P.L,
+                               P.nb, nt, buckets, cnt);
+        else
+            hipLaunchKernelGGL(sort_count<4>, dim3(grid), dim3(4 * kWave), (size_t)P.nb * sizeof(uint32_t), st, P.L,
+                               P.nb, nt, buckets, cnt);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    const uint64_t mmagic = (uint64_t)(0xffffffffull / (uint64_t)P.m) + 1u;
     ProfScope prof(LSH_KERNEL_SORT_SCATTER, st);
-    hipLaunchKernelGGL(sort_scatter, dim3(grid), dim3(kThreads), (size_t)(2 + kWaves) * P.nb * sizeof(uint32_t), st,
-                       P.L, P.nb, nbits, P.m, (uint64_t)(0xffffffffull / (uint64_t)P.m) + 1u, nt, buckets,
-                       (const uint32_t *)cnt, perm, inv, win_lo);
+    if (wide)
+        hipLaunchKernelGGL(sort_scatter<8>, dim3(grid), dim3(8 * kWave), (size_t)(2 + 8) * P.nb * sizeof(uint32_t), st,
+                           P.L, P.nb, nbits, P.m, mmagic, nt, buckets, (const uint32_t *)cnt, perm, inv, win_lo);
+    else
+        hipLaunchKernelGGL(sort_scatter<4>, dim3(grid), dim3(4 * kWave), (size_t)(2 + 4) * P.nb * sizeof(uint32_t), st,
+                           P.L, P.nb, nbits, P.m, mmagic, nt, buckets, (const uint32_t *)cnt, perm, inv, win_lo);
     return hipGetLastError();
 }
 
