@@ -242,43 +242,82 @@ __global__ __launch_bounds__(kThreads) void tile_prep_kernel(int L, int nh, int 
     const int k = lane % kBlk;
     const uint32_t rec = srec[((size_t)bh * nh + r) * L + blk * kBlk + k];
     const size_t tok = (size_t)bh * L + rec_lo(rec);
-    const uint32_t *m = meta + tok * nh;
-    const uint32_t *bm = bmeta ? bmeta + tok * nh : nullptr;
-    const int nr = bm ? nh - 1 : (r < kMaxEarlier ? r : kMaxEarlier);
+    const int nr = bmeta ? nh - 1 : (r < kMaxEarlier ? r : kMaxEarlier);
+    // a token's nh records of one kind, 16 bytes at a time when nh is a
+    // multiple of 4 (then they start 16-byte aligned): a gather of 4 records
+    // costs one line request instead of four
+    auto recs_of = [&](const uint32_t *base, uint32_t (&v)[kMaxEarlier + 3]) __attribute__((always_inline)) {
+        const uint32_t *p = base + tok * nh;
+        if ((nh & 3) == 0) {
+#pragma unroll
+            for (int i = 0; i < (kMaxEarlier + 3) / 4; ++i)
+                if (4 * i < nh) {
+                    const u32x4_t u = ld16(p + 4 * i);
+                    v[4 * i] = u.x;
+                    v[4 * i + 1] = u.y;
+                    v[4 * i + 2] = u.z;
+                    v[4 * i + 3] = u.w;
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMaxEarlier + 3; ++i)
+                if (i < nh)
+                    v[i] = p[i];
+        }
+    };
+    // record of round rr (< r) or, with bmeta, of the other rounds in turn
+    auto other = [&](int rr) __attribute__((always_inline)) { return rr < r ? rr : rr + 1; };
+    uint32_t mv[kMaxEarlier + 3];
     if (lane < kBlk) {
         if (!ktile)
             return;
+        recs_of(bmeta ? bmeta : meta, mv);
         uint8_t *kt = ktile + (size_t)tile * ktile_stride(nh);
         reinterpret_cast<float *>(kt)[k] = rnorm[tok] * scale_log2;
-        for (int rr = 0; rr < nr; ++rr)
-            reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] =
-                (uint16_t)(bm ? bm[rr < r ? rr : rr + 1] : rec_lo(m[rr]));
+#pragma unroll
+        for (int rr = 0; rr < kMaxEarlier; ++rr)
+            if (rr < nr)
+                reinterpret_cast<uint16_t *>(kt + 128 + 64 * rr)[k] =
+                    (uint16_t)(bmeta ? mv[other(rr)] : rec_lo(mv[rr]));
     } else if (qtile) {
         uint8_t *qt = qtile + (size_t)tile * qtile_stride(nh);
         reinterpret_cast<float *>(qt)[k] = lse[tok] * kLog2e;
         reinterpret_cast<float *>(qt + 128)[k] = Dvec[tok];
-        if (wmeta) {
-            const uint32_t *wm = wmeta + tok * nh;
-            const uint32_t u = rec_lo(wm[r]) - (uint32_t)(blk * kBlk + k);
+        if (bmeta) {
+            recs_of(bmeta, mv);
+            if (wmeta) {
+                const uint32_t u = rec_lo(wmeta[tok * nh + r]) - (uint32_t)(blk * kBlk + k);
+                reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)(rec_hi(rec) | (u << 8));
+            } else {
+                reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
+            }
+#pragma unroll
+            for (int rr = 0; rr < kMaxEarlier; ++rr)
+                if (rr < nr) {
+                    reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)mv[other(rr)];
+                    reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = 0;
+                }
+        } else if (wmeta) {
+            recs_of(wmeta, mv);
+            const uint32_t u = rec_lo(mv[r]) - (uint32_t)(blk * kBlk + k);
             reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)(rec_hi(rec) | (u << 8));
-            for (int rr = 0; rr < (bm ? 0 : nr); ++rr) {
-                const uint32_t x = wm[rr];
-                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)rec_lo(x);
-                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)(rec_hi(x) + 1u);
-            }
+#pragma unroll
+            for (int rr = 0; rr < kMaxEarlier; ++rr)
+                if (rr < nr) {
+                    const uint32_t x = mv[rr];
+                    reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)rec_lo(x);
+                    reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)(rec_hi(x) + 1u);
+                }
         } else {
+            recs_of(meta, mv);
             reinterpret_cast<uint16_t *>(qt + 256)[k] = (uint16_t)rec_hi(rec);
-            for (int rr = 0; rr < (bm ? 0 : nr); ++rr) {
-                const uint32_t mr = m[rr];
-                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(rec_lo(mr) - 1u);
-                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)rec_hi(mr);
-            }
-        }
-        if (bm) {
-            for (int rr = 0; rr < nr; ++rr) {
-                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)bm[rr < r ? rr : rr + 1];
-                reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = 0;
-            }
+#pragma unroll
+            for (int rr = 0; rr < kMaxEarlier; ++rr)
+                if (rr < nr) {
+                    const uint32_t mr = mv[rr];
+                    reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr)[k] = (uint16_t)(rec_lo(mr) - 1u);
+                    reinterpret_cast<uint16_t *>(qt + 320 + 128 * rr + 64)[k] = (uint16_t)rec_hi(mr);
+                }
         }
     }
 }

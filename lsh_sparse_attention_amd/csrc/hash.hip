@@ -75,122 +75,16 @@ __global__ __launch_bounds__(kHashThreads) void hash_generic(int L, int nh, int 
 // every round the rotation is walked in blocks of 64 columns, staged
 // row-major in LDS (fetched one block ahead) and read transposed with
 // ds_read_b64_tr_b16, so Y^T = R^T Q^T comes out with lane = row and 16
-// columns per lane per 32-column tile.  The running argmax of +y and of -y
-// stays in registers in increasing column order (strict comparisons keep the
-// first index); the column offsets are wave-uniform, so the index select
-// takes them from scalar registers and the lane's own offset 4 h is added at
-// the end.  The two lane halves that share a row are merged last.  bf16
+// columns per lane per 32-column tile.  The running argmax over [y ; -y]
+// keeps, per row, the best entry's key and the scores of the tile that holds
+// it (tile_track); the winning column is found in that tile when the round
+// ends, and the two lane halves that share a row are merged last.  bf16
 // products are exact in the fp32 accumulator.
 constexpr int kHashRows = 256;
 constexpr int kHashCols = 64;              // rotation columns per staged block
 
-// Argmax over [y ; -y] with first-index ties, one tracker per lane and
-// parity of the slot: the key rotl(bits(y'), 1) with y' = -y orders by |y|
-// (bits of |y| on top) and, for equal |y|, puts y > 0 (sign bit of y'
-// set) above y < 0, i.e. the +y half (lower indices) above the -y half;
-// a strictly greater key replaces the tracked one, so the first column
-// wins among equal keys.  Key 0 is y = 0 (never -0: the sums start at +0).
-//
-// acc[ct][4 g + t] = y'[column j0 + 8 g + 4 h + t] of row 32 ct + c.  Within
-// the tile each parity tracker keeps (key, slot offset 8 g + t), the offsets
-// being immediates; the tile result then merges into the round's tracker
-// (strictly greater key: an earlier tile wins ties).  FULL: all 32 columns
-// exist; otherwise columns at or past `half` are skipped.
-template <bool FULL>
-__device__ __forceinline__ void tile_argmax(const f32x16_t (&acc)[2], int j0, int h, int half, uint32_t (&bk)[2][2],
-                                            int (&bi)[2][2])
-{
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        uint32_t tk[2] = {0u, 0u};
-        int ts[2] = {0, 0};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t u = __float_as_uint(acc[ct][e]);
-            const int off = 8 * (e / 4) + (e % 4);
-            uint32_t key = __builtin_amdgcn_alignbit(u, u, 31);
-            if constexpr (!FULL)
-                key = (j0 + off + 4 * h < half) ? key : 0u;
-            const int p = e % 2;
-            ts[p] = key > tk[p] ? off : ts[p];
-            tk[p] = max(tk[p], key);
-        }
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            bi[ct][p] = tk[p] > bk[ct][p] ? j0 + ts[p] : bi[ct][p];
-            bk[ct][p] = max(bk[ct][p], tk[p]);
-        }
-    }
-}
-
-// The same update for a full tile with fewer vector instructions: the
-// tile's largest key by three-input maxima (over each half of the slots and
-// then both), then the first slot holding it, searched in two independent
-// chains (a compare and a select per score, last slot first).  The search
-// is written so that its result is always used; otherwise the compiler
-// turns it into a branch, which splits the code it can schedule together
-// with the next tile's products.  Only tracker 0 of each column tile is used.
-__device__ __forceinline__ void tile_argmax_full(const f32x16_t (&acc)[2], int j0, uint32_t (&bk)[2][2],
-                                                 int (&bi)[2][2])
-{
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        uint32_t k[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t u = __float_as_uint(acc[ct][e]);
-            k[e] = __builtin_amdgcn_alignbit(u, u, 31);
-        }
-        const uint32_t lo = max(max(max(max(k[0], k[1]), k[2]), max(max(k[3], k[4]), k[5])), max(k[6], k[7]));
-        const uint32_t hi = max(max(max(max(k[8], k[9]), k[10]), max(max(k[11], k[12]), k[13])), max(k[14], k[15]));
-        const uint32_t tm = max(lo, hi);
-        // the key searched for: the tile maximum if it beats the tracked one,
-        // else all ones (a NaN pattern, never the key of a finite score), so
-        // the search runs unconditionally and leaves the tracked column
-        const uint32_t want = tm > bk[ct][0] ? tm : 0xffffffffu;
-        const int keep = bi[ct][0] - j0;
-        int ta = keep, tb = keep;
-#pragma unroll
-        for (int e = 7; e >= 0; --e) {
-            ta = k[e] == want ? 8 * (e / 4) + (e % 4) : ta;
-            tb = k[e + 8] == want ? 8 * ((e + 8) / 4) + (e % 4) : tb;
-        }
-        bi[ct][0] = j0 + (lo == want ? ta : tb);
-        bk[ct][0] = max(bk[ct][0], tm);
-    }
-}
-
-// End of a round: merge the two slot parities, then the other half of the
-// row (larger key, else smaller column), store the bucket and reset.
-__device__ __forceinline__ void round_store(uint32_t (&bk)[2][2], int (&bi)[2][2], int h, int c, int row0, int L,
-                                            int half, int32_t *__restrict__ out)
-{
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        uint32_t k0 = bk[ct][0], k1 = bk[ct][1];
-        int i0 = bi[ct][0] + 4 * h, i1 = bi[ct][1] + 4 * h;
-        if (k1 > k0 || (k1 == k0 && i1 < i0)) {
-            k0 = k1;
-            i0 = i1;
-        }
-        const auto pk = __builtin_amdgcn_permlane32_swap(k0, k0, false, false);
-        const auto pi = __builtin_amdgcn_permlane32_swap((uint32_t)i0, (uint32_t)i0, false, false);
-        const uint32_t ok = h ? pk[0] : pk[1];
-        const int oi = (int)(h ? pi[0] : pi[1]);
-        if (ok > k0 || (ok == k0 && oi < i0)) {
-            k0 = ok;
-            i0 = oi;
-        }
-        const int row = row0 + 32 * ct + c;
-        // key 0: every projection is zero and bucket 0 (a +y entry) is the first maximum
-        if (h == 0 && row < L)
-            out[row] = k0 == 0u ? 0 : ((k0 & 1u) ? i0 : half + i0);
-        bk[ct][0] = bk[ct][1] = 0u;
-        bi[ct][0] = bi[ct][1] = 0;
-    }
-}
-
-// Deferred slot search (full tiles).  Per row (column tile ct) the round's
+// Argmax over [y ; -y] with first-index ties, slot search deferred to the
+// end of the round.  Per row (column tile ct) the round's
 // best entry so far is kept as a key and the lane's 16 scores y' = -y of the
 // tile that holds it; the slot inside that tile is searched for once, when
 // the round ends.  Per tile the lane takes the largest +y entry (max of -y')
@@ -327,8 +221,9 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
         }
     };
 
-    uint32_t bk[2][2] = {{0u, 0u}, {0u, 0u}};
-    int bi[2][2] = {{0, 0}, {0, 0}};
+    uint32_t bk[2] = {0u, 0u};
+    int bj[2] = {0, 0};
+    f32x16_t sv[2] = {f32x16_t{}, f32x16_t{}};
     fetch(0);
     for (int blk = 0; blk < nh * nblk; ++blk) {
         const int r = blk / nblk, jb = (blk % nblk) * kHashCols;
@@ -356,13 +251,21 @@ __global__ __launch_bounds__(kHashThreads) void hash_mfma_kernel(int L, int nh, 
                 for (int ks = 0; ks < D / 16; ++ks)
                     acc[ct] = mfma32(aop[ks], qop[ct][ks], acc[ct]);
             }
-            if (j0 + 32 <= half)
-                tile_argmax<true>(acc, j0, h, half, bk, bi);
-            else
-                tile_argmax<false>(acc, j0, h, half, bk, bi);
+            if (j0 + 32 > half) {
+                // columns at or past half: a score of 0 wins only where every
+                // real score of the row is 0 too, and then the search takes
+                // the lowest column, a real one
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (j0 + 8 * (e / 4) + 4 * h + (e % 4) >= half)
+                            acc[ct][e] = 0.f;
+            }
+            tile_track(acc, j0, bk, bj, sv);
         }
         if (jb + kHashCols >= half)   // last block of round r
-            round_store(bk, bi, h, c, row0, L, half, buckets + ((size_t)bh * nh + r) * L);
+            round_store_tracked(bk, bj, sv, h, c, row0, L, half, buckets + ((size_t)bh * nh + r) * L);
     }
 
 }
