@@ -720,22 +720,27 @@ __device__ __forceinline__ void dma_rows512(const bf16 *__restrict__ a, const bf
 
 // One wave loads one tensor of a block: rows [0, 32) of a (positions from
 // rec) into the swizzled tile A, D/16 instructions.
-template <int D>
+template <int D, int G = kBlk * D / 8 / kWave>
 __device__ __forceinline__ void dma_tensor_wave(const bf16 *__restrict__ a, uint16_t *A, const uint32_t *rec,
                                                 size_t tok0, int lane)
 {
     constexpr int CPR = D / 8, N = kBlk * CPR / kWave;
-    size_t off[N];   // records first (see dma_rows)
+    const bf16 *base = a + tok0 * D;   // the (b, h) slice: offsets within it fit 32 bits
+    // records first (see dma_rows), G rows' worth at a time
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int qc = i * kWave + lane;
-        const int row = qc / CPR, p = qc % CPR;
-        const int lc = p ^ (row & (CPR - 1));
-        off[i] = (tok0 + rec_lo(rec[row])) * D + lc * 8;
+    for (int i0 = 0; i0 < N; i0 += G) {
+        uint32_t off[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int qc = (i0 + i) * kWave + lane;
+            const int row = qc / CPR, p = qc % CPR;
+            const int lc = p ^ (row & (CPR - 1));
+            off[i] = rec_lo(rec[row]) * (uint32_t)D + lc * 8;
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            dma16(base + off[i], A + (i0 + i) * kWave * 8);
     }
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        dma16(a + off[i], A + i * kWave * 8);
 }
 
 template <int D>
@@ -941,6 +946,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // from the resident query blocks (shared QK); their value rows are loaded
 // one tile ahead into registers; per-32-row key tiles and the sorted
 // records arrive by the same direct-to-LDS loads.
+//
+// The waves do not meet at a workgroup barrier.  Two LDS counters per tile
+// parity: waves through blocks 0..3, and waves whose share of the loads
+// issued in the tile has landed.  The wave that completes the first count
+// issues its share at once, the others at the tile's end (checking after
+// each of blocks 4..7 as well costs the d = 128 kernel spills inside the
+// loop); a wave waits for the second count of the previous tile before its
+// blocks 4..7.
 
 constexpr int kStreamStages = 8;
 constexpr int kRecRing = 512;                 // records of sorted rows x at x mod 512
@@ -1166,6 +1179,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     __shared__ __align__(16) uint8_t Ts[kStreamStages][kQTile];
     __shared__ __align__(16) uint8_t Kt[3][kRows / kBlk][kKTile];     // key tiles, two tiles ahead
     __shared__ __align__(16) uint32_t recs[kRecRing];
+    // per tile parity, monotonic, 8 per tile: waves through blocks 0..3 of
+    // their tile, and waves whose share of the loads issued in that tile
+    // has landed
+    __shared__ uint32_t through[2], loaded[2];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int g = lane / 16, c = lane % 16;
@@ -1206,6 +1223,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // prologue: records of the first tile's window and the one after, the
     // key tiles of the first two tiles; then the first tile's eight query
     // blocks and the value rows of its keys
+    if (tid < 2) {
+        through[tid] = 0u;
+        loaded[tid] = 0u;
+    }
     {
         const int k0 = t_begin * kRows;
         issue_recs(k0, 6);
@@ -1236,6 +1257,20 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     f32x4_t dka[D / 16], dva[D / 16];
     int kpos_prev = 0;
     float rn_prev = 0.f;
+    // this wave's last share, not yet counted as landed: it is (after a
+    // wait for the wave's loads) kSettle blocks after its issue, or at the
+    // latest before the wave waits for the others' shares or issues another
+    bool due = false;
+    int due_slot = 0, since = 0;
+    constexpr int kSettle = 2;
+    auto settle = [&](bool now) __attribute__((always_inline)) {
+        if (due && (now || ++since >= kSettle)) {
+            wait_vm<0>();
+            if (lane == 0)
+                atomicAdd(&loaded[due_slot], 1u);
+            due = false;
+        }
+    };
     for (int t = t_begin; t < t_end; ++t) {
         const int k0 = t * kRows, a0 = k0 / kBlk, j = t - t_begin;
         if (t > t_begin)
@@ -1283,31 +1318,75 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             dkv_block<D, NR, MODE, DUPB>(Qs[st], Gs[st], Ts[st], kt, recs + qb % kRecRing, kpos, ke, r, nh, qb, sk, g,
                                          c, lane, krn2, scale, skp, kop, vop, dka, dva);
         };
-        for (int b = 0; b < 4 && b < nb; ++b)
+        for (int b = 0; b < 4 && b < nb; ++b) {
             work(b);
-        // Every wave is through blocks 0..3 of this tile (and the previous
-        // tile); everything issued during the previous tile has landed.
-        wait_vm<0>();
-        block_barrier();
+            settle(false);
+        }
+        // Once every wave is through blocks 0..3 (and so through the
+        // previous tile), their stages, the key-tile buffer of the previous
+        // tile and its records take this tile's loads for the next two
+        // tiles, each wave issuing its share: one tensor of one block.
+        const uint32_t goal = 8u * (uint32_t)(j / 2 + 1);
+        bool pending = t + 1 < t_end;
+        auto issue_share = [&]() __attribute__((always_inline)) {
+            settle(true);   // the previous share (a tile without blocks 4..7 never waits for it)
+            const int a = a0 + 8 + wave / 2, st = a % kStreamStages, h = wave % 2;
+            if (a < nblk) {
+                dma_tensor_wave<D, 2>(h ? dout : q, h ? Gs[st] : Qs[st], recs + (a * kBlk) % kRecRing, tok0, lane);
+                if (1024 * h + 16 * lane < qts)
+                    dma16(qtb + (size_t)a * qts + 1024 * h + 16 * lane, Ts[st] + 1024 * h);
+            }
+            if (t + 2 < t_end)
+                issue_ktiles(t + 2, (j + 2) % 3);
+            if (k0 + 3 * kRows < L)
+                issue_recs(k0 + 3 * kRows, 6);
+            pending = false;
+            due = true;
+            due_slot = (j + 1) % 2;
+            since = 0;
+        };
+        auto check = [&]() __attribute__((always_inline)) {
+            if (pending && *(volatile LDS_AS uint32_t *)(LDS_AS uint32_t *)&through[j % 2] >= goal)
+                issue_share();
+        };
+        {
+            uint32_t old = 0u;
+            if (lane == 0)
+                old = atomicAdd(&through[j % 2], 1u);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (pending && old + 1u == goal)
+                issue_share();
+        }
         bf16x8_t vnext[D / 32];
         if (t + 1 < t_end) {
-            // value rows of the next tile's keys first, so that waiting for
-            // them does not wait for the block loads issued after them
+            // value rows of the next tile's keys (records loaded two tiles ago)
             const int kn = (int)rec_lo(recs[(k0 + kRows + kg * 16 + c) % kRecRing]);
             const bf16 *vrow = v + (tok0 + kn) * D;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
                 vnext[ks] = as_bf16x8(ld16(vrow + 32 * ks + 8 * g));
-            for (int i = 0; i < 4; ++i)
-                if (a0 + 8 + i < nblk)
-                    issue_block(a0 + 8 + i);
-            if (t + 2 < t_end)
-                issue_ktiles(t + 2, (j + 2) % 3);
-            if (k0 + 3 * kRows < L)
-                issue_recs(k0 + 3 * kRows, 6);
         }
-        for (int b = 4; b < nb; ++b)
+        // blocks 4..7 were loaded during the previous tile: wait for every
+        // wave's share of them (the prologue loaded the first tile's)
+        if (j > 0 && nb > 4) {
+            settle(true);
+            const uint32_t want = 8u * (uint32_t)((j + 1) / 2);
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                if (*(volatile LDS_AS uint32_t *)(LDS_AS uint32_t *)&loaded[j % 2] >= want)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            asm volatile("" ::: "memory");
+        }
+        for (int b = 4; b < nb; ++b) {
             work(b);
+            settle(false);
+        }
+        // every wave reaches the count above without waiting, so this ends
+        for (int spin = 0; pending && spin < (1 << 22); ++spin) {
+            __builtin_amdgcn_s_sleep(1);
+            check();
+        }
         kpos_prev = kpos;
         rn_prev = rn;
         if (t + 1 < t_end) {
@@ -1332,6 +1411,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 // four earlier blocks first; then their stages take the next tile's new
 // blocks (and the next tile's query rows are loaded into registers) while
 // the tile's own four blocks are worked on.
+//
+// No workgroup barrier between tiles: a wave starts the next tile as soon as
+// all eight shares of its new blocks have landed (an LDS counter per tile
+// parity).  A share is issued only once every wave is through the four
+// earlier blocks it overwrites (a second counter), so waves drift apart by
+// less than a tile, and the record ring (rows x at x mod 512, written two
+// tiles ahead) never overwrites rows a slower wave still reads.
 
 template <int D, bool BWD, int NR, int MODE, bool DUPB>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q_stream_kernel(
@@ -1351,7 +1437,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     __shared__ __align__(16) uint16_t Vs[kStreamStages][kBlk * D];
     __shared__ __align__(16) uint8_t Kts[kStreamStages][kKTile];
     __shared__ __align__(16) uint32_t recs[kRecRing];
-    __shared__ uint32_t through;   // waves through the earlier blocks of their tile, 8 per tile
+    // per tile slot (tile index mod 2), monotonic: waves through the earlier
+    // blocks of their tile (8 per tile), and waves whose share of the next
+    // tile's blocks has landed in LDS (8 per tile)
+    __shared__ uint32_t through[2], loaded[2];
     // with more than seven earlier rounds the queries' records of those
     // rounds wait in LDS during a tile rather than in registers
     constexpr bool kKeepWin = NR <= 7;
@@ -1430,8 +1519,10 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     auto win_n = [](uint32_t qm) { return bcast16(NC ? rec_hi(qm) + 1u : rec_hi(qm)); };
 
     // prologue: records [s0 - 128, s0 + 256), then the first tile's eight blocks and query rows
-    if (tid < kStreamStages)
-        through = 0u;
+    if (tid < 2) {
+        through[tid] = 0u;
+        loaded[tid] = 0u;
+    }
     {
         const int s0 = t_begin * kRows;
         if (s0 >= kRows)
@@ -1481,7 +1572,19 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                         qmL[wave][rr][c] = cur.qm[rr];
             }
         }
-        block_barrier();
+        const int jt = t - t_begin;
+        if (jt == 0) {
+            block_barrier();   // the prologue's blocks, loaded by every wave
+        } else {
+            // every wave's share of this tile's four new blocks has landed
+            const uint32_t want = 8u * (uint32_t)((jt + 1) / 2);
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                if (*(volatile LDS_AS uint32_t *)(LDS_AS uint32_t *)&loaded[jt % 2] >= want)
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            asm volatile("" ::: "memory");
+        }
         // query operand: rows 16 (qg % 2) + c of own block a0 + qg / 2
         bf16x8_t qop[D / 32];
 #pragma unroll
@@ -1690,8 +1793,9 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int a = a0 - 4; a < a0; ++a)
             if (a >= 0)
                 work(a);
-        const uint32_t goal = 8u * (uint32_t)(t - t_begin + 1);
+        const uint32_t goal = 8u * (uint32_t)(jt / 2 + 1);
         bool pending = t + 1 < t_end;
+        bool signaled = !pending;
         auto issue_share = [&]() __attribute__((always_inline)) {
             const int a = a0 + 4 + wave / 2, st = a % kStreamStages;
             if (a < nblk) {
@@ -1703,13 +1807,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             pending = false;
         };
         auto check = [&]() __attribute__((always_inline)) {
-            if (pending && *(volatile LDS_AS uint32_t *)(LDS_AS uint32_t *)&through >= goal)
+            if (pending && *(volatile LDS_AS uint32_t *)(LDS_AS uint32_t *)&through[jt % 2] >= goal)
                 issue_share();
         };
         {
             uint32_t old = 0u;
             if (lane == 0)
-                old = atomicAdd(&through, 1u);
+                old = atomicAdd(&through[jt % 2], 1u);
             old = __builtin_amdgcn_readfirstlane(old);
             if (pending && old + 1u == goal)
                 issue_share();
@@ -1719,15 +1823,31 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             if (s0 + 2 * kRows < L)
                 issue_recs(s0 + 2 * kRows, 6);
         }
+        // once this wave's share has landed, tell the others: they wait for
+        // all eight shares at the next tile's start.  The wait for the share
+        // comes after kSettle of the wave's own blocks (the forward at d = 128
+        // has the least work per block to hide the loads behind).
+        constexpr int kSettle = BWD || D <= 64 ? 1 : 3;
+        auto settle = [&]() __attribute__((always_inline)) {
+            if (!pending && !signaled) {
+                wait_vm<0>();
+                if (lane == 0)
+                    atomicAdd(&loaded[(jt + 1) % 2], 1u);
+                signaled = true;
+            }
+        };
         for (int a = a0; a < a0 + 4; ++a) {
             work(a);
+            if (a - a0 + 1 >= kSettle)
+                settle();
             check();
         }
         // every wave reaches the count above without waiting, so this ends
-        while (pending) {
+        for (int spin = 0; pending && spin < (1 << 22); ++spin) {
             __builtin_amdgcn_s_sleep(1);
             check();
         }
+        settle();
         qpos_prev = cur.qpos;
     }
     finish(qpos_prev);
