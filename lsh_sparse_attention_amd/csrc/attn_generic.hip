@@ -25,6 +25,44 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRowsPerWave = 4;
 
+// Read-once / write-once rows: the same as load8 / store8 with nontemporal
+// accesses (prep's q, O and dO rows, the combine's per-round rows and its
+// output: 10-12 % less time in either kernel at the long-text shape than
+// plain accesses).
+__device__ __forceinline__ void load8_nt(const bf16 *p, float out[8])
+{
+    const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[2 * k] = __uint_as_float(w[k] << 16);
+        out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8_nt(const float *p, float out[8])
+{
+    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p + 4));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[k] = a[k];
+        out[4 + k] = b[k];
+    }
+}
+__device__ __forceinline__ void store8_nt(bf16 *p, const float x[8])
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = (uint32_t)from_f<bf16>(x[2 * k]).bits | ((uint32_t)from_f<bf16>(x[2 * k + 1]).bits << 16);
+    __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4_t *>(p));
+}
+__device__ __forceinline__ void store8_nt(float *p, const float x[8])
+{
+    __builtin_nontemporal_store(f32x4_t{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4_t *>(p));
+    __builtin_nontemporal_store(f32x4_t{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4_t *>(p + 4));
+}
+
 // ---------------------------------------------------------------------------
 // prep: packed records, inverse norms, and (backward) D = dO . O.  The
 // records' window start is win_lo, or with chunk_only (no bucket condition)
@@ -54,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, int m, in
     if (meta) {
         float ss = 0.f;
         if (valid) {
-            load8(q + tok * D + ch * 8, x);
+            load8_nt(q + tok * D + ch * 8, x);
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 ss = fmaf(x[k], x[k], ss);
@@ -76,8 +114,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(int L, int nh, int m, in
     if (Dvec) {
         float acc = 0.f;
         if (valid) {
-            load8(out + tok * D + ch * 8, x);
-            load8(dout + tok * D + ch * 8, y);
+            load8_nt(out + tok * D + ch * 8, x);
+            load8_nt(dout + tok * D + ch * 8, y);
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 acc = fmaf(x[k], y[k], acc);
@@ -376,42 +414,6 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(int L, int nh, float scal
 // ---------------------------------------------------------------------------
 // combine: one wave per token
 
-// Read-once / write-once rows: the same as load8 / store8 with nontemporal
-// accesses (the combine's per-round rows and its output: 10 % less time at
-// the long-text shape than plain accesses).
-__device__ __forceinline__ void load8_nt(const bf16 *p, float out[8])
-{
-    const u32x4_t u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        out[2 * k] = __uint_as_float(w[k] << 16);
-        out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
-}
-__device__ __forceinline__ void load8_nt(const float *p, float out[8])
-{
-    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
-    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p + 4));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        out[k] = a[k];
-        out[4 + k] = b[k];
-    }
-}
-__device__ __forceinline__ void store8_nt(bf16 *p, const float x[8])
-{
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        w[k] = (uint32_t)from_f<bf16>(x[2 * k]).bits | ((uint32_t)from_f<bf16>(x[2 * k + 1]).bits << 16);
-    __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4_t *>(p));
-}
-__device__ __forceinline__ void store8_nt(float *p, const float x[8])
-{
-    __builtin_nontemporal_store(f32x4_t{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4_t *>(p));
-    __builtin_nontemporal_store(f32x4_t{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4_t *>(p + 4));
-}
 
 template <typename T, int D, int NH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int L, int nh, int ntok, float scale,
