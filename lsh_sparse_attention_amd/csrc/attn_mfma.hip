@@ -1192,8 +1192,9 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int nt = L / kRows, nblk = L / kBlk;
     const int rps = (nt + T - 1) / T;                      // runs per (b, h, round)
     const int lb = xcd_block(blockIdx.x, gridDim.x);
-    const int seg = lb / rps, run = lb % rps;
-    const int r = seg % nh, bh = seg / nh;
+    // rounds in descending order within a (b, h): see stream_run_tiles
+    const int run = lb % rps, r = nh - 1 - (lb / rps) % nh, bh = (lb / rps) / nh;
+    const int seg = bh * nh + r;
     const int t_begin = run * T, t_end = min(nt, t_begin + T);
     const uint32_t *sr = srec + (size_t)seg * L;
     const size_t tok0 = (size_t)bh * L;
@@ -1455,8 +1456,9 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int nt = L / kRows, nblk = L / kBlk;
     const int rps = (nt + T - 1) / T;
     const int lb = xcd_block(blockIdx.x, gridDim.x);
-    const int seg = lb / rps, run = lb % rps;
-    const int r = seg % nh, bh = seg / nh;
+    // rounds in descending order within a (b, h): see stream_run_tiles
+    const int run = lb % rps, r = nh - 1 - (lb / rps) % nh, bh = (lb / rps) / nh;
+    const int seg = bh * nh + r;
     const int nrec = DUPB ? nh - 1 : r;   // other-round records in use
     const int t_begin = run * T, t_end = min(nt, t_begin + T);
     const uint32_t *sr = srec + (size_t)seg * L;
@@ -1941,12 +1943,20 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
 }
 
 // Tiles per run of the persistent kernels: about one run per CU in total
-// (a workgroup of these kernels fills a CU), runs within one (b, h, round).
+// (a workgroup of these kernels fills a CU), runs within one (b, h, round),
+// at most kMaxRunTiles tiles.  A round's tiles cost more the more earlier
+// rounds its membership tests cover (the last of eight rounds about 1.5x the
+// first), so with one run per segment the CUs holding round 0 idle for a
+// third of the launch; shorter runs, dealt out as CUs free up, even that out,
+// and the workgroups take the rounds last to first within a (b, h) so that
+// the cheap runs come last.
+constexpr int kMaxRunTiles = 128;
 int stream_run_tiles(int nt, int segs)
 {
     constexpr int kCUs = 256;
     const long total = (long)nt * segs;
     int T = (int)((total + kCUs - 1) / kCUs);
+    T = T > kMaxRunTiles ? kMaxRunTiles : T;
     return T < 1 ? 1 : (T > nt ? nt : T);
 }
 
