@@ -1942,20 +1942,25 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(int L, int nh, int nto
     st8(dv + (size_t)tok * D + ch * 8, av);
 }
 
-// Tiles per run of the persistent kernels: about one run per CU in total
-// (a workgroup of these kernels fills a CU), runs within one (b, h, round),
-// at most kMaxRunTiles tiles.  A round's tiles cost more the more earlier
-// rounds its membership tests cover (the last of eight rounds about 1.5x the
-// first), so with one run per segment the CUs holding round 0 idle for a
-// third of the launch; shorter runs, dealt out as CUs free up, even that out,
-// and the workgroups take the rounds last to first within a (b, h) so that
-// the cheap runs come last.
+// Tiles per run of the persistent kernels: one run per CU in total (a
+// workgroup of these kernels fills a CU), or two when one per CU gives runs
+// of kMinSplitTiles to kMaxSplitTiles tiles (2x the minimum to the maximum);
+// runs within one (b, h, round), at most kMaxRunTiles tiles.  A round's tiles cost more the more earlier rounds its
+// membership tests cover (the last of eight rounds about 1.5x the first), so
+// with one run per segment the CUs holding round 0 idle for a third of the
+// launch.  Runs dealt out as CUs free up, with the rounds of a (b, h) taken
+// last to first so that the cheap runs come last, even that out; each run
+// costs a prologue whose loads nothing overlaps, hence the bounds.
 constexpr int kMaxRunTiles = 128;
+constexpr int kMinSplitTiles = 12, kMaxSplitTiles = 32;
 int stream_run_tiles(int nt, int segs)
 {
     constexpr int kCUs = 256;
     const long total = (long)nt * segs;
     int T = (int)((total + kCUs - 1) / kCUs);
+    const int half = (int)((total + 2 * kCUs - 1) / (2 * kCUs));
+    if (T <= kMaxSplitTiles && half >= kMinSplitTiles)
+        T = half;
     T = T > kMaxRunTiles ? kMaxRunTiles : T;
     return T < 1 ? 1 : (T > nt ? nt : T);
 }
