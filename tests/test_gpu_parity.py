@@ -48,6 +48,13 @@ SMALL = [
     ("bf16-nh12-d128", 1, 1, 1024, 128, 32, 12, 64, "bf16", False),
     ("bf16-nh10-d64", 1, 2, 512, 64, 16, 10, 32, "bf16", False),
     ("bf16-nh6", 1, 1, 1024, 128, 64, 6, 128, "bf16", False),
+    # persistent runs whose last one is short (40 tiles per segment in runs of 3; 50 in runs of 4;
+    # 50 in runs of 13, two runs per CU, eight rounds); with m = 32 and ~20 rows per bucket, some
+    # key tiles are reached by no query block past their own four
+    ("bf16-ragged-runs", 1, 8, 5120, 64, 64, 2, 128, "bf16", False),
+    ("bf16-ragged-runs-d128", 1, 4, 6400, 128, 64, 4, 128, "bf16", False),
+    ("bf16-split-runs-nh8", 2, 8, 6400, 64, 64, 8, 128, "bf16", False),
+    ("bf16-ragged-runs-m32", 1, 8, 5120, 64, 256, 2, 32, "bf16", False),
 ]
 
 
