@@ -21,11 +21,13 @@
 // (no staging registers) into a ring of LDS stages, several blocks ahead of
 // the block in use, so that enough bytes are in flight per CU to cover the
 // loaded memory latency; each wave waits on its own outstanding loads with
-// s_waitcnt vmcnt and a workgroup barrier publishes the block.  Two kernel
-// families: for chunk lengths that divide 128 (every workload), persistent
-// 8-wave workgroups (one per CU) walk runs of consecutive 128-row tiles with
-// an 8-stage ring shared between neighbouring tiles (q_stream_kernel,
-// dkv_stream_kernel, below); for other chunk lengths, one 4-wave workgroup per
+// s_waitcnt vmcnt, and a workgroup barrier (the per-tile kernels) or an LDS
+// counter of the waves whose loads have landed (the persistent ones)
+// publishes the block.  Two kernel families: for chunk lengths that divide
+// 128 (every workload), persistent 8-wave workgroups (one per CU) walk runs
+// of consecutive 128-row tiles with an 8-stage ring shared between
+// neighbouring tiles (q_stream_kernel, dkv_stream_kernel, below); for other
+// chunk lengths, one 4-wave workgroup per
 // tile (fwd_kernel, dq_kernel with a 4-stage ring and two workgroups per CU;
 // dkv_kernel).  Tiles are stored unpadded with the
 // 16-byte chunks of row r XOR-swizzled by r, so that both the row reads
