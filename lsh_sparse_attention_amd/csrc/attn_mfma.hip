@@ -1321,10 +1321,14 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             dkv_block<D, NR, MODE, DUPB>(Qs[st], Gs[st], Ts[st], kt, recs + qb % kRecRing, kpos, ke, r, nh, qb, sk, g,
                                          c, lane, krn2, scale, skp, kop, vop, dka, dva);
         };
+        // raised wave priority while the blocks that gate the next loads are
+        // worked on (see q_stream_kernel)
+        __builtin_amdgcn_s_setprio(2);
         for (int b = 0; b < 4 && b < nb; ++b) {
             work(b);
             settle(false);
         }
+        __builtin_amdgcn_s_setprio(0);
         // Once every wave is through blocks 0..3 (and so through the
         // previous tile), their stages, the key-tile buffer of the previous
         // tile and its records take this tile's loads for the next two
@@ -1794,9 +1798,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         // count at once, the others at their next check (after each of their
         // own blocks, and at the latest before the tile's end), so the loads
         // start early and no wave carries all of them.
+        // raised wave priority while the blocks that gate the next loads are
+        // worked on (the SIMD's other wave yields to a wave still in them)
+        __builtin_amdgcn_s_setprio(2);
         for (int a = a0 - 4; a < a0; ++a)
             if (a >= 0)
                 work(a);
+        __builtin_amdgcn_s_setprio(0);
         const uint32_t goal = 8u * (uint32_t)(jt / 2 + 1);
         bool pending = t + 1 < t_end;
         bool signaled = !pending;
